@@ -1,0 +1,369 @@
+"""Seeded synthetic inputs for the table-batched embedding-bag (TBE) operator.
+
+This module is the one piece shared by the HIP path's callers and by the CPU
+oracle's callers.  It only draws inputs (table shapes, bag lengths, ids,
+per-sample weights, output gradients, embedding weights); it performs none of
+the operator's arithmetic (no pooling, no sorting, no gradient math).
+
+Input layout it produces follows the problem statement of the FBTriton TBE
+article (ai.thesatyajit.com, "A lookup table that is most of the model"):
+
+* one flat ``indices`` array holding every bag's ids;
+* ``offsets`` with T*B+1 entries, laid out feature-major, so bag (t, b) is
+  ``indices[offsets[t*B+b] : offsets[t*B+b+1]]``;
+* every table packed row-major into one weight buffer, table after table.
+
+Random streams: ``numpy.random.default_rng([seed, purpose, ...])`` with
+purpose 0 = table shapes, 2 = bag lengths, 3 = ids (per table), 4 = per-sample
+weights, 5 = output gradient.  Embedding weights (purpose 1) come from a
+counter-based generator, ``lowbias32`` (Chris Wellons' integer hash), keyed on
+(seed, table, element index), so that any row can be regenerated on the host
+without materialising a multi-GB table, and the whole table can be built on the
+GPU with identical bits.  A weight value is an Irwin-Hall sum of four 16-bit
+uniforms, centred and scaled to the configured standard deviation (an
+approximately normal law), or a 24-bit uniform on [-1, 1).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+M32 = 0xFFFFFFFF
+
+# --------------------------------------------------------------------------
+# Workload recipes.  Shapes follow the five configurations this operator is
+# measured and checked on; see the module docstring for the stream layout.
+# --------------------------------------------------------------------------
+CONFIGS = {
+    # Three tables of different widths, a handful of bags, one forced empty bag
+    # and one forced repeated id.
+    "toy": dict(seed=100, T=3, B=4, rows=[100, 50, 20], dims=[8, 16, 4],
+                wdtype="f32", wdist=("uniform", -1.0, 1.0),
+                lengths=("uniform_int", 0, 5), ids="uniform",
+                weighted="none", lr=0.1, force_toy=True),
+    # Eight 1M-row D=128 fp32 tables, Poisson(20) bags, uniform ids.
+    "uniform": dict(seed=101, T=8, B=2048, rows=[1_000_000] * 8, dims=[128] * 8,
+                    wdtype="f32", wdist=("normal", 0.01),
+                    lengths=("poisson", 20.0), ids="uniform",
+                    weighted="none", lr=0.1),
+    # Forty features, log-uniform rows, D in {64,128,256}, fp16, geometric bags,
+    # Zipf(1.1) ids, per-sample weights on the first 20 features.
+    "mixed": dict(seed=102, T=40, B=4096, rows=("loguniform", 1e4, 1e7),
+                  dims=("choice", [64, 128, 256]), wdtype="f16",
+                  wdist=("normal", 0.01), lengths=("geometric", 30.0, 500),
+                  ids=("zipf", 1.1), weighted=("first", 20), lr=0.1),
+    # One 64-row D=128 fp16 table, 16384 bags of exactly 256 ids.
+    "hist": dict(seed=103, T=1, B=16384, rows=[64], dims=[128], wdtype="f16",
+                 wdist=("normal", 0.1), lengths=("const", 256), ids="uniform",
+                 weighted="none", lr=0.1),
+    # Four 1M-row D=128 fp32 tables, 8192 bags of 50 Zipf(1.2) ids, weighted.
+    "stress": dict(seed=104, T=4, B=8192, rows=[1_000_000] * 4, dims=[128] * 4,
+                   wdtype="f32", wdist=("normal", 0.01), lengths=("const", 50),
+                   ids=("zipf", 1.2), weighted="all", lr=0.1),
+}
+
+
+@dataclasses.dataclass
+class Problem:
+    """One seeded TBE problem instance (host arrays)."""
+    name: str
+    seed: int
+    T: int
+    B: int
+    rows: np.ndarray          # int64 [T]
+    dims: np.ndarray          # int32 [T]
+    wdtype: str               # "f32" | "f16"
+    wdist: tuple
+    weighted: np.ndarray      # bool [T]
+    lengths: np.ndarray       # int64 [T, B]
+    offsets: np.ndarray       # int64 [T*B+1]
+    indices: np.ndarray       # int64 [N]
+    psw: Optional[np.ndarray]   # float32 [N] or None (unweighted problem)
+    grad: np.ndarray          # float32 [B, sum(dims)]
+    lr: float
+
+    @property
+    def N(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def sum_D(self) -> int:
+        return int(self.dims.sum())
+
+    @property
+    def np_wdtype(self):
+        return np.float32 if self.wdtype == "f32" else np.float16
+
+    def table_of_lookup(self) -> np.ndarray:
+        """Feature id of every lookup (input bookkeeping, int64 [N])."""
+        per_t = self.lengths.sum(axis=1)
+        return np.repeat(np.arange(self.T, dtype=np.int64), per_t)
+
+    def summary(self) -> dict:
+        lens = self.lengths.ravel()
+        return dict(name=self.name, seed=self.seed, T=self.T, B=self.B, N=self.N,
+                    sum_rows=int(self.rows.sum()), sum_D=self.sum_D,
+                    weight_bytes=int((self.rows * self.dims).sum()) *
+                    (4 if self.wdtype == "f32" else 2),
+                    max_bag=int(lens.max()) if lens.size else 0,
+                    empty_bags=int((lens == 0).sum()),
+                    weighted_tables=int(self.weighted.sum()))
+
+
+# --------------------------------------------------------------------------
+# Counter-based weight generator (host numpy and device torch, same bits).
+# --------------------------------------------------------------------------
+def _mul32(x, c):
+    """(x * c) mod 2**32 for 0 <= x < 2**32, safe in signed 64-bit lanes."""
+    lo = c & 0xFFFF
+    hi = c >> 16
+    return (x * lo + (((x * hi) & 0xFFFF) << 16)) & M32
+
+
+def _lowbias32(x):
+    x = x ^ (x >> 16)
+    x = _mul32(x, 0x7FEB352D)
+    x = x ^ (x >> 15)
+    x = _mul32(x, 0x846CA68B)
+    x = x ^ (x >> 16)
+    return x
+
+
+def _stream_key(seed: int, t: int, lane: int) -> int:
+    k = (seed * 0x9E3779B9 + t * 0x85EBCA6B + lane * 0xC2B2AE35 + 0x27D4EB2F) & M32
+    return int(_lowbias32(k))
+
+
+def _ih_scale(sigma: float) -> float:
+    # standard deviation of a sum of four independent uniforms on {0..65535}
+    return sigma / math.sqrt(4.0 * (65536.0 ** 2 - 1.0) / 12.0)
+
+
+def _values_from_hash(h0, h1, wdist, lib):
+    """Map two hash words per element to a float64 value (numpy or torch)."""
+    if wdist[0] == "normal":
+        s = (h0 & 0xFFFF) + (h0 >> 16) + (h1 & 0xFFFF) + (h1 >> 16) - 131070
+        return lib_float64(s, lib) * _ih_scale(float(wdist[1]))
+    if wdist[0] == "uniform":
+        lo, hi = float(wdist[1]), float(wdist[2])
+        assert (lo, hi) == (-1.0, 1.0), "only U(-1,1) is generated"
+        u24 = h0 >> 8
+        return lib_float64(2 * u24 - (1 << 24), lib) * (2.0 ** -24)
+    raise ValueError(wdist)
+
+
+def lib_float64(x, lib):
+    if lib is np:
+        return x.astype(np.float64)
+    return x.to(lib.float64)
+
+
+def _hash_elems(e, seed, t, lib):
+    """Two 32-bit hash words per element index e (int64 array/tensor)."""
+    k0 = _stream_key(seed, t, 0)
+    k1 = _stream_key(seed, t, 1)
+    e_lo = e & M32
+    e_hi = e >> 32
+    h0 = _lowbias32(_lowbias32(e_lo ^ k0) ^ e_hi)
+    h1 = _lowbias32(_lowbias32(e_lo ^ k1) ^ e_hi)
+    return h0, h1
+
+
+def weight_rows(prob: Problem, t: int, row_ids) -> np.ndarray:
+    """Rows ``row_ids`` of table t as a [len, D_t] array of the weight dtype."""
+    D = int(prob.dims[t])
+    r = np.asarray(row_ids, dtype=np.int64).reshape(-1)
+    e = (r[:, None] * D + np.arange(D, dtype=np.int64)[None, :]).reshape(-1)
+    h0, h1 = _hash_elems(e, prob.seed, t, np)
+    v = _values_from_hash(h0, h1, prob.wdist, np).astype(np.float32)
+    if prob.wdtype == "f16":
+        v = v.astype(np.float16)
+    return v.reshape(len(r), D)
+
+
+def table_weights_torch(prob: Problem, t: int, out, chunk: int = 1 << 25):
+    """Fill the 1-D torch tensor ``out`` (rows_t*D_t elements) with table t."""
+    import torch
+    n = int(prob.rows[t]) * int(prob.dims[t])
+    assert out.numel() == n
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        e = torch.arange(s, s + m, dtype=torch.int64, device=out.device)
+        h0, h1 = _hash_elems(e, prob.seed, t, torch)
+        del e
+        v = _values_from_hash(h0, h1, prob.wdist, torch)
+        del h0, h1
+        v = v.to(torch.float32)
+        out[s:s + m].copy_(v.to(out.dtype))
+        del v
+    return out
+
+
+def table_element_starts(prob: Problem) -> np.ndarray:
+    """Element offset of each table inside the packed input buffer (int64 [T+1]).
+
+    This is the packing convention of the input format: table after table, each
+    row-major with stride D_t.
+    """
+    sizes = prob.rows.astype(np.int64) * prob.dims.astype(np.int64)
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def packed_weights_torch(prob: Problem, device):
+    """All tables packed into one 1-D torch tensor on ``device``."""
+    import torch
+    starts = table_element_starts(prob)
+    dt = torch.float32 if prob.wdtype == "f32" else torch.float16
+    w = torch.empty(int(starts[-1]), dtype=dt, device=device)
+    for t in range(prob.T):
+        table_weights_torch(prob, t, w[int(starts[t]):int(starts[t + 1])])
+    return w
+
+
+def packed_weights_np(prob: Problem) -> np.ndarray:
+    """All tables packed into one host array (small problems only)."""
+    parts = [weight_rows(prob, t, np.arange(int(prob.rows[t]))).reshape(-1)
+             for t in range(prob.T)]
+    return np.concatenate(parts) if parts else np.zeros(0, prob.np_wdtype)
+
+
+# --------------------------------------------------------------------------
+# Index / length / weight / gradient draws.
+# --------------------------------------------------------------------------
+def _zipf_bounded(rng, a: float, R: int, n: int) -> np.ndarray:
+    """n draws of Zipf(a) restricted to ranks 1..R (rejection), minus one."""
+    out = np.empty(n, dtype=np.int64)
+    filled = 0
+    while filled < n:
+        need = n - filled
+        d = rng.zipf(a, size=max(1024, int(need * 1.6) + 16))
+        d = d[(d >= 1) & (d <= R)]
+        take = min(need, d.size)
+        out[filled:filled + take] = d[:take] - 1
+        filled += take
+    return out
+
+
+def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
+                 rows_cap: Optional[int] = None, T: Optional[int] = None,
+                 weighted: Optional[str] = None, wdtype: Optional[str] = None) -> Problem:
+    """Build a seeded problem from a named recipe; optional size overrides
+    (``B``, ``T``, ``rows_cap``) give smaller instances of the same shape."""
+    cfg = dict(CONFIGS[name])
+    seed = cfg["seed"] if seed is None else int(seed)
+    Tn = cfg["T"] if T is None else int(T)
+    Bn = cfg["B"] if B is None else int(B)
+
+    rng0 = np.random.default_rng([seed, 0])
+    rspec = cfg["rows"]
+    if isinstance(rspec, tuple) and rspec[0] == "loguniform":
+        rows = np.floor(np.exp(rng0.uniform(math.log(rspec[1]), math.log(rspec[2]),
+                                            size=cfg["T"]))).astype(np.int64)
+    else:
+        rows = np.asarray(rspec, dtype=np.int64)
+    dspec = cfg["dims"]
+    if isinstance(dspec, tuple) and dspec[0] == "choice":
+        dims = rng0.choice(np.asarray(dspec[1]), size=cfg["T"]).astype(np.int32)
+    else:
+        dims = np.asarray(dspec, dtype=np.int32)
+    rows = rows[:Tn].copy()
+    dims = dims[:Tn].copy()
+    if rows_cap is not None:
+        rows = np.minimum(rows, int(rows_cap))
+
+    rng2 = np.random.default_rng([seed, 2])
+    lspec = cfg["lengths"]
+    if lspec[0] == "uniform_int":
+        lengths = rng2.integers(lspec[1], lspec[2] + 1, size=(Tn, Bn))
+    elif lspec[0] == "poisson":
+        lengths = rng2.poisson(lspec[1], size=(Tn, Bn))
+    elif lspec[0] == "geometric":
+        lengths = np.minimum(rng2.geometric(1.0 / lspec[1], size=(Tn, Bn)), lspec[2])
+    elif lspec[0] == "const":
+        lengths = np.full((Tn, Bn), lspec[1])
+    else:
+        raise ValueError(lspec)
+    lengths = lengths.astype(np.int64)
+    if cfg.get("force_toy"):
+        # bag (t=1, b=2) empty; bag (0, 0) holds at least two ids, second = first
+        if Tn > 1 and Bn > 2:
+            lengths[1, 2] = 0
+        lengths[0, 0] = max(int(lengths[0, 0]), 2)
+
+    ids = []
+    for t in range(Tn):
+        n_t = int(lengths[t].sum())
+        rng3 = np.random.default_rng([seed, 3, t])
+        R = int(rows[t])
+        if cfg["ids"] == "uniform":
+            it = rng3.integers(0, R, size=n_t, dtype=np.int64)
+        elif isinstance(cfg["ids"], tuple) and cfg["ids"][0] == "zipf":
+            it = _zipf_bounded(rng3, float(cfg["ids"][1]), R, n_t)
+        else:
+            raise ValueError(cfg["ids"])
+        if cfg.get("force_toy") and t == 0 and n_t >= 2:
+            it[1] = it[0]
+        ids.append(it)
+    indices = np.concatenate(ids) if ids else np.zeros(0, np.int64)
+    offsets = np.concatenate([[0], np.cumsum(lengths.ravel())]).astype(np.int64)
+
+    wspec = cfg["weighted"] if weighted is None else weighted
+    if wspec == "none":
+        wmask = np.zeros(Tn, dtype=bool)
+    elif wspec == "all":
+        wmask = np.ones(Tn, dtype=bool)
+    elif isinstance(wspec, tuple) and wspec[0] == "first":
+        wmask = np.arange(Tn) < wspec[1]
+    else:
+        raise ValueError(wspec)
+    N = int(offsets[-1])
+    psw = None
+    if wmask.any():
+        psw = np.random.default_rng([seed, 4]).random(N, dtype=np.float32)
+        # lookups of unweighted features carry weight exactly 1
+        tl = np.repeat(np.arange(Tn), lengths.sum(axis=1))
+        psw[~wmask[tl]] = np.float32(1.0)
+
+    grad = np.random.default_rng([seed, 5]).standard_normal(
+        (Bn, int(dims.sum())), dtype=np.float32)
+
+    return Problem(name=name, seed=seed, T=Tn, B=Bn, rows=rows, dims=dims,
+                   wdtype=cfg["wdtype"] if wdtype is None else wdtype,
+                   wdist=cfg["wdist"], weighted=wmask,
+                   lengths=lengths, offsets=offsets, indices=indices, psw=psw,
+                   grad=grad, lr=float(cfg["lr"]))
+
+
+def exact_problem(seed: int, T: int = 3, B: int = 37, max_rows: int = 40,
+                  dims=(8, 16, 4), wdtype: str = "f32", weighted: bool = True,
+                  max_len: int = 9):
+    """A small problem whose every partial sum is exactly representable.
+
+    Weights are integers in [-8, 8], per-sample weights are in
+    {0.25, 0.5, 1, 2}, output gradients are integers in [-4, 4], and the
+    learning rate is 0.5, so any summation order yields the same bits.
+    Returns (problem, packed host weights).
+    """
+    rng = np.random.default_rng([seed, 77])
+    dims = np.asarray(list(dims)[:T], dtype=np.int32)
+    rows = rng.integers(1, max_rows + 1, size=T).astype(np.int64)
+    lengths = rng.integers(0, max_len + 1, size=(T, B)).astype(np.int64)
+    ids = [rng.integers(0, rows[t], size=int(lengths[t].sum()), dtype=np.int64)
+           for t in range(T)]
+    indices = np.concatenate(ids)
+    offsets = np.concatenate([[0], np.cumsum(lengths.ravel())]).astype(np.int64)
+    N = int(offsets[-1])
+    wmask = np.ones(T, dtype=bool) if weighted else np.zeros(T, dtype=bool)
+    psw = (rng.choice(np.asarray([0.25, 0.5, 1.0, 2.0], np.float32), size=N)
+           if weighted else None)
+    grad = rng.integers(-4, 5, size=(B, int(dims.sum()))).astype(np.float32)
+    npdt = np.float32 if wdtype == "f32" else np.float16
+    packed = rng.integers(-8, 9, size=int((rows * dims).sum())).astype(npdt)
+    prob = Problem(name="exact", seed=seed, T=T, B=B, rows=rows, dims=dims,
+                   wdtype=wdtype, wdist=("explicit",), weighted=wmask,
+                   lengths=lengths, offsets=offsets, indices=indices, psw=psw,
+                   grad=grad, lr=0.5)
+    return prob, packed

@@ -1,0 +1,70 @@
+"""Glue between the seeded problems and the CPU oracle / the HIP binding.
+
+Only marshalling lives here: the arithmetic under test is in ``oracle/`` (CPU)
+and in the HIP library (GPU).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from pooling_tbe_forward_amd import datagen as dg
+
+
+def wcode(prob):
+    return oracle.F32 if prob.wdtype == "f32" else oracle.F16
+
+
+def oracle_forward(prob, packed, bag_list=None):
+    tabs = oracle.dense_tables(packed, prob.rows, prob.dims)
+    return oracle.forward(prob.T, prob.B, prob.rows, prob.dims, wcode(prob), tabs,
+                          prob.indices, prob.offsets, prob.psw, prob.weighted,
+                          bag_list=bag_list)
+
+
+def oracle_sort(prob, tau):
+    return oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, tau)
+
+
+def oracle_backward(prob, packed, keys=None, write_back=True, lr=None):
+    """Run the backward-SGD oracle on a packed host weight copy (modified in
+    place when write_back).  Returns (keys, grad_rows, new_rows)."""
+    if keys is None:
+        keys = oracle_sort(prob, 1 << 62)["unique_keys"]
+    tabs = oracle.dense_tables(packed, prob.rows, prob.dims)
+    gr, nr = oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, wcode(prob), tabs,
+                                 prob.indices, prob.offsets, prob.psw, prob.weighted,
+                                 prob.grad, prob.lr if lr is None else lr, keys,
+                                 write_back=write_back)
+    return keys, gr, nr
+
+
+def sparse_tables(prob, row_sets):
+    """Per-table sparse row stores generated on the host: row_sets[t] is a
+    sorted unique int64 array of row ids."""
+    out = []
+    for t in range(prob.T):
+        ids = np.asarray(row_sets[t], dtype=np.int64)
+        data = np.ascontiguousarray(dg.weight_rows(prob, t, ids).reshape(-1))
+        out.append((ids, data))
+    return out
+
+
+def key_to_table_row(prob, keys):
+    hcs = np.concatenate([[0], np.cumsum(prob.rows)]).astype(np.int64)
+    t = np.searchsorted(hcs, keys, side="right") - 1
+    return t, keys - hcs[t]
+
+
+def allclose_report(got, ref, rtol, atol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    return dict(ok=not bool(bad.any()), n_bad=int(bad.sum()), n=int(err.size),
+                max_abs=float(err.max()) if err.size else 0.0,
+                max_rel=float(rel.max()) if rel.size else 0.0)
+
+
+TOL = {"f32": (1e-5, 1e-6), "f16": (2e-3, 1e-3)}

@@ -1,0 +1,300 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+* the hand-worked example of tests/golden/handworked.json (every value derived
+  by hand from the FBTriton TBE article's definitions);
+* brute force: dense one-hot matrices A_t (A_t[b, r] = sum of the weights of
+  bag (t, b)'s lookups of row r), forward = A_t W_t, row gradients = A_t^T G_t;
+* library special cases: torch.nn.functional.embedding_bag(mode="sum") per
+  table, numpy's stable argsort and unique for the integer stage, numpy's
+  IEEE binary16 conversions;
+* exact-arithmetic invariants (integer weights, dyadic per-sample weights).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from pooling_tbe_forward_amd import datagen as dg
+from tests import helpers as H
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "handworked.json")))
+
+
+def _gold_problem(weighted):
+    g = GOLD
+    return dict(T=g["T"], B=g["B"], rows=np.array(g["rows"]), dims=np.array(g["dims"], np.int32),
+                indices=np.array(g["indices"]), offsets=np.array(g["offsets"]),
+                psw=np.array(g["per_sample_weights"], np.float32) if weighted else None,
+                weighted=np.ones(g["T"], bool) if weighted else None)
+
+
+@pytest.mark.parametrize("wdtype", [oracle.F32, oracle.F16])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_handworked_forward(wdtype, weighted):
+    p = _gold_problem(weighted)
+    npdt = np.float32 if wdtype == oracle.F32 else np.float16
+    packed = np.array(GOLD["packed_weights"], npdt)
+    tabs = oracle.dense_tables(packed, p["rows"], p["dims"])
+    out = oracle.forward(p["T"], p["B"], p["rows"], p["dims"], wdtype, tabs, p["indices"],
+                         p["offsets"], p["psw"], p["weighted"])
+    key = "forward_weighted" if weighted else "forward_unweighted"
+    assert np.array_equal(out, np.array(GOLD[key], np.float64))
+
+
+def test_handworked_layout_and_sort():
+    wo, do, hc = oracle.layout(GOLD["rows"], GOLD["dims"])
+    assert wo.tolist() == GOLD["weights_offsets"]
+    assert do.tolist() == GOLD["D_offsets"]
+    assert hc.tolist() == GOLD["hash_size_cumsum"]
+    r = oracle.sort_rle(GOLD["T"], GOLD["B"], GOLD["rows"], GOLD["indices"], GOLD["offsets"],
+                        GOLD["tau"])
+    for k in ("sorted_keys", "sorted_pos", "unique_keys", "run_start", "run_len",
+              "long_runs", "short_runs"):
+        assert r[k].tolist() == GOLD[k], k
+    assert r["num_runs"] == len(GOLD["unique_keys"])
+
+
+@pytest.mark.parametrize("wdtype", [oracle.F32, oracle.F16])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_handworked_backward(wdtype, weighted):
+    p = _gold_problem(weighted)
+    npdt = np.float32 if wdtype == oracle.F32 else np.float16
+    packed = np.array(GOLD["packed_weights"], npdt)
+    tabs = oracle.dense_tables(packed, p["rows"], p["dims"])
+    keys = np.array(GOLD["unique_keys"])
+    gr, nr = oracle.backward_sgd(p["T"], p["B"], p["rows"], p["dims"], wdtype, tabs,
+                                 p["indices"], p["offsets"], p["psw"], p["weighted"],
+                                 np.array(GOLD["grad_output"], np.float32), GOLD["lr"], keys,
+                                 write_back=True)
+    sfx = "weighted" if weighted else "unweighted"
+    for k, want in enumerate(GOLD["row_grads_" + sfx]):
+        assert gr[k, :len(want)].tolist() == want
+    assert packed.astype(np.float64).tolist() == GOLD["weights_after_" + sfx]
+
+
+# ---------------------------------------------------------------- brute force
+def _onehot(prob, t):
+    """A_t[b, r] = sum of per-sample weights of bag (t, b)'s lookups of row r."""
+    A = np.zeros((prob.B, int(prob.rows[t])), np.float64)
+    for b in range(prob.B):
+        s, e = prob.offsets[t * prob.B + b], prob.offsets[t * prob.B + b + 1]
+        for j in range(s, e):
+            w = float(prob.psw[j]) if (prob.psw is not None and prob.weighted[t]) else 1.0
+            A[b, prob.indices[j]] += w
+    return A
+
+
+def _tables_f64(prob, packed):
+    out, pos = [], 0
+    for t in range(prob.T):
+        n = int(prob.rows[t]) * int(prob.dims[t])
+        out.append(packed[pos:pos + n].astype(np.float64).reshape(int(prob.rows[t]), -1))
+        pos += n
+    return out
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("weighted", ["none", "all"])
+def test_bruteforce_onehot(seed, weighted):
+    prob = dg.make_problem("toy", seed=seed, weighted=weighted)
+    packed = dg.packed_weights_np(prob)
+    W = _tables_f64(prob, packed)
+    out = H.oracle_forward(prob, packed)
+    cols = np.concatenate([[0], np.cumsum(prob.dims)])
+    for t in range(prob.T):
+        A = _onehot(prob, t)
+        np.testing.assert_allclose(out[:, cols[t]:cols[t + 1]], A @ W[t], rtol=1e-13, atol=1e-15)
+
+    keys, gr, nr = H.oracle_backward(prob, packed.copy(), write_back=False)
+    tt, rr = H.key_to_table_row(prob, keys)
+    for t in range(prob.T):
+        A = _onehot(prob, t)
+        G = prob.grad[:, cols[t]:cols[t + 1]].astype(np.float64)
+        grad_t = A.T @ G
+        touched = np.flatnonzero(np.abs(A).sum(axis=0) > 0)
+        sel = np.flatnonzero(tt == t)
+        assert np.array_equal(rr[sel], touched)
+        D = int(prob.dims[t])
+        np.testing.assert_allclose(gr[sel, :D], grad_t[touched], rtol=1e-12, atol=1e-12)
+        want = W[t][touched] - np.float64(np.float32(prob.lr)) * grad_t[touched]
+        np.testing.assert_allclose(nr[sel, :D], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [5, 6])
+def test_embedding_bag_special_case(seed):
+    """One table of a TBE equals torch's EmbeddingBag(mode='sum')."""
+    prob = dg.make_problem("toy", seed=seed, weighted="all")
+    packed = dg.packed_weights_np(prob)
+    W = _tables_f64(prob, packed)
+    out = H.oracle_forward(prob, packed)
+    cols = np.concatenate([[0], np.cumsum(prob.dims)])
+    for t in range(prob.T):
+        s, e = prob.offsets[t * prob.B], prob.offsets[(t + 1) * prob.B]
+        idx = torch.from_numpy(prob.indices[s:e].copy())
+        off = torch.from_numpy(prob.offsets[t * prob.B:(t + 1) * prob.B] - s)
+        psw = torch.from_numpy(prob.psw[s:e].astype(np.float64))
+        ref = torch.nn.functional.embedding_bag(idx, torch.from_numpy(W[t]), off, mode="sum",
+                                                per_sample_weights=psw)
+        np.testing.assert_allclose(out[:, cols[t]:cols[t + 1]], ref.numpy(), rtol=1e-13,
+                                   atol=1e-15)
+
+
+@pytest.mark.parametrize("name,seed,B", [("toy", 11, None), ("stress", 12, 64),
+                                         ("mixed", 13, 32)])
+@pytest.mark.parametrize("tau", [1, 2, 4, 32, 1 << 40])
+def test_sort_rle_vs_numpy(name, seed, B, tau):
+    prob = dg.make_problem(name, seed=seed, B=B)
+    r = H.oracle_sort(prob, tau)
+    hcs = np.concatenate([[0], np.cumsum(prob.rows)])
+    keys = hcs[prob.table_of_lookup()] + prob.indices
+    perm = np.argsort(keys, kind="stable")
+    assert np.array_equal(r["sorted_pos"], perm)
+    assert np.array_equal(r["sorted_keys"], keys[perm])
+    u, counts = np.unique(keys, return_counts=True)
+    assert np.array_equal(r["unique_keys"], u)
+    assert np.array_equal(r["run_len"], counts)
+    assert np.array_equal(r["run_start"], np.concatenate([[0], np.cumsum(counts)[:-1]]))
+    assert np.array_equal(r["long_runs"], np.flatnonzero(counts >= tau))
+    assert np.array_equal(r["short_runs"], np.flatnonzero(counts < tau))
+
+
+# ---------------------------------------------------------------- fp16 codec
+def test_half_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.half_to_double(bits)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+
+
+def _half_midpoints():
+    h = np.arange(0, 0x7bff, dtype=np.uint16)
+    a = h.view(np.float16).astype(np.float64)
+    b = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    return (a + b) / 2
+
+
+def test_half_encode_matches_numpy():
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        # exact midpoints between neighbouring finite halves (ties), incl. subnormals
+        _half_midpoints()[::37],
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -25, 2.0 ** -24 * 1.5,
+         2.0 ** -14 * (1 - 2.0 ** -11)],
+    ])
+    vals = np.concatenate([vals, -vals])
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = oracle.double_to_half(vals)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+
+
+# ---------------------------------------------------------------- invariants
+@pytest.mark.parametrize("wdtype", ["f32", "f16"])
+@pytest.mark.parametrize("seed", [21, 22])
+def test_exact_invariants(wdtype, seed):
+    prob, packed = dg.exact_problem(seed, wdtype=wdtype)
+    out = H.oracle_forward(prob, packed)
+    # permuting ids inside every bag leaves the pooled result unchanged
+    rng = np.random.default_rng(seed)
+    perm = np.arange(prob.N)
+    for k in range(prob.T * prob.B):
+        s, e = prob.offsets[k], prob.offsets[k + 1]
+        perm[s:e] = s + rng.permutation(e - s)
+    p2 = dg.Problem(**{**prob.__dict__, "indices": prob.indices[perm],
+                       "psw": prob.psw[perm] if prob.psw is not None else None})
+    assert np.array_equal(H.oracle_forward(p2, packed), out)
+    # empty bags are zero
+    cols = np.concatenate([[0], np.cumsum(prob.dims)])
+    for t in range(prob.T):
+        for b in np.flatnonzero(prob.lengths[t] == 0):
+            assert not out[b, cols[t]:cols[t + 1]].any()
+    # lr = 0 leaves every weight bit-identical
+    w0 = packed.copy()
+    H.oracle_backward(prob, w0, lr=0.0)
+    assert np.array_equal(w0.view(np.uint8), packed.view(np.uint8))
+    # rows nobody read stay bit-identical; checksum identity on the gradient
+    w1 = packed.copy()
+    keys, gr, _ = H.oracle_backward(prob, w1)
+    tt, rr = H.key_to_table_row(prob, keys)
+    wo, _, _ = oracle.layout(prob.rows, prob.dims)
+    touched = np.zeros(packed.size, bool)
+    for k in range(keys.size):
+        D = int(prob.dims[tt[k]])
+        s = int(wo[tt[k]]) + int(rr[k]) * D
+        touched[s:s + D] = True
+    assert np.array_equal(w1[~touched].view(np.uint8) if w1.dtype == np.float32 else
+                          w1[~touched].view(np.uint16), packed[~touched].view(
+                              np.uint8 if w1.dtype == np.float32 else np.uint16))
+    for t in range(prob.T):
+        D = int(prob.dims[t])
+        bagw = np.zeros(prob.B)
+        for b in range(prob.B):
+            s, e = prob.offsets[t * prob.B + b], prob.offsets[t * prob.B + b + 1]
+            bagw[b] = prob.psw[s:e].astype(np.float64).sum() if prob.psw is not None else e - s
+        want = bagw @ prob.grad[:, cols[t]:cols[t] + D].astype(np.float64)
+        assert np.array_equal(gr[tt == t, :D].sum(axis=0), want)
+
+
+def test_sparse_store_equals_dense():
+    prob = dg.make_problem("stress", seed=31, B=16)
+    rowsets = [np.unique(prob.indices[prob.offsets[t * prob.B]:prob.offsets[(t + 1) * prob.B]])
+               for t in range(prob.T)]
+    sparse = H.sparse_tables(prob, rowsets)
+    out_s = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, oracle.F32, sparse,
+                           prob.indices, prob.offsets, prob.psw, prob.weighted)
+    # dense reference built row by row from the same generator
+    for t in range(prob.T):
+        assert np.array_equal(sparse[t][1].reshape(-1, 128),
+                              dg.weight_rows(prob, t, rowsets[t]))
+    bags = np.arange(prob.T * prob.B)
+    out_b = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, oracle.F32, sparse,
+                           prob.indices, prob.offsets, prob.psw, prob.weighted, bag_list=bags)
+    for k in bags:
+        t, b = divmod(int(k), prob.B)
+        assert np.array_equal(out_b[k], out_s[b, t * 128:(t + 1) * 128])
+    with pytest.raises(oracle.OracleError):
+        bad = [(ids[1:], d[128:]) for ids, d in sparse]
+        oracle.forward(prob.T, prob.B, prob.rows, prob.dims, oracle.F32, bad,
+                       prob.indices, prob.offsets, prob.psw, prob.weighted)
+
+
+def test_rejects_bad_inputs():
+    p = _gold_problem(False)
+    packed = np.array(GOLD["packed_weights"], np.float32)
+    tabs = oracle.dense_tables(packed, p["rows"], p["dims"])
+    bad_off = p["offsets"].copy()
+    bad_off[2] = 1                                   # non-monotone
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(2, 2, p["rows"], p["dims"], oracle.F32, tabs, p["indices"], bad_off)
+    bad_idx = p["indices"].copy()
+    bad_idx[0] = 3                                   # row 3 of a 3-row table
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(2, 2, p["rows"], p["dims"], oracle.F32, tabs, bad_idx, p["offsets"])
+    with pytest.raises(oracle.OracleError):
+        oracle.sort_rle(2, 2, p["rows"], bad_idx, p["offsets"], 2)
+
+
+@settings(max_examples=40, deadline=None)
+@given(seed=st.integers(0, 2 ** 31 - 1), T=st.integers(1, 3), B=st.integers(0, 9),
+       tau=st.integers(1, 6))
+def test_property_integer_stage(seed, T, B, tau):
+    prob, _ = dg.exact_problem(seed, T=T, B=B, max_rows=6, max_len=6)
+    r = H.oracle_sort(prob, tau)
+    N = prob.N
+    assert r["run_len"].sum() == N
+    assert np.all(np.diff(r["unique_keys"]) > 0)
+    assert np.array_equal(np.sort(r["sorted_pos"]), np.arange(N))
+    for k in range(r["num_runs"]):
+        s, L = r["run_start"][k], r["run_len"][k]
+        seg = r["sorted_pos"][s:s + L]
+        assert np.all(np.diff(seg) > 0)              # lookup order kept inside a run
+        assert np.all(r["sorted_keys"][s:s + L] == r["unique_keys"][k])
+    assert r["num_short"] + r["num_long"] == r["num_runs"]
