@@ -1,0 +1,177 @@
+/*
+ * tbe.h -- C ABI of the MI355X (gfx950) table-batched embedding-bag library.
+ *
+ * The operator is the one described in "FBTriton table-batched embeddings:
+ * the backward win is a threshold moved from 32 to 256" (ai.thesatyajit.com):
+ *
+ *  - Section "A lookup table that is most of the model": every table is packed
+ *    into one weight buffer; all ids go into one flat indices array; offsets
+ *    are feature-major, so bag (t, b) is indices[offsets[t*B+b] :
+ *    offsets[t*B+b+1]]; the forward writes a [B, sum D] output with table t's
+ *    pooled vector at its own column offset.  Pooling is a sum.
+ *  - Section "Why the backward is the hard half": a read row's gradient is
+ *    the sum of the output gradients of the bags that read it; the backward
+ *    linearizes (table, row) into hash_size_cumsum[t] + row, sorts, run-length
+ *    encodes, and applies exact SGD to each row once its sum is finished.
+ *  - Section "Three tiers, routed by run length": runs are routed by length
+ *    against a threshold into a short-run path and a split long-run path.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the argument says "host".
+ *  - The caller allocates and owns every device buffer.  The library
+ *    allocates device memory only inside tbe_plan_create (three small
+ *    per-table arrays) and frees it in tbe_plan_destroy.  Forward and
+ *    backward never allocate; the backward uses the caller's workspace.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it; no call synchronises the host or reads device memory
+ *    back, so results are ready when the stream says so.
+ *  - Host-checkable problems return an error before anything is enqueued.
+ *    Device-resident preconditions are the caller's (offsets[0] = 0,
+ *    nondecreasing offsets, offsets[T*B] = num_indices, 0 <= id < rows[t]);
+ *    tbe_bounds_check verifies them on the device.
+ *  - Layout: table t, row r, column d is weights[weights_offsets[t] +
+ *    r*D_t + d] with weights_offsets[t] = sum_{t'<t} rows[t']*D[t']; output
+ *    column D_offsets[t] + d; linearized key hash_size_cumsum[t] + r.
+ *  - Limits: sum(rows) < 2^32, num_indices < 2^31, T*B < 2^31, D_t <= 4096.
+ *  - No exceptions cross this boundary.
+ */
+#ifndef TBE_H
+#define TBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TBE_OK = 0,
+    TBE_EINVAL = 1,   /* bad argument (NULL pointer, negative size, bad enum, small workspace) */
+    TBE_ERANGE = 2,   /* a size exceeds the limits above */
+    TBE_ENOMEM = 3,   /* device allocation in tbe_plan_create failed */
+    TBE_EHIP = 4,     /* a HIP runtime call or kernel launch failed */
+    TBE_ENOTSUP = 5   /* a valid but unsupported combination */
+} tbe_status;
+
+typedef enum { TBE_F32 = 0, TBE_F16 = 1 } tbe_fp;   /* weight storage type */
+typedef enum { TBE_I32 = 0, TBE_I64 = 1 } tbe_int;  /* applies to indices AND offsets */
+
+typedef struct tbe_plan tbe_plan;  /* opaque; immutable after create except tuning */
+
+/* Launch knobs.  Defaults come from measurements on MI355X; tbe_set_tuning
+ * exists for sweeps and for tests that force a path. */
+typedef struct {
+    int32_t tau;               /* runs with length >= tau take the long (split) path */
+    int32_t chunk;             /* lookups per long-run chunk (split-K) */
+    int32_t hist_mode;         /* 0 auto, 1 never, 2 always for eligible tables */
+    int32_t hist_min_mean_len; /* auto: histogram path when N/(T*B) >= this */
+    int32_t fwd_bags_per_wave; /* forward: consecutive bags handled by one wavefront */
+    int32_t bwd_runs_per_wave; /* backward: short runs handled by one wavefront per batch */
+    int32_t reserved[10];
+} tbe_tuning;
+
+/* Device pointers into a backward workspace (valid until the workspace is
+ * reused).  Every count lives in device memory: counts[0] = number of runs,
+ * counts[1] = short runs, counts[2] = long runs, counts[3] = long-run chunks. */
+typedef struct {
+    uint32_t* sorted_keys;   /* [N]   keys ascending; ties keep lookup order        */
+    uint32_t* sorted_pos;    /* [N]   lookup position j of each sorted entry        */
+    uint32_t* unique_keys;   /* [N]   first counts[0] valid, strictly ascending     */
+    uint32_t* run_start;     /* [N+1] first sorted position of each run             */
+    uint32_t* run_len;       /* [N]   lookups in each run                           */
+    uint32_t* short_runs;    /* [N]   run ids with len < tau, ascending             */
+    uint32_t* long_runs;     /* [N]   run ids with len >= tau, ascending            */
+    uint32_t* counts;        /* [4]                                                 */
+} tbe_sort_view;
+
+/*
+ * Create a plan for T tables.  rows/dims (host [T]): rows and width of each
+ * table (rows >= 0, 1 <= D <= 4096).  weight_dtype: tbe_fp.  index_dtype:
+ * tbe_int.  weighted (host [T] or NULL): which tables apply per-sample
+ * weights when a call passes them (NULL = every table).  On success *out owns
+ * three small device arrays (per-table descriptors) on the current device.
+ * Errors: TBE_EINVAL, TBE_ERANGE, TBE_ENOMEM, TBE_EHIP.
+ */
+tbe_status tbe_plan_create(int32_t T, const int64_t* rows, const int32_t* dims,
+                           int32_t weight_dtype, int32_t index_dtype,
+                           const uint8_t* weighted, tbe_plan** out);
+
+/* Free the plan and its device arrays.  NULL is a no-op.  The caller must
+ * make sure no enqueued work still uses the plan. */
+void tbe_plan_destroy(tbe_plan* plan);
+
+/* Host copies of the layout prefix sums: weights_offsets [T] (elements),
+ * D_offsets [T+1], hash_size_cumsum [T+1].  Any pointer may be NULL. */
+tbe_status tbe_plan_layout(const tbe_plan* plan, int64_t* weights_offsets,
+                           int64_t* D_offsets, int64_t* hash_size_cumsum);
+
+/*
+ * Forward pooled sum (section "A lookup table that is most of the model";
+ * the small-table path is section "The forward: a general gather and one
+ * clever special case").
+ *   weights  [sum rows*D] of weight_dtype (read only)
+ *   indices  [num_indices] of index_dtype
+ *   offsets  [T*B+1] of index_dtype, feature-major
+ *   per_sample_weights [num_indices] fp32 or NULL (applied on weighted tables)
+ *   output   [B, sum D] fp32; every element is written (empty bags -> 0)
+ * Accumulation is fp32.  B = 0 is a no-op.
+ */
+tbe_status tbe_forward(const tbe_plan* plan, int32_t B, const void* weights,
+                       const void* indices, int64_t num_indices, const void* offsets,
+                       const float* per_sample_weights, float* output, void* stream);
+
+/* Bytes of workspace tbe_backward_sgd / tbe_sort_rle need for (B,
+ * num_indices) under the plan's current tuning.  0 on invalid arguments. */
+size_t tbe_backward_workspace_bytes(const tbe_plan* plan, int32_t B, int64_t num_indices);
+
+/*
+ * Backward + exact SGD, in place (section "Why the backward is the hard
+ * half"; routing by run length from section "Three tiers, routed by run
+ * length").  For every row r of table t read by some lookup,
+ *   W_t[r] <- W_t[r] - lr * sum_{lookups j of (t, r)} w_j * grad_output[b(j), D_offsets[t] : +D_t]
+ * with w_j the per-sample weight (1 on unweighted tables or when NULL).
+ * Rows nobody read are not touched.  grad_output is [B, sum D] fp32.
+ * Accumulation is fp64 for fp32 tables and fp32 for fp16 tables; the update
+ * is rounded once to the storage type.  The result is deterministic.
+ * workspace: device buffer of at least tbe_backward_workspace_bytes bytes,
+ * 256-byte aligned.
+ */
+tbe_status tbe_backward_sgd(const tbe_plan* plan, int32_t B, void* weights,
+                            const void* indices, int64_t num_indices, const void* offsets,
+                            const float* per_sample_weights, const float* grad_output,
+                            float lr, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward's integer stage alone: linearize, stable radix sort,
+ * run-length encode, classify against tuning.tau.  Fills *view (host struct)
+ * with device pointers into the workspace.
+ */
+tbe_status tbe_sort_rle(const tbe_plan* plan, int32_t B, const void* indices,
+                        int64_t num_indices, const void* offsets, void* workspace,
+                        size_t workspace_bytes, tbe_sort_view* view, void* stream);
+
+/*
+ * Device-side input check: *error_count (device int64, overwritten) receives
+ * the number of violations: offsets[0] != 0, decreasing offsets,
+ * offsets[T*B] != num_indices, ids outside [0, rows[t]).  The caller syncs
+ * the stream to read it.
+ */
+tbe_status tbe_bounds_check(const tbe_plan* plan, int32_t B, const void* indices,
+                            int64_t num_indices, const void* offsets,
+                            int64_t* error_count, void* stream);
+
+/* Read / replace the plan's launch knobs (values are validated). */
+tbe_status tbe_get_tuning(const tbe_plan* plan, tbe_tuning* tuning);
+tbe_status tbe_set_tuning(tbe_plan* plan, const tbe_tuning* tuning);
+
+/* Static English text for a status code. */
+const char* tbe_status_string(tbe_status status);
+
+/* ABI version (major*10000 + minor*100 + patch). */
+int32_t tbe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TBE_H */

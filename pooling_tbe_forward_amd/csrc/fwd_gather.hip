@@ -1,0 +1,178 @@
+// Forward pooled gather-sum for gfx950.
+//
+// Operator: section "A lookup table that is most of the model" of the FBTriton
+// TBE article -- bag (t, b) = indices[offsets[t*B+b] : offsets[t*B+b+1]], its
+// rows (times the per-sample weight on weighted tables) summed into output row
+// b at column D_offsets[t]; an empty bag writes zeros.
+//
+// Design (section "The forward: a general gather and one clever special case"
+// describes the latency problem: a gather is a dependent chain, index then
+// row, so several chains must be in flight):
+//  * one 64-lane wavefront owns one bag at a time; a row of D elements is
+//    covered by L = D/VEC lanes (16-byte loads), so the wave holds G = 64/L
+//    row slots side by side and each lane keeps U independent row loads in
+//    flight: G*U rows per wavefront per step;
+//  * the bag's ids are fetched with one coalesced load per 64 ids and handed
+//    to the row slots through cross-lane permutes, so the only serial chain is
+//    offsets -> ids -> rows;
+//  * accumulation in fp32 VGPRs; slots are folded with lane swaps at the end.
+#include "tbe_internal.h"
+
+namespace tbe {
+namespace {
+
+template <typename T, int N>
+struct alignas(sizeof(T) * N) Pack {
+    T v[N];
+};
+
+template <typename WT>
+__device__ __forceinline__ float to_f32(WT x) { return static_cast<float>(x); }
+
+template <typename IT>
+__device__ __forceinline__ int64_t lane_bcast(IT v, int src) {
+    return static_cast<int64_t>(__shfl(v, src));
+}
+
+template <typename WT, typename IT, int VEC, int U, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_fwd_gather(
+    const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, int32_t sumD,
+    const WT* __restrict__ weights, const IT* __restrict__ indices,
+    const IT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
+    uint32_t bags_per_wave, int32_t hist_active)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) +
+                                                         (threadIdx.x >> 6));
+    const uint32_t g0 = wave * bags_per_wave;
+    if (g0 >= total_bags) return;
+    const uint32_t g1 = min(g0 + bags_per_wave, total_bags);
+
+    for (uint32_t g = g0; g < g1; ++g) {
+        const uint32_t t = g / B;
+        const uint32_t b = g - t * B;
+        const TableDesc d = tables[t];
+        if (hist_active && (d.flags & TD_HIST_OK) && !(WEIGHTED && (d.flags & TD_WEIGHTED)))
+            continue;  // pooled by the histogram kernel
+        const bool tw = WEIGHTED && (d.flags & TD_WEIGHTED);
+        const int64_t s = static_cast<int64_t>(offsets[g]);
+        const int64_t e = static_cast<int64_t>(offsets[g + 1]);
+        const int D = d.D;
+        const int lanes = D / VEC;
+        const int lpr_log2 = lanes >= 64 ? 6 : (lanes <= 1 ? 0 : 32 - __builtin_clz(lanes - 1));
+        const int g_log2 = 6 - lpr_log2;
+        const int grp = lane >> lpr_log2;
+        const int col = (lane & ((1 << lpr_log2) - 1)) * VEC;
+        const WT* __restrict__ tb = weights + d.w_off;
+        float* __restrict__ orow = out + static_cast<int64_t>(b) * sumD + d.out_off;
+
+        for (int c0 = 0; c0 < D; c0 += 64 * VEC) {
+            const int c = c0 + col;
+            const bool active = c < D;
+            float acc[VEC];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
+
+            for (int64_t base = s; base < e; base += 64) {
+                const int n = (e - base) < 64 ? static_cast<int>(e - base) : 64;
+                IT my_id = 0;
+                float my_w = 1.f;
+                if (lane < n) {
+                    my_id = indices[base + lane];
+                    if (tw) my_w = psw[base + lane];
+                }
+                for (int r0 = 0; r0 < n; r0 += (U << g_log2)) {
+                    Pack<WT, VEC> v[U];
+                    float w[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int r = r0 + (u << g_log2) + grp;
+                        const int64_t row = lane_bcast(my_id, r & 63);
+                        w[u] = tw ? __shfl(my_w, r & 63) : 1.f;
+                        if (r < n && active) {
+                            v[u] = *reinterpret_cast<const Pack<WT, VEC>*>(tb + row * D + c);
+                        } else {
+#pragma unroll
+                            for (int k = 0; k < VEC; ++k) v[u].v[k] = WT(0);
+                            w[u] = 0.f;
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            if (tw)
+                                acc[k] = fmaf(w[u], to_f32(v[u].v[k]), acc[k]);
+                            else
+                                acc[k] += to_f32(v[u].v[k]);
+                        }
+                    }
+                }
+            }
+            // fold the G row slots: lanes that differ only in the slot bits
+            for (int m = 32; m >= (1 << lpr_log2); m >>= 1) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc[k] += __shfl_xor(acc[k], m);
+            }
+            if (grp == 0 && active) {
+                Pack<float, VEC> o;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) o.v[k] = acc[k];
+                *reinterpret_cast<Pack<float, VEC>*>(orow + c) = o;
+            }
+        }
+    }
+}
+
+template <typename WT, typename IT, int VEC>
+hipError_t launch_vec(const FwdArgs& a)
+{
+    const tbe_plan* p = a.plan;
+    const uint32_t total = static_cast<uint32_t>(p->T) * static_cast<uint32_t>(a.B);
+    const uint32_t bpw = static_cast<uint32_t>(max(1, p->tuning.fwd_bags_per_wave));
+    const uint32_t waves = (total + bpw - 1) / bpw;
+    const uint32_t wpb = 4;
+    const uint32_t blocks = (waves + wpb - 1) / wpb;
+    constexpr int U = (VEC * sizeof(WT) >= 16) ? 4 : 8;
+    if (blocks == 0) return hipSuccess;
+    if (a.psw)
+        hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, true>), dim3(blocks), dim3(wpb * 64), 0,
+                           a.stream, p->d_tables, static_cast<uint32_t>(a.B), total, p->sum_D,
+                           static_cast<const WT*>(a.weights), static_cast<const IT*>(a.indices),
+                           static_cast<const IT*>(a.offsets), a.psw, a.out, bpw,
+                           a.hist_active ? 1 : 0);
+    else
+        hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, false>), dim3(blocks), dim3(wpb * 64), 0,
+                           a.stream, p->d_tables, static_cast<uint32_t>(a.B), total, p->sum_D,
+                           static_cast<const WT*>(a.weights), static_cast<const IT*>(a.indices),
+                           static_cast<const IT*>(a.offsets), a.psw, a.out, bpw,
+                           a.hist_active ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <typename WT, typename IT>
+hipError_t launch_wt_it(const FwdArgs& a)
+{
+    switch (a.vec) {
+    case 1: return launch_vec<WT, IT, 1>(a);
+    case 2: return launch_vec<WT, IT, 2>(a);
+    case 4: return launch_vec<WT, IT, 4>(a);
+    case 8:
+        if constexpr (sizeof(WT) == 2) return launch_vec<WT, IT, 8>(a);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_gather(const FwdArgs& a)
+{
+    const bool f16 = a.plan->wdtype == TBE_F16;
+    const bool i64 = a.plan->idtype == TBE_I64;
+    if (f16)
+        return i64 ? launch_wt_it<_Float16, int64_t>(a) : launch_wt_it<_Float16, int32_t>(a);
+    return i64 ? launch_wt_it<float, int64_t>(a) : launch_wt_it<float, int32_t>(a);
+}
+
+}  // namespace tbe

@@ -1,0 +1,296 @@
+// C ABI of libtbe: argument validation, plan construction, kernel dispatch.
+// Every entry point is declared and documented in include/tbe.h.
+#include <new>
+
+#include "tbe_internal.h"
+
+using namespace tbe;
+
+namespace {
+
+constexpr int64_t kMaxD = 4096;
+
+tbe_tuning default_tuning()
+{
+    tbe_tuning t{};
+    t.tau = 256;              // long-run threshold (runs >= tau are split)
+    t.chunk = 256;            // lookups per long-run chunk
+    t.hist_mode = 0;          // auto
+    t.hist_min_mean_len = 64; // histogram path pays once bags are this long
+    t.fwd_bags_per_wave = 1;
+    t.bwd_runs_per_wave = 0;
+    return t;
+}
+
+bool valid_dtype(int32_t wd, int32_t id)
+{
+    return (wd == TBE_F32 || wd == TBE_F16) && (id == TBE_I32 || id == TBE_I64);
+}
+
+tbe_status check_call(const tbe_plan* p, int32_t B, int64_t num_indices, const void* indices,
+                      const void* offsets)
+{
+    if (!p || B < 0 || num_indices < 0) return TBE_EINVAL;
+    if (B > 0 && !offsets) return TBE_EINVAL;
+    if (num_indices > 0 && !indices) return TBE_EINVAL;
+    if (num_indices >= (int64_t(1) << 31)) return TBE_ERANGE;
+    if (int64_t(p->T) * B >= (int64_t(1) << 31)) return TBE_ERANGE;
+    return TBE_OK;
+}
+
+bool use_hist(const tbe_plan* p, int32_t B, int64_t N)
+{
+    if (p->tuning.hist_mode == 1) return false;
+    bool any = false;
+    for (int t = 0; t < p->T; ++t) any |= (p->h_tables[t].flags & TD_HIST_OK) != 0;
+    if (!any) return false;
+    if (p->tuning.hist_mode == 2) return true;
+    const int64_t bags = int64_t(p->T) * B;
+    return bags > 0 && N >= int64_t(p->tuning.hist_min_mean_len) * bags;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tbe_version(void) { return 100; }
+
+const char* tbe_status_string(tbe_status s)
+{
+    switch (s) {
+    case TBE_OK: return "ok";
+    case TBE_EINVAL: return "invalid argument";
+    case TBE_ERANGE: return "size out of supported range";
+    case TBE_ENOMEM: return "device allocation failed";
+    case TBE_EHIP: return "HIP runtime error";
+    case TBE_ENOTSUP: return "unsupported combination";
+    }
+    return "unknown status";
+}
+
+tbe_status tbe_plan_create(int32_t T, const int64_t* rows, const int32_t* dims,
+                           int32_t weight_dtype, int32_t index_dtype, const uint8_t* weighted,
+                           tbe_plan** out)
+{
+    if (!out) return TBE_EINVAL;
+    *out = nullptr;
+    if (T < 1 || !rows || !dims || !valid_dtype(weight_dtype, index_dtype)) return TBE_EINVAL;
+    tbe_plan* p = new (std::nothrow) tbe_plan();
+    if (!p) return TBE_ENOMEM;
+    p->T = T;
+    p->wdtype = weight_dtype;
+    p->idtype = index_dtype;
+    p->tuning = default_tuning();
+    int64_t w = 0, dsum = 0, h = 0;
+    for (int t = 0; t < T; ++t) {
+        if (rows[t] < 0 || dims[t] < 1) { delete p; return TBE_EINVAL; }
+        if (dims[t] > kMaxD) { delete p; return TBE_ERANGE; }
+        p->rows.push_back(rows[t]);
+        p->dims.push_back(dims[t]);
+        p->weighted.push_back(weighted ? (weighted[t] ? 1 : 0) : 1);
+        p->w_off.push_back(w);
+        p->D_off.push_back(dsum);
+        p->hash_off.push_back(h);
+        w += rows[t] * dims[t];
+        dsum += dims[t];
+        h += rows[t];
+        if (dims[t] > p->max_D) p->max_D = dims[t];
+    }
+    p->D_off.push_back(dsum);
+    p->hash_off.push_back(h);
+    if (h >= (int64_t(1) << 32) || dsum >= (int64_t(1) << 31)) { delete p; return TBE_ERANGE; }
+    p->sum_rows = h;
+    p->sum_D = static_cast<int32_t>(dsum);
+
+    p->h_tables.resize(T);
+    std::vector<uint32_t> hoff(T + 1);
+    for (int t = 0; t < T; ++t) {
+        TableDesc& d = p->h_tables[t];
+        d.w_off = p->w_off[t];
+        d.hash_off = static_cast<uint32_t>(p->hash_off[t]);
+        d.rows = static_cast<uint32_t>(p->rows[t]);
+        d.D = p->dims[t];
+        d.out_off = static_cast<int32_t>(p->D_off[t]);
+        d.flags = 0;
+        if (p->weighted[t]) d.flags |= TD_WEIGHTED;
+        if (weight_dtype == TBE_F16 && p->rows[t] >= 1 && p->rows[t] <= kHistMaxRows &&
+            p->dims[t] <= kHistMaxD)
+            d.flags |= TD_HIST_OK;
+        d.pad = 0;
+        hoff[t] = static_cast<uint32_t>(p->hash_off[t]);
+    }
+    hoff[T] = static_cast<uint32_t>(h);
+    if (hipGetDevice(&p->device) != hipSuccess) { delete p; return TBE_EHIP; }
+    if (hipMalloc(&p->d_tables, sizeof(TableDesc) * T) != hipSuccess) {
+        delete p;
+        return TBE_ENOMEM;
+    }
+    if (hipMalloc(&p->d_hash_off, sizeof(uint32_t) * (T + 1)) != hipSuccess) {
+        (void)hipFree(p->d_tables);
+        delete p;
+        return TBE_ENOMEM;
+    }
+    if (hipMemcpy(p->d_tables, p->h_tables.data(), sizeof(TableDesc) * T,
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(p->d_hash_off, hoff.data(), sizeof(uint32_t) * (T + 1),
+                  hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(p->d_tables);
+        (void)hipFree(p->d_hash_off);
+        delete p;
+        return TBE_EHIP;
+    }
+    *out = p;
+    return TBE_OK;
+}
+
+void tbe_plan_destroy(tbe_plan* p)
+{
+    if (!p) return;
+    (void)hipFree(p->d_tables);
+    (void)hipFree(p->d_hash_off);
+    delete p;
+}
+
+tbe_status tbe_plan_layout(const tbe_plan* p, int64_t* weights_offsets, int64_t* D_offsets,
+                           int64_t* hash_size_cumsum)
+{
+    if (!p) return TBE_EINVAL;
+    for (int t = 0; t <= p->T; ++t) {
+        if (weights_offsets && t < p->T) weights_offsets[t] = p->w_off[t];
+        if (D_offsets) D_offsets[t] = p->D_off[t];
+        if (hash_size_cumsum) hash_size_cumsum[t] = p->hash_off[t];
+    }
+    return TBE_OK;
+}
+
+tbe_status tbe_get_tuning(const tbe_plan* p, tbe_tuning* t)
+{
+    if (!p || !t) return TBE_EINVAL;
+    *t = p->tuning;
+    return TBE_OK;
+}
+
+tbe_status tbe_set_tuning(tbe_plan* p, const tbe_tuning* t)
+{
+    if (!p || !t) return TBE_EINVAL;
+    if (t->tau < 1 || t->chunk < 1 || t->hist_mode < 0 || t->hist_mode > 2 ||
+        t->hist_min_mean_len < 0 || t->fwd_bags_per_wave < 1 || t->fwd_bags_per_wave > 1024)
+        return TBE_EINVAL;
+    p->tuning = *t;
+    return TBE_OK;
+}
+
+tbe_status tbe_forward(const tbe_plan* p, int32_t B, const void* weights, const void* indices,
+                       int64_t num_indices, const void* offsets, const float* psw, float* output,
+                       void* stream)
+{
+    tbe_status st = check_call(p, B, num_indices, indices, offsets);
+    if (st != TBE_OK) return st;
+    if (B == 0) return TBE_OK;
+    if (!weights || !output) return TBE_EINVAL;
+    const size_t wbytes = p->wdtype == TBE_F32 ? 4 : 2;
+    int vec = static_cast<int>(16 / wbytes);
+    for (int t = 0; t < p->T; ++t)
+        while (p->dims[t] % vec) vec >>= 1;
+    while (vec > 1 && (reinterpret_cast<uintptr_t>(weights) % (vec * wbytes) ||
+                       reinterpret_cast<uintptr_t>(output) % (vec * 4)))
+        vec >>= 1;
+    FwdArgs a{p, B, weights, indices, offsets, psw, output, vec, use_hist(p, B, num_indices),
+              static_cast<hipStream_t>(stream)};
+    if (a.hist_active) {
+        if (launch_fwd_hist(a) != hipSuccess) return TBE_EHIP;
+    }
+    if (launch_fwd_gather(a) != hipSuccess) return TBE_EHIP;
+    return TBE_OK;
+}
+
+size_t tbe_backward_workspace_bytes(const tbe_plan* p, int32_t B, int64_t num_indices)
+{
+    if (check_call(p, B, num_indices, reinterpret_cast<const void*>(1),
+                   reinterpret_cast<const void*>(1)) != TBE_OK)
+        return 0;
+    return bwd_layout(p, B, num_indices).total;
+}
+
+static tbe_status prepare_bwd(const tbe_plan* p, int32_t B, const void* indices,
+                              int64_t num_indices, const void* offsets, void* workspace,
+                              size_t workspace_bytes, void* stream, BwdArgs& a)
+{
+    tbe_status st = check_call(p, B, num_indices, indices, offsets);
+    if (st != TBE_OK) return st;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TBE_EINVAL;
+    a.plan = p;
+    a.B = B;
+    a.N = num_indices;
+    a.indices = indices;
+    a.offsets = offsets;
+    a.psw = nullptr;
+    a.grad = nullptr;
+    a.weights = nullptr;
+    a.lr = 0.f;
+    a.ws = static_cast<char*>(workspace);
+    a.L = bwd_layout(p, B, num_indices);
+    a.stream = static_cast<hipStream_t>(stream);
+    a.final_buf = 0;
+    if (workspace_bytes < a.L.total) return TBE_EINVAL;
+    return TBE_OK;
+}
+
+tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const void* indices,
+                            int64_t num_indices, const void* offsets, const float* psw,
+                            const float* grad_output, float lr, void* workspace,
+                            size_t workspace_bytes, void* stream)
+{
+    if (p && B == 0 && num_indices >= 0) return TBE_OK;
+    BwdArgs a;
+    tbe_status st = prepare_bwd(p, B, indices, num_indices, offsets, workspace,
+                                workspace_bytes, stream, a);
+    if (st != TBE_OK) return st;
+    if (!weights || !grad_output) return TBE_EINVAL;
+    if (num_indices == 0) return TBE_OK;
+    a.psw = psw;
+    a.grad = grad_output;
+    a.weights = weights;
+    a.lr = lr;
+    if (run_sort_rle(a) != hipSuccess) return TBE_EHIP;
+    if (run_segment_sgd(a) != hipSuccess) return TBE_EHIP;
+    return TBE_OK;
+}
+
+tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64_t num_indices,
+                        const void* offsets, void* workspace, size_t workspace_bytes,
+                        tbe_sort_view* view, void* stream)
+{
+    if (!view) return TBE_EINVAL;
+    BwdArgs a;
+    tbe_status st = prepare_bwd(p, B, indices, num_indices, offsets, workspace,
+                                workspace_bytes, stream, a);
+    if (st != TBE_OK) return st;
+    if (run_sort_rle(a) != hipSuccess) return TBE_EHIP;
+    char* ws = a.ws;
+    const BwdLayout& L = a.L;
+    view->sorted_keys = reinterpret_cast<uint32_t*>(ws + L.off_keys[a.final_buf]);
+    view->sorted_pos = reinterpret_cast<uint32_t*>(ws + L.off_vals[a.final_buf]);
+    view->unique_keys = reinterpret_cast<uint32_t*>(ws + L.off_unique);
+    view->run_start = reinterpret_cast<uint32_t*>(ws + L.off_run_start);
+    view->run_len = reinterpret_cast<uint32_t*>(ws + L.off_run_len);
+    view->short_runs = reinterpret_cast<uint32_t*>(ws + L.off_short);
+    view->long_runs = reinterpret_cast<uint32_t*>(ws + L.off_long);
+    view->counts = reinterpret_cast<uint32_t*>(ws + L.off_counts);
+    return TBE_OK;
+}
+
+tbe_status tbe_bounds_check(const tbe_plan* p, int32_t B, const void* indices,
+                            int64_t num_indices, const void* offsets, int64_t* error_count,
+                            void* stream)
+{
+    tbe_status st = check_call(p, B, num_indices, indices, offsets);
+    if (st != TBE_OK) return st;
+    if (!error_count) return TBE_EINVAL;
+    if (launch_bounds_check(p, B, indices, num_indices, offsets, error_count,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TBE_EHIP;
+    return TBE_OK;
+}
+
+}  // extern "C"
