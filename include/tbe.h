@@ -32,7 +32,7 @@
  *  - Layout: table t, row r, column d is weights[weights_offsets[t] +
  *    r*D_t + d] with weights_offsets[t] = sum_{t'<t} rows[t']*D[t']; output
  *    column D_offsets[t] + d; linearized key hash_size_cumsum[t] + r.
- *  - Limits: sum(rows) < 2^32, num_indices < 2^31, T*B < 2^31, D_t <= 4096.
+ *  - Limits: sum(rows) < 2^32, num_indices < 2^30, T*B < 2^31, D_t <= 4096.
  *  - No exceptions cross this boundary.
  */
 #ifndef TBE_H
@@ -73,7 +73,9 @@ typedef struct {
 
 /* Device pointers into a backward workspace (valid until the workspace is
  * reused).  Every count lives in device memory: counts[0] = number of runs,
- * counts[1] = short runs, counts[2] = long runs, counts[3] = long-run chunks. */
+ * counts[1] = short runs, counts[2] = long runs, counts[3] = long-run chunks,
+ * counts[4] = error word (nonzero: the call's results are invalid; it stays
+ * set until tbe_workspace_init). */
 typedef struct {
     uint32_t* sorted_keys;   /* [N]   keys ascending; ties keep lookup order        */
     uint32_t* sorted_pos;    /* [N]   lookup position j of each sorted entry        */
@@ -82,7 +84,7 @@ typedef struct {
     uint32_t* run_len;       /* [N]   lookups in each run                           */
     uint32_t* short_runs;    /* [N]   run ids with len < tau, ascending             */
     uint32_t* long_runs;     /* [N]   run ids with len >= tau, ascending            */
-    uint32_t* counts;        /* [4]                                                 */
+    uint32_t* counts;        /* [5]                                                 */
 } tbe_sort_view;
 
 /*
@@ -126,6 +128,18 @@ tbe_status tbe_forward(const tbe_plan* plan, int32_t B, const void* weights,
 size_t tbe_backward_workspace_bytes(const tbe_plan* plan, int32_t B, int64_t num_indices);
 
 /*
+ * Prepare a backward workspace before its first use (enqueued on `stream`).
+ * The first 4160 bytes of a workspace are a control block (tile tickets and
+ * digit totals of the sort, counts, an error word) that must be zero when a
+ * call starts; every tbe_backward_sgd / tbe_sort_rle call leaves it zero
+ * again, so one init per allocation is enough, whatever plan, B or
+ * num_indices later calls use.  A zero-filled allocation is also initialised.
+ * Errors: TBE_EINVAL (NULL, not 256-byte aligned, fewer than 4160 bytes),
+ * TBE_EHIP.
+ */
+tbe_status tbe_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward + exact SGD, in place (section "Why the backward is the hard
  * half"; routing by run length from section "Three tiers, routed by run
  * length").  For every row r of table t read by some lookup,
@@ -135,7 +149,8 @@ size_t tbe_backward_workspace_bytes(const tbe_plan* plan, int32_t B, int64_t num
  * Accumulation is fp64 for fp32 tables and fp32 for fp16 tables; the update
  * is rounded once to the storage type.  The result is deterministic.
  * workspace: device buffer of at least tbe_backward_workspace_bytes bytes,
- * 256-byte aligned.
+ * 256-byte aligned, initialised once by tbe_workspace_init.  Calls that
+ * share a workspace must not overlap (same stream, or ordered by events).
  */
 tbe_status tbe_backward_sgd(const tbe_plan* plan, int32_t B, void* weights,
                             const void* indices, int64_t num_indices, const void* offsets,

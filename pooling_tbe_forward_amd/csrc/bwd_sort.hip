@@ -6,26 +6,31 @@
 // hash_size_cumsum[t] + row (rows of different tables never collide), the
 // keys are sorted so that every row's contributors sit next to each other,
 // and a run-length encode turns each row into one independent unit of work.
-// Section "Three tiers, routed by run length": runs are split against a
-// length threshold on the device, with counts that never go back to the host.
+// Section "Three tiers, routed by run length": runs are classified against a
+// length threshold on the device, and the counts never go back to the host.
+// Section "Using it, and the import that stops you": per-sample weights must
+// stay paired with their lookup, so the sort is stable, carries the lookup
+// position j as payload, and its last pass gathers the sample id and the
+// per-sample weight of every sorted entry -- nothing is ever sorted twice.
 //
-// Section "Using it, and the import that stops you" shows why the sort must be
-// stable and sorted only once: per-sample weights must stay paired with their
-// lookup.  Here the sort carries the lookup position j as payload, is stable,
-// and its last pass gathers the sample id and per-sample weight of every
-// sorted entry, so nothing is ever re-sorted.
+// Kernels (caller's stream, no host synchronisation):
+//   k_prep      per block of bags: key[j], sample[j] (the bag's sample id),
+//               digit histograms of every radix pass (LDS, then one global
+//               add per digit), and clears the look-back status words
+//   k_onesweep  one launch per radix pass (8-bit digits, only the
+//               ceil(log2(sum rows)) key bits are sorted): a tile takes a
+//               ticket in launch order, ranks its keys stably (wave ballots
+//               find equal digits, per-wave LDS counters order them), looks
+//               back over earlier tiles' published digit counts for its
+//               offsets, and scatters key + payload
+//   k_rle       one launch: run heads, lengths (galloping search), the short /
+//               long split and the long-run chunk counts; tile offsets come
+//               from the same look-back, so the run lists stay in key order
 //
-// Kernels (all on the caller's stream, no host synchronisation):
-//   k_linearize    one wavefront per bag: key[j], sample[j]; clears counters
-//   per radix pass (digit of <= 8 bits, only ceil(log2(sum rows)) bits):
-//     k_radix_up   per-tile digit counts, digit-major, plus global totals
-//     k_radix_scan one wavefront per digit: exclusive offsets of every tile
-//     k_radix_down stable scatter; ranks from wave ballots (a wave-level
-//                  match of equal digits) and per-wave LDS counters
-//   k_rle_count    per-tile run heads / long runs / long-run chunks
-//   k_rle_scan     one workgroup: tile prefixes and the device totals
-//   k_rle_write    unique keys, run starts and lengths, ordered short and long
-//                  run lists (ordered compaction, so the lists ascend)
+// Look-back waits are bounded: a tile that waits more than ~2^24 polls for a
+// predecessor raises an error flag and goes on, so a kernel always ends.
+// Tile tickets, digit totals and the error word live in the workspace's control
+// block, which is zero when a call starts and zero again when it ends.
 #include "tbe_internal.h"
 
 namespace tbe {
@@ -35,6 +40,11 @@ constexpr int kRadix = 256;
 constexpr int kSortWaves = 4;
 constexpr int kRleItems = 4;
 constexpr int kRleTile = 256 * kRleItems;
+constexpr uint32_t kFlagAgg = 1u << 30;
+constexpr uint32_t kFlagInc = 2u << 30;
+constexpr uint32_t kValMask = (1u << 30) - 1u;
+constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr int kPrepMaxBags = 2048;   // bags per k_prep block (LDS offsets cache)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -43,7 +53,6 @@ int sort_rounds(int64_t N) { return N > (int64_t(1) << 21) ? 16 : 8; }
 
 BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
 {
-    (void)B;
     BwdLayout L;
     L.N = N;
     int bits = 0;
@@ -60,15 +69,27 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.sort_blocks = static_cast<int32_t>((N + L.sort_tile - 1) / L.sort_tile);
     L.rle_tile = kRleTile;
     L.rle_blocks = static_cast<int32_t>((N + kRleTile - 1) / kRleTile);
+    const int64_t total_bags = int64_t(p->T) * B;
+    int64_t pb = total_bags / 64;
+    if (pb > 128) pb = 128;
+    const int64_t need = (total_bags + kPrepMaxBags - 1) / kPrepMaxBags;
+    if (pb < need) pb = need;
+    if (pb < 1) pb = 1;
+    L.prep_blocks = static_cast<int32_t>(pb);
+    L.prep_bags = static_cast<int32_t>((total_bags + pb - 1) / pb);
     const int64_t tau = p->tuning.tau > 0 ? p->tuning.tau : 1;
     const int64_t C = p->tuning.chunk > 0 ? p->tuning.chunk : 1;
     int64_t mc = N / C + N / tau + 1;
     if (mc > N) mc = N;
     L.max_chunks = mc;
+    int64_t ml = N / tau + 1;
+    if (ml > N) ml = N;
+    L.max_long = ml;
 
     const size_t n4 = align256(size_t(N + 1) * 4);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+    L.off_ctl = take(size_t(kCtlWords) * 4);   // fixed at offset 0 for every layout
     L.off_keys[0] = take(n4);
     L.off_keys[1] = take(n4);
     L.off_vals[0] = take(n4);
@@ -76,15 +97,18 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_sample = take(n4);
     L.off_sorted_sample = take(n4);
     L.off_sorted_psw = take(n4);
-    L.off_hist = take(size_t(kRadix) * (L.sort_blocks > 0 ? L.sort_blocks : 1) * 4);
+    L.off_status = take(size_t(L.npasses) * kRadix * (L.sort_blocks > 0 ? L.sort_blocks : 1) * 4);
+    L.off_rle_status = take(size_t(3) * (L.rle_blocks > 0 ? L.rle_blocks : 1) * 4);
+    L.status_words = (L.off_rle_status - L.off_status) / 4 +
+                     size_t(3) * (L.rle_blocks > 0 ? L.rle_blocks : 1);
     L.off_unique = take(n4);
     L.off_run_start = take(n4);
     L.off_run_len = take(n4);
     L.off_short = take(n4);
     L.off_long = take(n4);
-    L.off_long_chunk = take(n4);
-    L.off_tile_counts = take(size_t(L.rle_blocks > 0 ? L.rle_blocks : 1) * 16);
-    L.off_counts = take(size_t(16 + 4 * kRadix) * 4);
+    L.off_short_info = take(size_t(N + 1) * 16);
+    L.off_long_info = take(size_t(ml + 1) * 16);
+    L.off_arrive = take(size_t(ml + 1) * 4);
     const size_t acc = p->wdtype == TBE_F32 ? 8 : 4;
     L.off_partials = take(size_t(mc > 0 ? mc : 1) * p->max_D * acc);
     L.total = o;
@@ -110,100 +134,182 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
     return v;
 }
 
-// ---------------------------------------------------------------------------
-template <typename IT>
-__global__ __launch_bounds__(256) void k_linearize(
-    const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags,
-    const IT* __restrict__ indices, const IT* __restrict__ offsets, uint32_t* __restrict__ keys,
-    uint32_t* __restrict__ sample, uint32_t* __restrict__ zero_buf, int32_t zero_n)
+__device__ __forceinline__ uint32_t ld_acq(const uint32_t* p)
 {
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_buf[i] = 0u;
-    const int lane = threadIdx.x & 63;
-    const uint32_t nw = gridDim.x * (blockDim.x >> 6);
-    for (uint32_t g = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) +
-                                                     (threadIdx.x >> 6));
-         g < total_bags; g += nw) {
-        const uint32_t t = g / B;
-        const uint32_t b = g - t * B;
-        const uint32_t hoff = tables[t].hash_off;
-        const int64_t s = static_cast<int64_t>(offsets[g]);
-        const int64_t e = static_cast<int64_t>(offsets[g + 1]);
-        for (int64_t p = s + lane; p < e; p += 64) {
-            keys[p] = hoff + static_cast<uint32_t>(indices[p]);
-            sample[p] = b;
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_rel(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix of `value` over tiles 0..tile-1 through the status words
+// st[0..tile) (one word per tile, stride `stride`).  Publishes this tile's
+// aggregate first and its inclusive prefix last.  Predecessors are read W at a
+// time (independent loads), so a chain of published aggregates is crossed W
+// tiles per memory round trip.
+template <int W>
+__device__ __forceinline__ uint32_t lookback(uint32_t* st, uint32_t stride, uint32_t tile,
+                                             uint32_t value, uint32_t* err)
+{
+    if (tile == 0) {
+        st_rel(st, kFlagInc | value);
+        return 0;
+    }
+    st_rel(st + static_cast<size_t>(tile) * stride, kFlagAgg | value);
+    uint32_t excl = 0;
+    int64_t tp = static_cast<int64_t>(tile) - 1;
+    uint32_t spins = 0;
+    while (true) {
+        uint32_t s[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            s[i] = (tp - i >= 0) ? ld_acq(st + static_cast<size_t>(tp - i) * stride) : kFlagInc;
+        uint32_t consumed = 0;
+        bool stop = false, done = false;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            if (!stop) {
+                const uint32_t f = s[i] & ~kValMask;
+                if (f == 0) {
+                    stop = true;        // not published yet: fetch again from here
+                } else {
+                    excl += s[i] & kValMask;
+                    ++consumed;
+                    if (f == kFlagInc) stop = done = true;
+                }
+            }
+        }
+        if (done) break;
+        tp -= consumed;
+        if (consumed == 0) {
+            if (++spins > kSpinLimit) {
+                atomicOr(err, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
     }
+    st_rel(st + static_cast<size_t>(tile) * stride, kFlagInc | ((excl + value) & kValMask));
+    return excl;
+}
+
+// Tile ticket in launch order.  The block that takes the last ticket resets
+// the counter, so it is zero again for the next launch.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ticket, uint32_t ntiles)
+{
+    const uint32_t t = atomicAdd(ticket, 1u);
+    if (t == ntiles - 1) st_rel(ticket, 0u);
+    return t;
 }
 
 // ---------------------------------------------------------------------------
-template <int R>
-__global__ __launch_bounds__(256) void k_radix_up(
-    const uint32_t* __restrict__ keys, uint32_t N, int shift, uint32_t mask, uint32_t nblocks,
-    uint32_t* __restrict__ counts, uint32_t* __restrict__ totals)
+__global__ void k_fill_zero(uint32_t* __restrict__ p, int n)
 {
-    __shared__ uint32_t h[kRadix];
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+struct PassBits {
+    int32_t npasses;
+    int32_t shift[4];
+    uint32_t mask[4];
+};
+
+template <typename IT>
+__global__ __launch_bounds__(256) void k_prep(
+    const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
+    const IT* __restrict__ indices, const IT* __restrict__ offsets, uint32_t* __restrict__ keys,
+    uint32_t* __restrict__ sample, uint32_t* __restrict__ totals, PassBits pb,
+    uint32_t* __restrict__ status, size_t status_words)
+{
+    __shared__ uint32_t hist[4][kRadix];
+    __shared__ int64_t boff[kPrepMaxBags + 1];
     const int tid = threadIdx.x;
-    h[tid] = 0u;
+    for (size_t i = blockIdx.x * 256ull + tid; i < status_words; i += gridDim.x * 256ull)
+        status[i] = 0u;
+    for (int i = tid; i < 4 * kRadix; i += 256) (&hist[0][0])[i] = 0u;
+    const uint32_t g0 = blockIdx.x * bags_per_block;
+    if (g0 >= total_bags) return;
+    const uint32_t nb = min(bags_per_block, total_bags - g0);
+    for (uint32_t i = tid; i <= nb; i += 256) boff[i] = static_cast<int64_t>(offsets[g0 + i]);
     __syncthreads();
-    const uint32_t base = blockIdx.x * (256u * R);
-    uint32_t k[R];
+    const int64_t P0 = boff[0], P1 = boff[nb];
+    constexpr int UN = 4;
+    for (int64_t base = P0; base < P1; base += 256 * UN) {
+        IT id[UN];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint32_t i = base + r * 256u + tid;
-        k[r] = i < N ? keys[i] : 0u;
-    }
+        for (int u = 0; u < UN; ++u) {
+            const int64_t p = base + u * 256 + tid;
+            id[u] = p < P1 ? indices[p] : IT(0);
+        }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint32_t i = base + r * 256u + tid;
-        if (i < N) atomicAdd(&h[(k[r] >> shift) & mask], 1u);
+        for (int u = 0; u < UN; ++u) {
+            const int64_t p = base + u * 256 + tid;
+            if (p >= P1) continue;
+            uint32_t lo = 0, hi = nb;  // boff[lo] <= p < boff[hi]
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (boff[mid] <= p) lo = mid; else hi = mid;
+            }
+            const uint32_t g = g0 + lo;
+            const uint32_t t = g / B;
+            const uint32_t key = tables[t].hash_off + static_cast<uint32_t>(id[u]);
+            keys[p] = key;
+            sample[p] = g - t * B;
+            for (int q = 0; q < pb.npasses; ++q)
+                atomicAdd(&hist[q][(key >> pb.shift[q]) & pb.mask[q]], 1u);
+        }
     }
     __syncthreads();
-    const uint32_t c = h[tid];
-    counts[static_cast<size_t>(tid) * nblocks + blockIdx.x] = c;
-    if (c) atomicAdd(&totals[tid], c);
+    for (int q = 0; q < pb.npasses; ++q) {
+        const uint32_t c = hist[q][tid];
+        if (c) atomicAdd(&totals[q * kRadix + tid], c);
+    }
 }
 
-__global__ __launch_bounds__(256) void k_radix_scan(uint32_t* __restrict__ counts,
-                                                    uint32_t nblocks,
-                                                    const uint32_t* __restrict__ totals)
-{
-    const int lane = threadIdx.x & 63;
-    const int d = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (d >= kRadix) return;
-    uint32_t part = 0;
-    for (int k = lane; k < d; k += 64) part += totals[k];
-    uint32_t run = wave_sum(part);
-    uint32_t* row = counts + static_cast<size_t>(d) * nblocks;
-    for (uint32_t b0 = 0; b0 < nblocks; b0 += 64) {
-        const uint32_t b = b0 + lane;
-        const uint32_t v = b < nblocks ? row[b] : 0u;
-        const uint32_t inc = wave_incl_scan(v, lane);
-        if (b < nblocks) row[b] = run + inc - v;
-        run += __shfl(inc, 63);
-    }
-}
-
+// ---------------------------------------------------------------------------
 template <int R, bool FIRST, bool LAST>
-__global__ __launch_bounds__(256) void k_radix_down(
+__global__ __launch_bounds__(256) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t N, int shift,
-    int nbits, uint32_t nblocks, const uint32_t* __restrict__ offs,
-    const uint32_t* __restrict__ sample, const float* __restrict__ psw,
-    uint32_t* __restrict__ sorted_sample, float* __restrict__ sorted_psw)
+    int nbits, const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
+    uint32_t* __restrict__ ticket, uint32_t* __restrict__ err, uint32_t ntiles,
+    uint32_t* __restrict__ prev_totals, const uint32_t* __restrict__ sample,
+    const float* __restrict__ psw, uint32_t* __restrict__ sorted_sample,
+    float* __restrict__ sorted_psw)
 {
     __shared__ uint32_t wcnt[kSortWaves][kRadix];
     __shared__ uint32_t gofs[kRadix];
+    __shared__ uint32_t wsum[kSortWaves];
+    __shared__ uint32_t s_tile;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    if (tid == 0) s_tile = take_ticket(ticket, ntiles);
     for (int i = tid; i < kSortWaves * kRadix; i += 256) (&wcnt[0][0])[i] = 0u;
-    gofs[tid] = offs[static_cast<size_t>(tid) * nblocks + blockIdx.x];
+    // exclusive scan of the global digit totals: first position of each digit
+    {
+        const uint32_t v = totals[tid];
+        const uint32_t inc = wave_incl_scan(v, lane);
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        uint32_t pre = 0;
+        for (int w = 0; w < wave; ++w) pre += wsum[w];
+        gofs[tid] = pre + inc - v;
+    }
     __syncthreads();
+    const uint32_t tile = s_tile;
+    if (tile >= ntiles) {          // only with an uninitialised control block
+        if (tid == 0) atomicOr(err, 2u);
+        return;
+    }
+    // the previous pass's digit totals are no longer needed: leave them zero
+    if (tile == 0 && prev_totals) prev_totals[tid] = 0u;
 
     const uint32_t mask = (1u << nbits) - 1u;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const uint32_t wbase = blockIdx.x * (256u * R) + static_cast<uint32_t>(wave) * (64u * R);
+    const uint32_t wbase = tile * (256u * R) + static_cast<uint32_t>(wave) * (64u * R);
     uint32_t k[R], v[R], dg[R], rk[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -232,13 +338,16 @@ __global__ __launch_bounds__(256) void k_radix_down(
     }
     __syncthreads();
     {
+        const int d = tid;
         uint32_t run = 0;
 #pragma unroll
         for (int w = 0; w < kSortWaves; ++w) {
-            const uint32_t c = wcnt[w][tid];
-            wcnt[w][tid] = run;
+            const uint32_t c = wcnt[w][d];
+            wcnt[w][d] = run;
             run += c;
         }
+        const uint32_t excl = lookback<16>(status + d, kRadix, tile, run, err);
+        gofs[d] += excl;
     }
     __syncthreads();
 #pragma unroll
@@ -275,125 +384,62 @@ __device__ __forceinline__ uint32_t run_length(const uint32_t* __restrict__ keys
     return lo - i + 1;
 }
 
-struct RunInfo {
-    uint32_t head, len, is_long, chunks;
-};
-
-__device__ __forceinline__ RunInfo run_info(const uint32_t* __restrict__ keys, uint32_t N,
-                                            uint32_t i, uint32_t tau, uint32_t chunk)
+__device__ __forceinline__ int find_table_g(const uint32_t* __restrict__ hash_off, int T,
+                                            uint32_t key)
 {
-    RunInfo ri{0, 0, 0, 0};
-    if (i >= N) return ri;
-    const uint32_t k = keys[i];
-    if (i != 0 && keys[i - 1] == k) return ri;
-    ri.head = 1;
-    ri.len = run_length(keys, N, i, k);
-    if (ri.len >= tau) {
-        ri.is_long = 1;
-        ri.chunks = (ri.len + chunk - 1) / chunk;
+    int lo = 0, hi = T;  // hash_off[lo] <= key < hash_off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (hash_off[mid] <= key) lo = mid; else hi = mid;
     }
-    return ri;
+    return lo;
 }
 
-__global__ __launch_bounds__(256) void k_rle_count(const uint32_t* __restrict__ keys, uint32_t N,
-                                                   uint32_t tau, uint32_t chunk,
-                                                   uint32_t* __restrict__ tile_counts)
-{
-    __shared__ uint32_t red[3][4];
-    const int tid = threadIdx.x;
-    const uint32_t i0 = blockIdx.x * kRleTile + tid * kRleItems;
-    uint32_t h = 0, l = 0, c = 0;
-#pragma unroll
-    for (int q = 0; q < kRleItems; ++q) {
-        const RunInfo ri = run_info(keys, N, i0 + q, tau, chunk);
-        h += ri.head;
-        l += ri.is_long;
-        c += ri.chunks;
-    }
-    h = wave_sum(h);
-    l = wave_sum(l);
-    c = wave_sum(c);
-    if ((tid & 63) == 0) {
-        red[0][tid >> 6] = h;
-        red[1][tid >> 6] = l;
-        red[2][tid >> 6] = c;
-    }
-    __syncthreads();
-    if (tid < 3)
-        tile_counts[blockIdx.x * 4 + tid] = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
-}
-
-// One workgroup of 1024 threads: exclusive prefix of the per-tile
-// (heads, long runs, chunks) and the device totals.
-__global__ __launch_bounds__(1024) void k_rle_scan(uint32_t* __restrict__ tile_counts,
-                                                   uint32_t ntiles, uint32_t N,
-                                                   uint32_t* __restrict__ counts,
-                                                   uint32_t* __restrict__ run_start,
-                                                   uint32_t* __restrict__ long_chunk)
-{
-    __shared__ uint32_t wsum[3][16];
-    __shared__ uint32_t carry[3];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    if (tid < 3) carry[tid] = 0;
-    __syncthreads();
-    for (uint32_t t0 = 0; t0 < ntiles; t0 += 1024) {
-        const uint32_t t = t0 + tid;
-        uint32_t v[3], inc[3];
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-            v[c] = t < ntiles ? tile_counts[t * 4 + c] : 0u;
-            inc[c] = wave_incl_scan(v[c], lane);
-            if (lane == 63) wsum[c][wave] = inc[c];
-        }
-        __syncthreads();
-        if (tid < 3) {
-            uint32_t run = carry[tid];
-            for (int w = 0; w < 16; ++w) {
-                const uint32_t x = wsum[tid][w];
-                wsum[tid][w] = run;
-                run += x;
-            }
-            carry[tid] = run;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < 3; ++c)
-            if (t < ntiles) tile_counts[t * 4 + c] = wsum[c][wave] + inc[c] - v[c];
-        __syncthreads();
-    }
-    if (tid == 0) {
-        const uint32_t runs = carry[0], nlong = carry[1], chunks = carry[2];
-        counts[0] = runs;
-        counts[1] = runs - nlong;
-        counts[2] = nlong;
-        counts[3] = chunks;
-        run_start[runs] = N;
-        long_chunk[nlong] = chunks;
-    }
-}
-
-__global__ __launch_bounds__(256) void k_rle_write(
-    const uint32_t* __restrict__ keys, uint32_t N, uint32_t tau, uint32_t chunk,
-    const uint32_t* __restrict__ tile_prefix, uint32_t* __restrict__ unique,
-    uint32_t* __restrict__ run_start, uint32_t* __restrict__ run_len,
-    uint32_t* __restrict__ short_runs, uint32_t* __restrict__ long_runs,
-    uint32_t* __restrict__ long_chunk)
+template <bool API>
+__global__ __launch_bounds__(256) void k_rle(
+    const uint32_t* __restrict__ keys, uint32_t N, uint32_t tau, uint32_t chunk, uint32_t ntiles,
+    uint32_t* __restrict__ rstatus, uint32_t* __restrict__ ticket, uint32_t* __restrict__ err,
+    const uint32_t* __restrict__ hash_off, int32_t T, uint4* __restrict__ short_info,
+    uint4* __restrict__ long_info, uint32_t* __restrict__ arrive, uint32_t* __restrict__ counts,
+    uint32_t max_long, uint32_t* __restrict__ prev_totals,
+    uint32_t* __restrict__ unique, uint32_t* __restrict__ run_start,
+    uint32_t* __restrict__ run_len, uint32_t* __restrict__ short_ids,
+    uint32_t* __restrict__ long_ids)
 {
     __shared__ uint32_t wsum[3][4];
+    __shared__ uint32_t texcl[3];
+    __shared__ uint32_t s_tile;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const uint32_t i0 = blockIdx.x * kRleTile + tid * kRleItems;
-    RunInfo ri[kRleItems];
+    if (tid == 0) s_tile = take_ticket(ticket, ntiles);
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    if (tile >= ntiles) {          // only with an uninitialised control block
+        if (tid == 0) atomicOr(err, 2u);
+        return;
+    }
+    if (tile == 0 && prev_totals) prev_totals[tid] = 0u;   // last radix pass is done
+    const uint32_t i0 = tile * kRleTile + tid * kRleItems;
+
+    uint32_t kk[kRleItems], len[kRleItems];
     uint32_t v[3] = {0, 0, 0};
 #pragma unroll
     for (int q = 0; q < kRleItems; ++q) {
-        ri[q] = run_info(keys, N, i0 + q, tau, chunk);
-        v[0] += ri[q].head;
-        v[1] += ri[q].is_long;
-        v[2] += ri[q].chunks;
+        const uint32_t i = i0 + q;
+        len[q] = 0;
+        kk[q] = 0;
+        if (i < N) {
+            kk[q] = keys[i];
+            if (i == 0 || keys[i - 1] != kk[q]) {
+                len[q] = run_length(keys, N, i, kk[q]);
+                v[0] += 1;
+                if (len[q] >= tau) {
+                    v[1] += 1;
+                    v[2] += (len[q] + chunk - 1) / chunk;
+                }
+            }
+        }
     }
     uint32_t inc[3];
 #pragma unroll
@@ -402,28 +448,53 @@ __global__ __launch_bounds__(256) void k_rle_write(
         if (lane == 63) wsum[c][wave] = inc[c];
     }
     __syncthreads();
+    if (tid < 3) {
+        const uint32_t tot = wsum[tid][0] + wsum[tid][1] + wsum[tid][2] + wsum[tid][3];
+        const uint32_t ex =
+            lookback<32>(rstatus + static_cast<size_t>(tid) * ntiles, 1, tile, tot, err);
+        texcl[tid] = ex;
+        if (tile == ntiles - 1) {
+            // the last tile knows the totals
+            counts[tid == 0 ? 0 : (tid == 1 ? 2 : 3)] = ex + tot;
+        }
+    }
+    __syncthreads();
     uint32_t base[3];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-        uint32_t pre = tile_prefix[blockIdx.x * 4 + c];
+        uint32_t pre = texcl[c];
         for (int w = 0; w < wave; ++w) pre += wsum[c][w];
         base[c] = pre + inc[c] - v[c];
+    }
+    if (tile == ntiles - 1 && tid == 255) {
+        const uint32_t R = base[0] + v[0], Lg = base[1] + v[1];
+        counts[1] = R - Lg;
+        if (API) run_start[R] = N;
     }
     uint32_t r = base[0], lb = base[1], cb = base[2];
 #pragma unroll
     for (int q = 0; q < kRleItems; ++q) {
-        if (!ri[q].head || r >= N || lb > r) continue;  // guards: unreachable when consistent
+        if (len[q] == 0) continue;
+        if (r >= N || lb > r) break;  // guards: unreachable when consistent
         const uint32_t i = i0 + q;
-        unique[r] = keys[i];
-        run_start[r] = i;
-        run_len[r] = ri[q].len;
-        if (ri[q].is_long) {
-            long_runs[lb] = r;
-            long_chunk[lb] = cb;
+        const uint32_t key = kk[q];
+        if (API) {
+            unique[r] = key;
+            run_start[r] = i;
+            run_len[r] = len[q];
+        }
+        if (len[q] >= tau) {
+            if (lb < max_long) {
+                long_info[lb] = make_uint4(key, i, len[q], cb);
+                arrive[lb] = 0u;
+            }
+            if (API) long_ids[lb] = r;
             ++lb;
-            cb += ri[q].chunks;
+            cb += (len[q] + chunk - 1) / chunk;
         } else {
-            short_runs[r - lb] = r;
+            const uint32_t t = static_cast<uint32_t>(find_table_g(hash_off, T, key));
+            short_info[r - lb] = make_uint4(key, i, len[q], t);
+            if (API) short_ids[r - lb] = r;
         }
         ++r;
     }
@@ -440,8 +511,8 @@ hipError_t sort_passes(BwdArgs& a)
                          reinterpret_cast<uint32_t*>(ws + L.off_keys[1])};
     uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + L.off_vals[0]),
                          reinterpret_cast<uint32_t*>(ws + L.off_vals[1])};
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.off_hist);
-    uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.off_counts);
+    uint32_t* ctl = reinterpret_cast<uint32_t*>(ws + L.off_ctl);
+    uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.off_status);
     uint32_t* sample = reinterpret_cast<uint32_t*>(ws + L.off_sample);
     uint32_t* ssample = reinterpret_cast<uint32_t*>(ws + L.off_sorted_sample);
     float* spsw = reinterpret_cast<float*>(ws + L.off_sorted_psw);
@@ -449,18 +520,16 @@ hipError_t sort_passes(BwdArgs& a)
     int shift = 0;
     for (int pass = 0; pass < L.npasses; ++pass) {
         const int nbits = L.digit_bits[pass];
-        const uint32_t mask = (1u << nbits) - 1u;
-        uint32_t* totals = counters + 16 + pass * kRadix;
-        hipLaunchKernelGGL(k_radix_up<R>, dim3(nb), dim3(256), 0, a.stream, keys[cur], N, shift,
-                           mask, nb, hist, totals);
-        hipLaunchKernelGGL(k_radix_scan, dim3(kRadix / 4), dim3(256), 0, a.stream, hist, nb,
-                           totals);
         const bool first = pass == 0, last = pass == L.npasses - 1;
-        auto kern = first ? (last ? k_radix_down<R, true, true> : k_radix_down<R, true, false>)
-                          : (last ? k_radix_down<R, false, true> : k_radix_down<R, false, false>);
+        auto kern = first ? (last ? k_onesweep<R, true, true> : k_onesweep<R, true, false>)
+                          : (last ? k_onesweep<R, false, true> : k_onesweep<R, false, false>);
         hipLaunchKernelGGL(kern, dim3(nb), dim3(256), 0, a.stream, keys[cur], vals[cur],
-                           keys[cur ^ 1], vals[cur ^ 1], N, shift, nbits, nb, hist, sample, a.psw,
-                           ssample, spsw);
+                           keys[cur ^ 1], vals[cur ^ 1], N, shift, nbits,
+                           ctl + kCtlTotals + pass * kRadix,
+                           status + static_cast<size_t>(pass) * kRadix * nb,
+                           ctl + kCtlTicket + pass, ctl + kCtlError, nb,
+                           pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadix : nullptr,
+                           sample, a.psw, ssample, spsw);
         cur ^= 1;
         shift += nbits;
     }
@@ -470,59 +539,81 @@ hipError_t sort_passes(BwdArgs& a)
 
 }  // namespace
 
-hipError_t run_sort_rle(BwdArgs& a)
+hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
 {
     const tbe_plan* p = a.plan;
     const BwdLayout& L = a.L;
     char* ws = a.ws;
     const uint32_t N = static_cast<uint32_t>(L.N);
     const uint32_t total_bags = static_cast<uint32_t>(p->T) * static_cast<uint32_t>(a.B);
-    uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.off_counts);
-    const int zero_n = 16 + 4 * kRadix;
+    uint32_t* ctl = reinterpret_cast<uint32_t*>(ws + L.off_ctl);
+    if (N == 0 || total_bags == 0) {
+        a.final_buf = 0;
+        hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, a.stream, ctl + kCtlCounts, 4);
+        return hipGetLastError();
+    }
+    PassBits pb{};
+    pb.npasses = L.npasses;
     {
-        const uint32_t waves = total_bags < 65536u ? total_bags : 65536u;
-        const uint32_t blocks = (waves + 3) / 4 > 0 ? (waves + 3) / 4 : 1;
+        int s = 0;
+        for (int i = 0; i < L.npasses; ++i) {
+            pb.shift[i] = s;
+            pb.mask[i] = (1u << L.digit_bits[i]) - 1u;
+            s += L.digit_bits[i];
+        }
+    }
+    {
         uint32_t* keys0 = reinterpret_cast<uint32_t*>(ws + L.off_keys[0]);
         uint32_t* sample = reinterpret_cast<uint32_t*>(ws + L.off_sample);
+        uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.off_status);
         if (p->idtype == TBE_I64)
-            hipLaunchKernelGGL(k_linearize<int64_t>, dim3(blocks), dim3(256), 0, a.stream,
+            hipLaunchKernelGGL(k_prep<int64_t>, dim3(L.prep_blocks), dim3(256), 0, a.stream,
                                p->d_tables, static_cast<uint32_t>(a.B), total_bags,
+                               static_cast<uint32_t>(L.prep_bags),
                                static_cast<const int64_t*>(a.indices),
-                               static_cast<const int64_t*>(a.offsets), keys0, sample, counters,
-                               zero_n);
+                               static_cast<const int64_t*>(a.offsets), keys0, sample,
+                               ctl + kCtlTotals, pb, status, L.status_words);
         else
-            hipLaunchKernelGGL(k_linearize<int32_t>, dim3(blocks), dim3(256), 0, a.stream,
+            hipLaunchKernelGGL(k_prep<int32_t>, dim3(L.prep_blocks), dim3(256), 0, a.stream,
                                p->d_tables, static_cast<uint32_t>(a.B), total_bags,
+                               static_cast<uint32_t>(L.prep_bags),
                                static_cast<const int32_t*>(a.indices),
-                               static_cast<const int32_t*>(a.offsets), keys0, sample, counters,
-                               zero_n);
+                               static_cast<const int32_t*>(a.offsets), keys0, sample,
+                               ctl + kCtlTotals, pb, status, L.status_words);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (N == 0) {
-        a.final_buf = 0;
-        return hipSuccess;   // counters are zero; run_start[0] is never read
-    }
     e = sort_rounds(L.N) == 16 ? sort_passes<16>(a) : sort_passes<8>(a);
     if (e != hipSuccess) return e;
 
     const uint32_t* skeys = reinterpret_cast<const uint32_t*>(ws + L.off_keys[a.final_buf]);
-    uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.off_tile_counts);
     const uint32_t tau = static_cast<uint32_t>(p->tuning.tau);
     const uint32_t chunk = static_cast<uint32_t>(p->tuning.chunk);
     const uint32_t nt = static_cast<uint32_t>(L.rle_blocks);
-    hipLaunchKernelGGL(k_rle_count, dim3(nt), dim3(256), 0, a.stream, skeys, N, tau, chunk, tiles);
-    hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(1024), 0, a.stream, tiles, nt, N, counters,
-                       reinterpret_cast<uint32_t*>(ws + L.off_run_start),
-                       reinterpret_cast<uint32_t*>(ws + L.off_long_chunk));
-    hipLaunchKernelGGL(k_rle_write, dim3(nt), dim3(256), 0, a.stream, skeys, N, tau, chunk, tiles,
+    auto kern = api_outputs ? k_rle<true> : k_rle<false>;
+    hipLaunchKernelGGL(kern, dim3(nt), dim3(256), 0, a.stream, skeys, N, tau, chunk, nt,
+                       reinterpret_cast<uint32_t*>(ws + L.off_rle_status), ctl + kCtlRleTicket,
+                       ctl + kCtlError, p->d_hash_off, p->T,
+                       reinterpret_cast<uint4*>(ws + L.off_short_info),
+                       reinterpret_cast<uint4*>(ws + L.off_long_info),
+                       reinterpret_cast<uint32_t*>(ws + L.off_arrive), ctl + kCtlCounts,
+                       static_cast<uint32_t>(L.max_long),
+                       ctl + kCtlTotals + (L.npasses - 1) * kRadix,
                        reinterpret_cast<uint32_t*>(ws + L.off_unique),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_start),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_len),
                        reinterpret_cast<uint32_t*>(ws + L.off_short),
-                       reinterpret_cast<uint32_t*>(ws + L.off_long),
-                       reinterpret_cast<uint32_t*>(ws + L.off_long_chunk));
+                       reinterpret_cast<uint32_t*>(ws + L.off_long));
     return hipGetLastError();
 }
 
+}  // namespace tbe
+
+namespace tbe {
+hipError_t launch_workspace_init(void* ws, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(1024), 0, s, static_cast<uint32_t*>(ws),
+                       kCtlWords);
+    return hipGetLastError();
+}
 }  // namespace tbe

@@ -33,7 +33,7 @@ tbe_status check_call(const tbe_plan* p, int32_t B, int64_t num_indices, const v
     if (!p || B < 0 || num_indices < 0) return TBE_EINVAL;
     if (B > 0 && !offsets) return TBE_EINVAL;
     if (num_indices > 0 && !indices) return TBE_EINVAL;
-    if (num_indices >= (int64_t(1) << 31)) return TBE_ERANGE;
+    if (num_indices >= (int64_t(1) << 30)) return TBE_ERANGE;
     if (int64_t(p->T) * B >= (int64_t(1) << 31)) return TBE_ERANGE;
     return TBE_OK;
 }
@@ -252,7 +252,7 @@ tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const v
     a.grad = grad_output;
     a.weights = weights;
     a.lr = lr;
-    if (run_sort_rle(a) != hipSuccess) return TBE_EHIP;
+    if (run_sort_rle(a, false) != hipSuccess) return TBE_EHIP;
     if (run_segment_sgd(a) != hipSuccess) return TBE_EHIP;
     return TBE_OK;
 }
@@ -266,7 +266,7 @@ tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64
     tbe_status st = prepare_bwd(p, B, indices, num_indices, offsets, workspace,
                                 workspace_bytes, stream, a);
     if (st != TBE_OK) return st;
-    if (run_sort_rle(a) != hipSuccess) return TBE_EHIP;
+    if (run_sort_rle(a, true) != hipSuccess) return TBE_EHIP;
     char* ws = a.ws;
     const BwdLayout& L = a.L;
     view->sorted_keys = reinterpret_cast<uint32_t*>(ws + L.off_keys[a.final_buf]);
@@ -276,7 +276,17 @@ tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64
     view->run_len = reinterpret_cast<uint32_t*>(ws + L.off_run_len);
     view->short_runs = reinterpret_cast<uint32_t*>(ws + L.off_short);
     view->long_runs = reinterpret_cast<uint32_t*>(ws + L.off_long);
-    view->counts = reinterpret_cast<uint32_t*>(ws + L.off_counts);
+    view->counts = reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlCounts;
+    return TBE_OK;
+}
+
+tbe_status tbe_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+        workspace_bytes < size_t(kCtlWords) * 4)
+        return TBE_EINVAL;
+    if (launch_workspace_init(workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TBE_EHIP;
     return TBE_OK;
 }
 

@@ -73,24 +73,41 @@ hipError_t launch_fwd_gather(const FwdArgs& a);
 hipError_t launch_fwd_hist(const FwdArgs& a);
 
 // ---- backward --------------------------------------------------------------
+// Control block at offset 0 of every backward workspace.  It must be zero when
+// a call starts (tbe_workspace_init), and every call leaves it zero again:
+// tile tickets reset themselves, each pass's digit totals are cleared by the
+// next kernel.  Counts and the error word are outputs.
+constexpr int kCtlTicket = 0;      // [4] tile tickets of the radix passes
+constexpr int kCtlRleTicket = 4;   // tile ticket of the run-length encode
+constexpr int kCtlError = 12;      // nonzero: a look-back wait gave up (sticky)
+constexpr int kCtlCounts = 8;      // [4] runs, short runs, long runs, long-run chunks
+constexpr int kCtlTotals = 16;     // [4][256] digit totals of every radix pass
+constexpr int kCtlWords = 16 + 4 * 256;
+
 // Workspace carve-up (byte offsets), computed on the host.
 struct BwdLayout {
     int64_t N = 0;
     int32_t nbits = 0;          // key bits to sort
     int32_t npasses = 0;
     int32_t digit_bits[4] = {0, 0, 0, 0};
-    int32_t sort_tile = 0;      // keys per sort block
+    int32_t sort_tile = 0;      // keys per sort tile
     int32_t sort_blocks = 0;
     int32_t rle_tile = 0;
     int32_t rle_blocks = 0;
+    int32_t prep_blocks = 0;
+    int32_t prep_bags = 0;      // bags per k_prep block
     int64_t max_chunks = 0;     // bound on long-run chunks
+    int64_t max_long = 0;       // bound on long runs
     size_t off_keys[2], off_vals[2];
     size_t off_sample, off_sorted_sample, off_sorted_psw;
-    size_t off_hist;            // [sort_blocks * 256] digit counts
+    size_t off_status;          // [npasses][sort_blocks][256] look-back words
+    size_t off_rle_status;      // [3][rle_blocks]
+    size_t status_words = 0;    // words cleared by k_prep from off_status on
+    size_t off_ctl;             // [kCtlWords]
     size_t off_unique, off_run_start, off_run_len, off_short, off_long;
-    size_t off_long_chunk;      // [N+1] first chunk of each long run
-    size_t off_tile_counts;     // [rle_blocks * 4]
-    size_t off_counts;          // [16]
+    size_t off_short_info;      // [N] {key, start, len, table}
+    size_t off_long_info;       // [max_long] {key, start, len, first chunk}
+    size_t off_arrive;          // [max_long] chunks of each long run already summed
     size_t off_partials;        // [max_chunks * max_D] (fp64 or fp32)
     size_t total = 0;
 };
@@ -112,8 +129,12 @@ struct BwdArgs {
     // filled by run_sort_rle: which ping-pong buffer holds the sorted result
     int final_buf;
 };
-hipError_t run_sort_rle(BwdArgs& a);
+// api_outputs: also write unique keys, run starts / lengths and run-id lists.
+hipError_t run_sort_rle(BwdArgs& a, bool api_outputs);
 hipError_t run_segment_sgd(const BwdArgs& a);
+
+// Zero the control block (first kCtlWords words) of a fresh workspace.
+hipError_t launch_workspace_init(void* ws, hipStream_t s);
 
 hipError_t launch_bounds_check(const tbe_plan* p, int32_t B, const void* indices,
                                int64_t N, const void* offsets, int64_t* err, hipStream_t s);

@@ -247,11 +247,21 @@ def _zipf_bounded(rng, a: float, R: int, n: int) -> np.ndarray:
     return out
 
 
+def _rng(seed: int, batch: int, *key):
+    """Stream for one purpose; batch 0 keeps the base streams, other batches
+    draw fresh lengths / ids / weights / gradients over the same tables."""
+    if batch == 0:
+        return np.random.default_rng([seed, *key])
+    return np.random.default_rng([seed, *key, 1000 + int(batch)])
+
+
 def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
                  rows_cap: Optional[int] = None, T: Optional[int] = None,
-                 weighted: Optional[str] = None, wdtype: Optional[str] = None) -> Problem:
+                 weighted: Optional[str] = None, wdtype: Optional[str] = None,
+                 batch: int = 0) -> Problem:
     """Build a seeded problem from a named recipe; optional size overrides
-    (``B``, ``T``, ``rows_cap``) give smaller instances of the same shape."""
+    (``B``, ``T``, ``rows_cap``) give smaller instances of the same shape, and
+    ``batch`` selects another batch of lookups over the same tables."""
     cfg = dict(CONFIGS[name])
     seed = cfg["seed"] if seed is None else int(seed)
     Tn = cfg["T"] if T is None else int(T)
@@ -274,7 +284,7 @@ def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
     if rows_cap is not None:
         rows = np.minimum(rows, int(rows_cap))
 
-    rng2 = np.random.default_rng([seed, 2])
+    rng2 = _rng(seed, batch, 2)
     lspec = cfg["lengths"]
     if lspec[0] == "uniform_int":
         lengths = rng2.integers(lspec[1], lspec[2] + 1, size=(Tn, Bn))
@@ -296,7 +306,7 @@ def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
     ids = []
     for t in range(Tn):
         n_t = int(lengths[t].sum())
-        rng3 = np.random.default_rng([seed, 3, t])
+        rng3 = _rng(seed, batch, 3, t)
         R = int(rows[t])
         if cfg["ids"] == "uniform":
             it = rng3.integers(0, R, size=n_t, dtype=np.int64)
@@ -322,12 +332,12 @@ def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
     N = int(offsets[-1])
     psw = None
     if wmask.any():
-        psw = np.random.default_rng([seed, 4]).random(N, dtype=np.float32)
+        psw = _rng(seed, batch, 4).random(N, dtype=np.float32)
         # lookups of unweighted features carry weight exactly 1
         tl = np.repeat(np.arange(Tn), lengths.sum(axis=1))
         psw[~wmask[tl]] = np.float32(1.0)
 
-    grad = np.random.default_rng([seed, 5]).standard_normal(
+    grad = _rng(seed, batch, 5).standard_normal(
         (Bn, int(dims.sum())), dtype=np.float32)
 
     return Problem(name=name, seed=seed, T=Tn, B=Bn, rows=rows, dims=dims,

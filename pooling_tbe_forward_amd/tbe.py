@@ -64,6 +64,8 @@ def lib():
         L.tbe_backward_sgd.restype = I32
         L.tbe_sort_rle.argtypes = [P, I32, P, I64, P, P, SZ, ctypes.POINTER(tbe_sort_view), P]
         L.tbe_sort_rle.restype = I32
+        L.tbe_workspace_init.argtypes = [P, SZ, P]
+        L.tbe_workspace_init.restype = I32
         L.tbe_bounds_check.argtypes = [P, I32, P, I64, P, P, P]
         L.tbe_bounds_check.restype = I32
         L.tbe_get_tuning.argtypes = [P, ctypes.POINTER(tbe_tuning)]
@@ -189,6 +191,22 @@ def tbe_backward_workspace_bytes(plan: Plan, B: int, num_indices: int) -> int:
     return int(lib().tbe_backward_workspace_bytes(plan.handle, int(B), int(num_indices)))
 
 
+def tbe_workspace_init(workspace, stream=None):
+    _check(lib().tbe_workspace_init(_ptr(workspace),
+                                    int(workspace.numel() * workspace.element_size()),
+                                    _stream(stream)), "tbe_workspace_init")
+    return workspace
+
+
+def alloc_workspace(plan: Plan, B: int, num_indices: int, device="cuda"):
+    """Allocate (through torch) and initialise a backward workspace."""
+    n = tbe_backward_workspace_bytes(plan, B, num_indices)
+    if n == 0:
+        raise TBEError(TBE_EINVAL, "tbe_backward_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return tbe_workspace_init(ws)
+
+
 def tbe_backward_sgd(plan: Plan, B: int, weights, indices, offsets, per_sample_weights,
                      grad_output, lr: float, workspace, stream=None):
     _check(lib().tbe_backward_sgd(plan.handle, int(B), _ptr(weights), _ptr(indices),
@@ -217,7 +235,7 @@ def tbe_sort_rle(plan: Plan, B: int, indices, offsets, workspace, stream=None) -
     return dict(sorted_keys=view(v.sorted_keys, N), sorted_pos=view(v.sorted_pos, N),
                 unique_keys=view(v.unique_keys, N), run_start=view(v.run_start, N + 1),
                 run_len=view(v.run_len, N), short_runs=view(v.short_runs, N),
-                long_runs=view(v.long_runs, N), counts=view(v.counts, 4))
+                long_runs=view(v.long_runs, N), counts=view(v.counts, 5))
 
 
 def tbe_bounds_check(plan: Plan, B: int, indices, offsets, error_count, stream=None):

@@ -18,9 +18,7 @@ GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "handwor
 
 
 def _workspace(plan, prob):
-    n = tbe.tbe_backward_workspace_bytes(plan, prob.B, prob.N)
-    assert n > 0
-    return torch.empty(n, dtype=torch.uint8, device="cuda")
+    return tbe.alloc_workspace(plan, prob.B, prob.N)
 
 
 def _u32(t):
@@ -36,6 +34,7 @@ def gpu_sort(prob, index_dtype="i32", **tuning):
     v = tbe.tbe_sort_rle(plan, prob.B, d["indices"], d["offsets"], ws)
     torch.cuda.synchronize()
     c = _u32(v["counts"])
+    assert c[4] == 0, "look-back error word set"
     R, S, L = int(c[0]), int(c[1]), int(c[2])
     return dict(sorted_keys=_u32(v["sorted_keys"]), sorted_pos=_u32(v["sorted_pos"]),
                 unique_keys=_u32(v["unique_keys"][:R]), run_start=_u32(v["run_start"][:R]),
@@ -300,7 +299,7 @@ def test_error_codes():
     prob = dg.make_problem("toy", seed=4)
     plan = H.make_plan(prob)
     d = H.device_inputs(prob)
-    ws = torch.empty(16, dtype=torch.uint8, device="cuda")  # far too small
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")  # far too small
     with pytest.raises(tbe.TBEError) as e:
         tbe.tbe_backward_sgd(plan, prob.B, torch.zeros(10, device="cuda"), d["indices"],
                              d["offsets"], None, d["grad"], 0.1, ws)
@@ -309,3 +308,32 @@ def test_error_codes():
         tbe.tbe_set_tuning(plan, tau=0)
     with pytest.raises(tbe.TBEError):
         tbe.tbe_plan_create([10], [0])
+
+
+def test_workspace_reused_across_calls_and_sizes():
+    """One initialised workspace serves many calls of different sizes and both
+    entry points: every call leaves the control block clean."""
+    big = dg.make_problem("stress", seed=21, B=512)
+    plan_big = H.make_plan(big)
+    tbe.tbe_set_tuning(plan_big, tau=8, chunk=4)
+    ws = _workspace(plan_big, big)
+    for k, B in enumerate([512, 37, 300, 500]):
+        prob = dg.make_problem("stress", seed=30 + k, B=B)
+        plan = H.make_plan(prob)
+        tbe.tbe_set_tuning(plan, tau=8, chunk=4)
+        d = H.device_inputs(prob)
+        if k % 2 == 0:
+            v = tbe.tbe_sort_rle(plan, prob.B, d["indices"], d["offsets"], ws)
+            torch.cuda.synchronize()
+            c = _u32(v["counts"])
+            o = H.oracle_sort(prob, 8)
+            assert c[4] == 0 and int(c[0]) == o["num_runs"] and int(c[2]) == o["num_long"]
+            assert np.array_equal(_u32(v["sorted_pos"]), o["sorted_pos"])
+        w0 = dg.packed_weights_torch(prob, "cuda")
+        tbe.tbe_backward_sgd(plan, prob.B, w0, d["indices"], d["offsets"], d["psw"], d["grad"],
+                             prob.lr, ws)
+        torch.cuda.synchronize()
+        o = H.oracle_sort(prob, 8)
+        rep = _sampled_backward_check(prob, None, w0, _key_sample(prob, o, n_short=500, seed=k))
+        assert rep["ok"], (k, rep)
+        assert int(_u32(ws[48:52].view(torch.int32))[0]) == 0   # error word stays clear
