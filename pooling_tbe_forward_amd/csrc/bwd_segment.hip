@@ -7,8 +7,7 @@
 // materialised; one owner per run means a plain store, no atomics.
 // Section "Three tiers, routed by run length": short runs are owned outright
 // by one worker; long runs are cut into fixed-size chunks whose partial sums
-// meet in a workspace and are added once all have landed (the article's fused
-// tier: each chunk publishes its partial, fences, and counts itself in).
+// meet in a workspace and a second kernel adds them and applies the update.
 // Section "Where the backward speedup comes from": the short-run kernel's
 // speed is latency hiding -- how many independent row loads are in flight.
 //
@@ -20,9 +19,11 @@
 //    step, so U sample-id loads and U gradient-row loads are in flight per
 //    step; a run of one lookup costs one dependent step, not U;
 //  * long runs: the same launch carries chunk workers (one chunk of `chunk`
-//    lookups each) that write partial sums; the worker finishing a run's last
-//    chunk adds the run's partials in chunk order and applies the update, so
-//    the result does not depend on scheduling;
+//    lookups each) that write partial sums; the next launch adds each run's
+//    partials in chunk order and applies the update, so the result does not
+//    depend on scheduling.  (Combining in the same launch, last arrival wins,
+//    needs a device-scope release per chunk, which on gfx950 writes back and
+//    invalidates the whole L2 -- far dearer than one more launch);
 //  * accumulation is fp64 for fp32 tables (long Zipf runs would otherwise
 //    drift past 1e-5 relative) and fp32 for fp16 tables; w - lr*g is rounded
 //    once to the storage type;
@@ -56,11 +57,9 @@ struct SegArgs {
     int32_t lpr_log2;      // lanes per worker (log2)
     int32_t max_D;
     const float* grad;
-    const uint32_t* sorted_sample;
-    const float* sorted_psw;
+    const void* sorted_payload;   // sample ids, or (sample, weight) pairs when weighted
     const uint4* short_info;   // {key, start, len, table}
     const uint4* long_info;    // {key, start, len, first chunk}
-    uint32_t* arrive;          // per long run: chunks whose partial has landed
     const uint32_t* counts;    // runs, short, long, chunks
     uint32_t chunk;
     uint32_t max_chunks;
@@ -81,172 +80,241 @@ __device__ __forceinline__ void sgd_store(WT* __restrict__ wp, const Pack<WT, VE
     *reinterpret_cast<Pack<WT, VEC>*>(wp) = o;
 }
 
-// Sum of w_i * grad[sample_i, col .. col+VEC) over sorted positions [i0, i1).
-template <typename ACC, int VEC, int UC, bool WEIGHTED>
-__device__ __forceinline__ void seg_sum(const SegArgs& c, const float* __restrict__ gcol,
-                                        uint32_t i0, uint32_t i1, bool tw, ACC (&acc)[VEC])
+// Sum, for S runs held by one worker (L lanes), of w_i * grad[sample_i, col..]
+// over each run's contributions, walked as one flat sequence: the worker's
+// lanes load L sample ids (and per-sample weights) at once, then U gradient
+// rows are kept in flight at a time, across run boundaries.  pos0/len give
+// each run's first sorted position and length; gcol its gradient column base.
+template <typename ACC, int VEC, int S, int U, bool WEIGHTED>
+__device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0)[S],
+                                         const uint32_t (&len)[S],
+                                         const float* const (&gcol)[S], const bool (&tw)[S],
+                                         int sub, int L, int gbase, ACC (&acc)[S][VEC])
 {
-    for (uint32_t i = i0; i < i1; i += UC) {
-        Pack<float, VEC> g[UC];
-        float w[UC];
+    uint32_t pre[S + 1];
+    pre[0] = 0;
 #pragma unroll
-        for (int u = 0; u < UC; ++u) {
-            const uint32_t ii = i + u;
-            if (ii < i1) {
-                const uint32_t smp = c.sorted_sample[ii];
-                w[u] = (WEIGHTED && tw) ? c.sorted_psw[ii] : 1.f;
-                g[u] = *reinterpret_cast<const Pack<float, VEC>*>(
-                    gcol + static_cast<int64_t>(smp) * c.sumD);
+    for (int u = 0; u < S; ++u) pre[u + 1] = pre[u] + len[u];
+    const uint32_t C = pre[S];
+    for (uint32_t cb = 0; cb < C; cb += L) {
+        // lane `sub` fetches contribution cb + sub
+        const uint32_t ci = cb + sub;
+        uint32_t my_smp = 0;
+        float my_w = 1.f;
+        if (ci < C) {
+            int sl = 0;
+#pragma unroll
+            for (int u = 1; u < S; ++u) sl += ci >= pre[u] ? 1 : 0;
+            uint32_t p = 0;
+            bool w_on = false;
+#pragma unroll
+            for (int u = 0; u < S; ++u)
+                if (u == sl) { p = pos0[u] + (ci - pre[u]); w_on = tw[u]; }
+            if (WEIGHTED) {
+                const uint2 pv = static_cast<const uint2*>(c.sorted_payload)[p];
+                my_smp = pv.x;
+                if (w_on) my_w = __uint_as_float(pv.y);
             } else {
-                w[u] = 0.f;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) g[u].v[k] = 0.f;
+                my_smp = static_cast<const uint32_t*>(c.sorted_payload)[p];
             }
         }
+        const uint32_t n = min(static_cast<uint32_t>(L), C - cb);
+        for (uint32_t j0 = 0; j0 < n; j0 += U) {
+            Pack<float, VEC> g[U];
+            float w[U];
+            int sl[U];
 #pragma unroll
-        for (int u = 0; u < UC; ++u)
+            for (int q = 0; q < U; ++q) {
+                const uint32_t j = j0 + q;
+                const uint32_t smp = __shfl(my_smp, gbase + static_cast<int>(j & 63));
+                w[q] = WEIGHTED ? __shfl(my_w, gbase + static_cast<int>(j & 63)) : 1.f;
+                sl[q] = 0;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                if (WEIGHTED)
-                    acc[k] += static_cast<ACC>(w[u]) * static_cast<ACC>(g[u].v[k]);
-                else
-                    acc[k] += static_cast<ACC>(g[u].v[k]);
+                for (int u = 1; u < S; ++u) sl[q] += (cb + j) >= pre[u] ? 1 : 0;
+                const float* base = gcol[0];
+#pragma unroll
+                for (int u = 1; u < S; ++u) base = (sl[q] == u) ? gcol[u] : base;
+                if (j < n && base) {
+                    g[q] = *reinterpret_cast<const Pack<float, VEC>*>(
+                        base + static_cast<int64_t>(smp) * c.sumD);
+                } else {
+                    w[q] = 0.f;
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) g[q].v[k] = 0.f;
+                }
             }
+#pragma unroll
+            for (int q = 0; q < U; ++q)
+#pragma unroll
+                for (int u = 0; u < S; ++u)
+                    if (sl[q] == u)
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            if (WEIGHTED)   // w*g is exact in fp64; explicit fma in fp32
+                                acc[u][k] = fma(static_cast<ACC>(w[q]),
+                                                static_cast<ACC>(g[q].v[k]), acc[u][k]);
+                            else
+                                acc[u][k] += static_cast<ACC>(g[q].v[k]);
+                        }
+        }
     }
 }
 
-template <typename WT, typename ACC, int VEC, int U, bool WEIGHTED>
+// One batch of S short runs per worker: prefetch the S weight rows, sum the
+// runs' contributions, apply SGD.
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED>
+__device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ weights,
+                                            const TableDesc* __restrict__ descs,
+                                            const uint4 (&info)[S], int sub, int L, int gbase)
+{
+    for (int c0 = 0; c0 < c.max_D; c0 += VEC * L) {
+        const int col = c0 + sub * VEC;
+        Pack<WT, VEC> w_old[S];
+        ACC acc[S][VEC];
+        WT* wrow[S];
+        const float* gcol[S];
+        bool tw[S];
+        uint32_t len[S], pos0[S];
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const TableDesc& d = descs[info[u].w];
+            // a run whose table is narrower than this column slab contributes
+            // nothing here (its lanes keep the loop shape but load no rows)
+            const bool act = info[u].z > 0 && col < d.D;
+            len[u] = info[u].z;
+            pos0[u] = info[u].y;
+            wrow[u] = weights + d.w_off + static_cast<int64_t>(info[u].x - d.hash_off) * d.D + col;
+            gcol[u] = act ? c.grad + d.out_off + col : nullptr;
+            tw[u] = WEIGHTED && (d.flags & TD_WEIGHTED);
+            if (act) w_old[u] = *reinterpret_cast<const Pack<WT, VEC>*>(wrow[u]);
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) acc[u][q] = ACC(0);
+        }
+        flat_sum<ACC, VEC, S, U, WEIGHTED>(c, pos0, len, gcol, tw, sub, L, gbase, acc);
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+            if (gcol[u]) sgd_store<WT, ACC, VEC>(wrow[u], w_old[u], acc[u], c.lr);
+    }
+}
+
+// Short runs.  Batches of G*S consecutive run records are dealt to the
+// wavefronts round-robin (neighbouring runs of a Zipf table, which are the
+// long ones, land on different wavefronts); a batch is read with one load
+// (one record per lane, the next batch already in flight) and handed to the G
+// workers S at a time through lane shuffles.  Runs shorter than kF32Run
+// lookups sum in fp32 (error well inside tolerance); longer ones (only when
+// tau is raised) and fp16 tables use the ACC type.
+constexpr uint32_t kF32Run = 256;
+
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED>
 __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ weights,
+                                           const TableDesc* __restrict__ descs,
                                            uint32_t wave, uint32_t nwaves)
 {
     const int lane = threadIdx.x & 63;
     const int g_log2 = 6 - c.lpr_log2;
     const int G = 1 << g_log2;
+    const int L = 1 << c.lpr_log2;
     const int grp = lane >> c.lpr_log2;
-    const int sub = lane & ((1 << c.lpr_log2) - 1);
+    const int sub = lane & (L - 1);
+    const int gbase = grp << c.lpr_log2;
     const uint32_t nshort = c.counts[1];
-    const uint32_t per_wave = static_cast<uint32_t>(G * U);
-    for (uint32_t k0 = wave * per_wave; k0 < nshort; k0 += nwaves * per_wave) {
-        uint4 info[U];
-        TableDesc d[U];
+    const uint32_t per = static_cast<uint32_t>(G * S);
+    uint32_t k0 = wave * per;
+    uint4 nxt = make_uint4(0, 0, 0, 0);
+    if (lane < static_cast<int>(per) && k0 + lane < nshort) nxt = c.short_info[k0 + lane];
+    for (; k0 < nshort; k0 += nwaves * per) {
+        const uint4 mine = nxt;
+        const uint32_t k1 = k0 + nwaves * per;
+        nxt = make_uint4(0, 0, 0, 0);
+        if (lane < static_cast<int>(per) && k1 + lane < nshort) nxt = c.short_info[k1 + lane];
+        uint4 info[S];
+        uint32_t maxlen = 0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t k = k0 + static_cast<uint32_t>(u * G + grp);
-            info[u] = k < nshort ? c.short_info[k] : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < S; ++u) {
+            const int src = u * G + grp;
+            info[u].x = __shfl(mine.x, src);
+            info[u].y = __shfl(mine.y, src);
+            info[u].z = __shfl(mine.z, src);
+            info[u].w = __shfl(mine.w, src);
+            maxlen = max(maxlen, info[u].z);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) d[u] = c.tables[info[u].w];
-        for (int c0 = 0; c0 < c.max_D; c0 += (VEC << c.lpr_log2)) {
-            const int col = c0 + sub * VEC;
-            Pack<WT, VEC> w_old[U];
-            ACC acc[U][VEC];
-            uint32_t maxlen = 0;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool act = info[u].z > 0 && col < d[u].D;
-                if (act) {
-                    WT* wrow = weights + d[u].w_off +
-                               static_cast<int64_t>(info[u].x - d[u].hash_off) * d[u].D;
-                    w_old[u] = *reinterpret_cast<const Pack<WT, VEC>*>(wrow + col);
-                    maxlen = max(maxlen, info[u].z);
-                } else {
-                    info[u].z = act ? info[u].z : 0u;
-                }
-#pragma unroll
-                for (int q = 0; q < VEC; ++q) acc[u][q] = ACC(0);
-            }
-            for (uint32_t j = 0; j < maxlen; ++j) {
-                Pack<float, VEC> g[U];
-                float w[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    w[u] = 0.f;
-                    if (j < info[u].z) {
-                        const uint32_t ii = info[u].y + j;
-                        const uint32_t smp = c.sorted_sample[ii];
-                        if (WEIGHTED)
-                            w[u] = (d[u].flags & TD_WEIGHTED) ? c.sorted_psw[ii] : 1.f;
-                        g[u] = *reinterpret_cast<const Pack<float, VEC>*>(
-                            c.grad + static_cast<int64_t>(smp) * c.sumD + d[u].out_off + col);
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < VEC; ++q) g[u].v[q] = 0.f;
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int q = 0; q < VEC; ++q) {
-                        if (WEIGHTED)
-                            acc[u][q] += static_cast<ACC>(w[u]) * static_cast<ACC>(g[u].v[q]);
-                        else
-                            acc[u][q] += static_cast<ACC>(g[u].v[q]);
-                    }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (info[u].z == 0) continue;
-                WT* wrow = weights + d[u].w_off +
-                           static_cast<int64_t>(info[u].x - d[u].hash_off) * d[u].D;
-                sgd_store<WT, ACC, VEC>(wrow + col, w_old[u], acc[u], c.lr);
-            }
-        }
+        if (sizeof(ACC) == 8 && maxlen < kF32Run)
+            short_batch<WT, float, VEC, S, U, WEIGHTED>(c, weights, descs, info, sub, L, gbase);
+        else
+            short_batch<WT, ACC, VEC, S, U, WEIGHTED>(c, weights, descs, info, sub, L, gbase);
     }
 }
 
-// Long runs: one worker per chunk of `chunk` lookups writes its partial sum;
-// the worker that completes a run's last chunk (per-run arrival counter,
-// release fence before the count, acquire fence after) adds the run's
-// partials in chunk order and applies the update.  Nothing waits.
-template <typename WT, typename ACC, int VEC, bool WEIGHTED>
-__device__ __forceinline__ void long_chunks(const SegArgs& c, WT* __restrict__ weights,
-                                            ACC* __restrict__ partials, uint32_t wave,
-                                            uint32_t nwaves)
+// Long runs, step 1: one worker per chunk of `chunk` lookups writes the
+// chunk's partial sum (fp64 for fp32 tables) to the workspace.
+template <typename ACC, int VEC, bool WEIGHTED>
+__device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ partials,
+                                            uint32_t wave, uint32_t nwaves)
 {
     const int lane = threadIdx.x & 63;
     const int g_log2 = 6 - c.lpr_log2;
     const int grp = lane >> c.lpr_log2;
     const int sub = lane & ((1 << c.lpr_log2) - 1);
-    const int leader = grp << c.lpr_log2;
     const uint32_t nlong = min(c.counts[2], c.max_long);
     const uint32_t nchunks = min(c.counts[3], c.max_chunks);
     for (uint32_t q0 = wave << g_log2; q0 < nchunks; q0 += nwaves << g_log2) {
         const uint32_t q = q0 + grp;
-        const bool have = q < nchunks;
-        uint32_t lo = 0;
-        uint4 li = make_uint4(0, 0, 0, 0);
-        TableDesc d{};
-        if (have) {
-            uint32_t hi = nlong;  // long run owning chunk q: last with first chunk <= q
-            while (hi - lo > 1) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if (c.long_info[mid].w <= q) lo = mid; else hi = mid;
-            }
-            li = c.long_info[lo];
-            d = c.tables[find_table(c.hash_off, c.T, li.x)];
-            const bool tw = WEIGHTED && (d.flags & TD_WEIGHTED);
-            const uint32_t i0 = li.y + (q - li.w) * c.chunk;
-            const uint32_t i1 = min(li.y + li.z, i0 + c.chunk);
-            ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
-            for (int c0 = 0; c0 < d.D; c0 += (VEC << c.lpr_log2)) {
-                const int col = c0 + sub * VEC;
-                if (col >= d.D) continue;
-                ACC acc[VEC];
+        if (q >= nchunks) continue;
+        uint32_t lo = 0, hi = nlong;  // long run owning chunk q: last with first chunk <= q
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (c.long_info[mid].w <= q) lo = mid; else hi = mid;
+        }
+        const uint4 li = c.long_info[lo];
+        const TableDesc d = c.tables[find_table(c.hash_off, c.T, li.x)];
+        const bool tw = WEIGHTED && (d.flags & TD_WEIGHTED);
+        const uint32_t i0 = li.y + (q - li.w) * c.chunk;
+        const uint32_t i1 = min(li.y + li.z, i0 + c.chunk);
+        ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
+        for (int c0 = 0; c0 < c.max_D; c0 += (VEC << c.lpr_log2)) {
+            const int col = c0 + sub * VEC;
+            const uint32_t p0[1] = {i0};
+            const uint32_t ln[1] = {i1 - i0};
+            const float* const gc[1] = {col < d.D ? c.grad + d.out_off + col : nullptr};
+            const bool twa[1] = {tw};
+            ACC acc[1][VEC];
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) acc[k] = ACC(0);
-                seg_sum<ACC, VEC, 4, WEIGHTED>(c, c.grad + d.out_off + col, i0, i1, tw, acc);
+            for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
+            flat_sum<ACC, VEC, 1, 4, WEIGHTED>(c, p0, ln, gc, twa, sub, 1 << c.lpr_log2,
+                                               grp << c.lpr_log2, acc);
+            if (col < d.D) {
+                Pack<ACC, VEC> o;
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) prow[col + k] = acc[k];
+                for (int k = 0; k < VEC; ++k) o.v[k] = acc[0][k];
+                *reinterpret_cast<Pack<ACC, VEC>*>(prow + col) = o;
             }
         }
-        __threadfence();                       // partials visible device-wide first
-        uint32_t prior = 0;
-        if (have && sub == 0) prior = atomicAdd(&c.arrive[lo], 1u);
-        prior = __shfl(prior, leader);
-        const uint32_t nq = (li.z + c.chunk - 1) / c.chunk;
-        if (!have || prior + 1 != nq) continue;  // not the run's last chunk
-        __threadfence();                       // see every other chunk's partial
+    }
+}
+
+// Long runs, step 2 (next launch, so every partial is visible without a
+// device-wide cache flush): one worker per long run adds its chunks'
+// partials in chunk order -- 8 loads in flight -- and applies SGD.
+template <typename WT, typename ACC, int VEC>
+__global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict__ weights,
+                                                      const ACC* __restrict__ partials)
+{
+    const int lane = threadIdx.x & 63;
+    const int g_log2 = 6 - c.lpr_log2;
+    const int grp = lane >> c.lpr_log2;
+    const int sub = lane & ((1 << c.lpr_log2) - 1);
+    const uint32_t nlong = min(c.counts[2], c.max_long);
+    const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
+    for (uint32_t k0 = wave << g_log2; k0 < nlong; k0 += nwaves << g_log2) {
+        const uint32_t k = k0 + grp;
+        if (k >= nlong) continue;
+        const uint4 li = c.long_info[k];
+        const TableDesc d = c.tables[find_table(c.hash_off, c.T, li.x)];
         WT* __restrict__ wrow = weights + d.w_off + static_cast<int64_t>(li.x - d.hash_off) * d.D;
+        const uint32_t nq = (li.z + c.chunk - 1) / c.chunk;
+        const uint32_t qend = min(li.w + nq, c.max_chunks);
         for (int c0 = 0; c0 < d.D; c0 += (VEC << c.lpr_log2)) {
             const int col = c0 + sub * VEC;
             if (col >= d.D) continue;
@@ -254,28 +322,48 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, WT* __restrict__ w
             ACC acc[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) acc[j] = ACC(0);
-            for (uint32_t qq = li.w; qq < li.w + nq && qq < c.max_chunks; ++qq) {
-                const ACC* pr = partials + static_cast<int64_t>(qq) * c.max_D + col;
+            for (uint32_t qq = li.w; qq < qend; qq += 8) {
+                Pack<ACC, VEC> part[8];
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) acc[j] += pr[j];
+                for (int m = 0; m < 8; ++m) {
+                    if (qq + m < qend)
+                        part[m] = *reinterpret_cast<const Pack<ACC, VEC>*>(
+                            partials + static_cast<int64_t>(qq + m) * c.max_D + col);
+                    else
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) part[m].v[j] = ACC(0);
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) acc[j] += part[m].v[j];
             }
             sgd_store<WT, ACC, VEC>(wrow + col, w_old, acc, c.lr);
         }
     }
 }
 
-template <typename WT, typename ACC, int VEC, int U, bool WEIGHTED>
+constexpr int kLdsTables = 256;   // table descriptors staged in LDS
+
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ weights,
                                                  ACC* __restrict__ partials)
 {
+    __shared__ TableDesc sdesc[kLdsTables];
     const uint32_t wib = threadIdx.x >> 6;
-    if (blockIdx.x < c.short_blocks)
-        short_runs<WT, ACC, VEC, U, WEIGHTED>(c, weights, blockIdx.x * 4 + wib,
-                                              c.short_blocks * 4);
+    if (blockIdx.x < c.short_blocks) {
+        const TableDesc* descs = c.tables;
+        if (c.T <= kLdsTables) {
+            for (int i = threadIdx.x; i < c.T; i += 256) sdesc[i] = c.tables[i];
+            __syncthreads();
+            descs = sdesc;
+        }
+        short_runs<WT, ACC, VEC, S, U, WEIGHTED>(c, weights, descs, blockIdx.x * 4 + wib,
+                                                 c.short_blocks * 4);
+    }
     else
-        long_chunks<WT, ACC, VEC, WEIGHTED>(c, weights, partials,
-                                            (blockIdx.x - c.short_blocks) * 4 + wib,
-                                            (gridDim.x - c.short_blocks) * 4);
+        long_chunks<ACC, VEC, WEIGHTED>(c, partials, (blockIdx.x - c.short_blocks) * 4 + wib,
+                                        (gridDim.x - c.short_blocks) * 4);
 }
 
 uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
@@ -286,6 +374,17 @@ uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
     return static_cast<uint32_t>(b);
 }
 
+template <typename WT, typename ACC, int VEC, int S, int U>
+void launch_seg(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
+{
+    if (a.psw)
+        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true>), grid, dim3(256), 0, a.stream, c,
+                           w, partials);
+    else
+        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, false>), grid, dim3(256), 0, a.stream,
+                           c, w, partials);
+}
+
 template <typename WT, typename ACC, int VEC>
 hipError_t launch_all(const BwdArgs& a, SegArgs c)
 {
@@ -293,16 +392,17 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     char* ws = a.ws;
     ACC* partials = reinterpret_cast<ACC*>(ws + L.off_partials);
     WT* w = static_cast<WT*>(a.weights);
-    constexpr int U = 4;
     const int G = 1 << (6 - c.lpr_log2);
-    c.short_blocks = blocks_for(L.N, int64_t(4) * G * U, 2048);
+    c.short_blocks = blocks_for(L.N, int64_t(4) * G * 2, 2048);  // G*S runs per wave batch
     const uint32_t b_chunk = blocks_for(L.max_chunks, int64_t(4) * G, 1024);
-    if (a.psw)
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, U, true>), dim3(c.short_blocks + b_chunk),
-                           dim3(256), 0, a.stream, c, w, partials);
-    else
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, U, false>), dim3(c.short_blocks + b_chunk),
-                           dim3(256), 0, a.stream, c, w, partials);
+    const uint32_t b_long = blocks_for(L.max_long, int64_t(4) * G, 256);
+    const dim3 grid(c.short_blocks + b_chunk);
+    // short-run batches: S = 2 runs per worker, U = 4 gradient rows in flight
+    // (measured best of S in {1,2,4} x U in {4,8} on the uniform, stress and
+    // mixed workloads)
+    launch_seg<WT, ACC, VEC, 2, 4>(a, grid, c, w, partials);
+    hipLaunchKernelGGL((k_long_combine<WT, ACC, VEC>), dim3(b_long), dim3(256), 0, a.stream, c, w,
+                       static_cast<const ACC*>(partials));
     return hipGetLastError();
 }
 
@@ -332,11 +432,9 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.lpr_log2 = lpr_log2;
     c.max_D = p->max_D;
     c.grad = a.grad;
-    c.sorted_sample = reinterpret_cast<const uint32_t*>(ws + L.off_sorted_sample);
-    c.sorted_psw = reinterpret_cast<const float*>(ws + L.off_sorted_psw);
+    c.sorted_payload = ws + L.off_vals[a.final_buf];
     c.short_info = reinterpret_cast<const uint4*>(ws + L.off_short_info);
     c.long_info = reinterpret_cast<const uint4*>(ws + L.off_long_info);
-    c.arrive = reinterpret_cast<uint32_t*>(ws + L.off_arrive);
     c.counts = reinterpret_cast<const uint32_t*>(ws + L.off_ctl) + kCtlCounts;
     c.chunk = static_cast<uint32_t>(p->tuning.chunk);
     c.max_chunks = static_cast<uint32_t>(L.max_chunks);

@@ -9,14 +9,17 @@
 // Section "Three tiers, routed by run length": runs are classified against a
 // length threshold on the device, and the counts never go back to the host.
 // Section "Using it, and the import that stops you": per-sample weights must
-// stay paired with their lookup, so the sort is stable, carries the lookup
-// position j as payload, and its last pass gathers the sample id and the
-// per-sample weight of every sorted entry -- nothing is ever sorted twice.
+// stay paired with their lookup, so the sort is stable and carries the
+// lookup's sample id and per-sample weight as its payload -- nothing is ever
+// sorted twice and no weight is looked up again by position.
 //
 // Kernels (caller's stream, no host synchronisation):
-//   k_prep      per block of bags: key[j], sample[j] (the bag's sample id),
-//               digit histograms of every radix pass (LDS, then one global
-//               add per digit), and clears the look-back status words
+//   k_prep      per block of bags: key[j] and its payload (j itself for the
+//               sort_rle entry point; the bag's sample id, plus the per-sample
+//               weight when there is one, for the backward -- so the sorted
+//               result needs no gather), digit histograms of every radix pass
+//               (equal digits of a wavefront merged by ballots, then LDS, then
+//               one global add per digit), and clears the look-back words
 //   k_onesweep  one launch per radix pass (8-bit digits, only the
 //               ceil(log2(sum rows)) key bits are sorted): a tile takes a
 //               ticket in launch order, ranks its keys stably (wave ballots
@@ -45,6 +48,7 @@ constexpr uint32_t kFlagInc = 2u << 30;
 constexpr uint32_t kValMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 24;
 constexpr int kPrepMaxBags = 2048;   // bags per k_prep block (LDS offsets cache)
+constexpr int kPrepKeys = 1024;      // target keys per k_prep block
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -70,10 +74,11 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.rle_tile = kRleTile;
     L.rle_blocks = static_cast<int32_t>((N + kRleTile - 1) / kRleTile);
     const int64_t total_bags = int64_t(p->T) * B;
-    int64_t pb = total_bags / 64;
-    if (pb > 128) pb = 128;
+    int64_t pb = (N + kPrepKeys - 1) / kPrepKeys;   // ~kPrepKeys keys per k_prep block
+    if (pb > 1024) pb = 1024;
     const int64_t need = (total_bags + kPrepMaxBags - 1) / kPrepMaxBags;
     if (pb < need) pb = need;
+    if (pb > total_bags) pb = total_bags;
     if (pb < 1) pb = 1;
     L.prep_blocks = static_cast<int32_t>(pb);
     L.prep_bags = static_cast<int32_t>((total_bags + pb - 1) / pb);
@@ -92,11 +97,8 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_ctl = take(size_t(kCtlWords) * 4);   // fixed at offset 0 for every layout
     L.off_keys[0] = take(n4);
     L.off_keys[1] = take(n4);
-    L.off_vals[0] = take(n4);
-    L.off_vals[1] = take(n4);
-    L.off_sample = take(n4);
-    L.off_sorted_sample = take(n4);
-    L.off_sorted_psw = take(n4);
+    L.off_vals[0] = take(2 * n4);   // payload: 4 bytes, or 8 with per-sample weights
+    L.off_vals[1] = take(2 * n4);
     L.off_status = take(size_t(L.npasses) * kRadix * (L.sort_blocks > 0 ? L.sort_blocks : 1) * 4);
     L.off_rle_status = take(size_t(3) * (L.rle_blocks > 0 ? L.rle_blocks : 1) * 4);
     L.status_words = (L.off_rle_status - L.off_status) / 4 +
@@ -108,7 +110,6 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_long = take(n4);
     L.off_short_info = take(size_t(N + 1) * 16);
     L.off_long_info = take(size_t(ml + 1) * 16);
-    L.off_arrive = take(size_t(ml + 1) * 4);
     const size_t acc = p->wdtype == TBE_F32 ? 8 : 4;
     L.off_partials = take(size_t(mc > 0 ? mc : 1) * p->max_D * acc);
     L.total = o;
@@ -213,71 +214,111 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, int n)
 struct PassBits {
     int32_t npasses;
     int32_t shift[4];
+    int32_t bits[4];
     uint32_t mask[4];
 };
 
-template <typename IT>
+// Add 1 per active lane to hist[d]: lanes with equal digits are found with
+// nbits ballots and the lowest of them adds their count, so a hot digit (Zipf
+// keys) costs one LDS atomic per wavefront instead of one per lane.
+__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t d, bool ok, int nbits,
+                                              uint64_t lt)
+{
+    uint64_t peers = __ballot(ok);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = (d >> bit) & 1u;
+        const uint64_t bal = __ballot(on);
+        peers &= on ? bal : ~bal;
+    }
+    if (ok && (peers & lt) == 0) atomicAdd(&hist[d], static_cast<uint32_t>(__popcll(peers)));
+}
+
+// Payload carried through the sort next to each key.
+enum PayloadMode : int {
+    kPayloadPos = 0,      // lookup position j (the sort_rle entry point)
+    kPayloadSample = 1,   // sample id b of the lookup's bag
+    kPayloadSampleW = 2,  // (b, per-sample weight bits) pair
+};
+
+template <typename IT, int MODE>
 __global__ __launch_bounds__(256) void k_prep(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
-    const IT* __restrict__ indices, const IT* __restrict__ offsets, uint32_t* __restrict__ keys,
-    uint32_t* __restrict__ sample, uint32_t* __restrict__ totals, PassBits pb,
-    uint32_t* __restrict__ status, size_t status_words)
+    const IT* __restrict__ indices, const IT* __restrict__ offsets,
+    const float* __restrict__ psw, uint32_t* __restrict__ keys, void* __restrict__ vals,
+    uint32_t* __restrict__ totals, PassBits pb, uint32_t* __restrict__ status,
+    size_t status_words)
 {
     __shared__ uint32_t hist[4][kRadix];
     __shared__ int64_t boff[kPrepMaxBags + 1];
+    __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (size_t i = blockIdx.x * 256ull + tid; i < status_words; i += gridDim.x * 256ull)
         status[i] = 0u;
     for (int i = tid; i < 4 * kRadix; i += 256) (&hist[0][0])[i] = 0u;
     const uint32_t g0 = blockIdx.x * bags_per_block;
-    if (g0 >= total_bags) return;
-    const uint32_t nb = min(bags_per_block, total_bags - g0);
-    for (uint32_t i = tid; i <= nb; i += 256) boff[i] = static_cast<int64_t>(offsets[g0 + i]);
+    const uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
+    const uint32_t t_first = nb ? g0 / B : 0;
+    const uint32_t t_count = nb ? (g0 + nb - 1) / B - t_first + 1 : 0;   // <= nb
+    for (uint32_t i = tid; i <= nb && nb > 0; i += 256) boff[i] = static_cast<int64_t>(offsets[g0 + i]);
+    for (uint32_t i = tid; i < t_count; i += 256) hoff[i] = tables[t_first + i].hash_off;
     __syncthreads();
-    const int64_t P0 = boff[0], P1 = boff[nb];
-    constexpr int UN = 4;
+    const int64_t P0 = nb ? boff[0] : 0, P1 = nb ? boff[nb] : 0;
+    constexpr int UN = 8;
     for (int64_t base = P0; base < P1; base += 256 * UN) {
         IT id[UN];
+        float wv[UN];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int64_t p = base + u * 256 + tid;
             id[u] = p < P1 ? indices[p] : IT(0);
+            wv[u] = (MODE == kPayloadSampleW && p < P1) ? psw[p] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int64_t p = base + u * 256 + tid;
-            if (p >= P1) continue;
-            uint32_t lo = 0, hi = nb;  // boff[lo] <= p < boff[hi]
-            while (hi - lo > 1) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if (boff[mid] <= p) lo = mid; else hi = mid;
+            const bool ok = p < P1;
+            uint32_t key = 0;
+            if (ok) {
+                uint32_t lo = 0, hi = nb;  // boff[lo] <= p < boff[hi]
+                while (hi - lo > 1) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (boff[mid] <= p) lo = mid; else hi = mid;
+                }
+                const uint32_t g = g0 + lo;
+                const uint32_t t = g / B;
+                key = hoff[t - t_first] + static_cast<uint32_t>(id[u]);
+                keys[p] = key;
+                const uint32_t b = g - t * B;
+                if (MODE == kPayloadPos)
+                    static_cast<uint32_t*>(vals)[p] = static_cast<uint32_t>(p);
+                else if (MODE == kPayloadSample)
+                    static_cast<uint32_t*>(vals)[p] = b;
+                else
+                    static_cast<uint2*>(vals)[p] = make_uint2(b, __float_as_uint(wv[u]));
             }
-            const uint32_t g = g0 + lo;
-            const uint32_t t = g / B;
-            const uint32_t key = tables[t].hash_off + static_cast<uint32_t>(id[u]);
-            keys[p] = key;
-            sample[p] = g - t * B;
             for (int q = 0; q < pb.npasses; ++q)
-                atomicAdd(&hist[q][(key >> pb.shift[q]) & pb.mask[q]], 1u);
+                wave_hist_add(hist[q], (key >> pb.shift[q]) & pb.mask[q], ok, pb.bits[q], lt);
         }
     }
     __syncthreads();
+    // digit totals are spread over kTotCopies copies (fewer adds per address)
+    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadix);
     for (int q = 0; q < pb.npasses; ++q) {
         const uint32_t c = hist[q][tid];
-        if (c) atomicAdd(&totals[q * kRadix + tid], c);
+        if (c) atomicAdd(&tcopy[q * kRadix + tid], c);
     }
 }
 
 // ---------------------------------------------------------------------------
-template <int R, bool FIRST, bool LAST>
+template <int R, typename PT>
 __global__ __launch_bounds__(256) void k_onesweep(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
-    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t N, int shift,
+    const uint32_t* __restrict__ keys_in, const PT* __restrict__ vals_in,
+    uint32_t* __restrict__ keys_out, PT* __restrict__ vals_out, uint32_t N, int shift,
     int nbits, const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ err, uint32_t ntiles,
-    uint32_t* __restrict__ prev_totals, const uint32_t* __restrict__ sample,
-    const float* __restrict__ psw, uint32_t* __restrict__ sorted_sample,
-    float* __restrict__ sorted_psw)
+    uint32_t* __restrict__ prev_totals)
 {
     __shared__ uint32_t wcnt[kSortWaves][kRadix];
     __shared__ uint32_t gofs[kRadix];
@@ -290,7 +331,9 @@ __global__ __launch_bounds__(256) void k_onesweep(
     for (int i = tid; i < kSortWaves * kRadix; i += 256) (&wcnt[0][0])[i] = 0u;
     // exclusive scan of the global digit totals: first position of each digit
     {
-        const uint32_t v = totals[tid];
+        uint32_t v = 0;
+#pragma unroll
+        for (int cp = 0; cp < kTotCopies; ++cp) v += totals[cp * 4 * kRadix + tid];
         const uint32_t inc = wave_incl_scan(v, lane);
         if (lane == 63) wsum[wave] = inc;
         __syncthreads();
@@ -305,18 +348,21 @@ __global__ __launch_bounds__(256) void k_onesweep(
         return;
     }
     // the previous pass's digit totals are no longer needed: leave them zero
-    if (tile == 0 && prev_totals) prev_totals[tid] = 0u;
+    if (tile == 0 && prev_totals)
+#pragma unroll
+        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
 
     const uint32_t mask = (1u << nbits) - 1u;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const uint32_t wbase = tile * (256u * R) + static_cast<uint32_t>(wave) * (64u * R);
-    uint32_t k[R], v[R], dg[R], rk[R];
+    uint32_t k[R], dg[R], rk[R];
+    PT v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = wbase + r * 64u + lane;
         const bool ok = i < N;
         k[r] = ok ? keys_in[i] : 0u;
-        v[r] = FIRST ? i : (ok ? vals_in[i] : 0u);
+        if (ok) v[r] = vals_in[i];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -358,10 +404,6 @@ __global__ __launch_bounds__(256) void k_onesweep(
             if (pos >= N) continue;  // unreachable when the counts are consistent
             keys_out[pos] = k[r];
             vals_out[pos] = v[r];
-            if (LAST) {
-                sorted_sample[pos] = sample[v[r]];
-                if (psw) sorted_psw[pos] = psw[v[r]];
-            }
         }
     }
 }
@@ -400,7 +442,7 @@ __global__ __launch_bounds__(256) void k_rle(
     const uint32_t* __restrict__ keys, uint32_t N, uint32_t tau, uint32_t chunk, uint32_t ntiles,
     uint32_t* __restrict__ rstatus, uint32_t* __restrict__ ticket, uint32_t* __restrict__ err,
     const uint32_t* __restrict__ hash_off, int32_t T, uint4* __restrict__ short_info,
-    uint4* __restrict__ long_info, uint32_t* __restrict__ arrive, uint32_t* __restrict__ counts,
+    uint4* __restrict__ long_info, uint32_t* __restrict__ counts,
     uint32_t max_long, uint32_t* __restrict__ prev_totals,
     uint32_t* __restrict__ unique, uint32_t* __restrict__ run_start,
     uint32_t* __restrict__ run_len, uint32_t* __restrict__ short_ids,
@@ -419,7 +461,9 @@ __global__ __launch_bounds__(256) void k_rle(
         if (tid == 0) atomicOr(err, 2u);
         return;
     }
-    if (tile == 0 && prev_totals) prev_totals[tid] = 0u;   // last radix pass is done
+    if (tile == 0 && prev_totals)   // the last radix pass is done with its totals
+#pragma unroll
+        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
     const uint32_t i0 = tile * kRleTile + tid * kRleItems;
 
     uint32_t kk[kRleItems], len[kRleItems];
@@ -484,10 +528,7 @@ __global__ __launch_bounds__(256) void k_rle(
             run_len[r] = len[q];
         }
         if (len[q] >= tau) {
-            if (lb < max_long) {
-                long_info[lb] = make_uint4(key, i, len[q], cb);
-                arrive[lb] = 0u;
-            }
+            if (lb < max_long) long_info[lb] = make_uint4(key, i, len[q], cb);
             if (API) long_ids[lb] = r;
             ++lb;
             cb += (len[q] + chunk - 1) / chunk;
@@ -500,7 +541,7 @@ __global__ __launch_bounds__(256) void k_rle(
     }
 }
 
-template <int R>
+template <int R, typename PT>
 hipError_t sort_passes(BwdArgs& a)
 {
     const BwdLayout& L = a.L;
@@ -509,32 +550,40 @@ hipError_t sort_passes(BwdArgs& a)
     char* ws = a.ws;
     uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.off_keys[0]),
                          reinterpret_cast<uint32_t*>(ws + L.off_keys[1])};
-    uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + L.off_vals[0]),
-                         reinterpret_cast<uint32_t*>(ws + L.off_vals[1])};
+    PT* vals[2] = {reinterpret_cast<PT*>(ws + L.off_vals[0]),
+                   reinterpret_cast<PT*>(ws + L.off_vals[1])};
     uint32_t* ctl = reinterpret_cast<uint32_t*>(ws + L.off_ctl);
     uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.off_status);
-    uint32_t* sample = reinterpret_cast<uint32_t*>(ws + L.off_sample);
-    uint32_t* ssample = reinterpret_cast<uint32_t*>(ws + L.off_sorted_sample);
-    float* spsw = reinterpret_cast<float*>(ws + L.off_sorted_psw);
     int cur = 0;
     int shift = 0;
     for (int pass = 0; pass < L.npasses; ++pass) {
         const int nbits = L.digit_bits[pass];
-        const bool first = pass == 0, last = pass == L.npasses - 1;
-        auto kern = first ? (last ? k_onesweep<R, true, true> : k_onesweep<R, true, false>)
-                          : (last ? k_onesweep<R, false, true> : k_onesweep<R, false, false>);
-        hipLaunchKernelGGL(kern, dim3(nb), dim3(256), 0, a.stream, keys[cur], vals[cur],
-                           keys[cur ^ 1], vals[cur ^ 1], N, shift, nbits,
+        hipLaunchKernelGGL((k_onesweep<R, PT>), dim3(nb), dim3(256), 0, a.stream, keys[cur],
+                           vals[cur], keys[cur ^ 1], vals[cur ^ 1], N, shift, nbits,
                            ctl + kCtlTotals + pass * kRadix,
                            status + static_cast<size_t>(pass) * kRadix * nb,
                            ctl + kCtlTicket + pass, ctl + kCtlError, nb,
-                           pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadix : nullptr,
-                           sample, a.psw, ssample, spsw);
+                           pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadix : nullptr);
         cur ^= 1;
         shift += nbits;
     }
     a.final_buf = cur;
     return hipGetLastError();
+}
+
+template <typename IT, int MODE>
+void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
+{
+    const BwdLayout& L = a.L;
+    char* ws = a.ws;
+    hipLaunchKernelGGL((k_prep<IT, MODE>), dim3(L.prep_blocks), dim3(256), 0, a.stream,
+                       a.plan->d_tables, static_cast<uint32_t>(a.B), total_bags,
+                       static_cast<uint32_t>(L.prep_bags), static_cast<const IT*>(a.indices),
+                       static_cast<const IT*>(a.offsets), a.psw,
+                       reinterpret_cast<uint32_t*>(ws + L.off_keys[0]),
+                       static_cast<void*>(ws + L.off_vals[0]),
+                       reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlTotals, pb,
+                       reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words);
 }
 
 }  // namespace
@@ -558,32 +607,30 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
         int s = 0;
         for (int i = 0; i < L.npasses; ++i) {
             pb.shift[i] = s;
+            pb.bits[i] = L.digit_bits[i];
             pb.mask[i] = (1u << L.digit_bits[i]) - 1u;
             s += L.digit_bits[i];
         }
     }
-    {
-        uint32_t* keys0 = reinterpret_cast<uint32_t*>(ws + L.off_keys[0]);
-        uint32_t* sample = reinterpret_cast<uint32_t*>(ws + L.off_sample);
-        uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.off_status);
-        if (p->idtype == TBE_I64)
-            hipLaunchKernelGGL(k_prep<int64_t>, dim3(L.prep_blocks), dim3(256), 0, a.stream,
-                               p->d_tables, static_cast<uint32_t>(a.B), total_bags,
-                               static_cast<uint32_t>(L.prep_bags),
-                               static_cast<const int64_t*>(a.indices),
-                               static_cast<const int64_t*>(a.offsets), keys0, sample,
-                               ctl + kCtlTotals, pb, status, L.status_words);
-        else
-            hipLaunchKernelGGL(k_prep<int32_t>, dim3(L.prep_blocks), dim3(256), 0, a.stream,
-                               p->d_tables, static_cast<uint32_t>(a.B), total_bags,
-                               static_cast<uint32_t>(L.prep_bags),
-                               static_cast<const int32_t*>(a.indices),
-                               static_cast<const int32_t*>(a.offsets), keys0, sample,
-                               ctl + kCtlTotals, pb, status, L.status_words);
-    }
+    const int mode = api_outputs ? kPayloadPos : (a.psw ? kPayloadSampleW : kPayloadSample);
+    a.payload_pairs = mode == kPayloadSampleW;
+    const bool i64 = p->idtype == TBE_I64;
+    if (mode == kPayloadPos)
+        i64 ? launch_prep<int64_t, kPayloadPos>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadPos>(a, pb, total_bags);
+    else if (mode == kPayloadSample)
+        i64 ? launch_prep<int64_t, kPayloadSample>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSample>(a, pb, total_bags);
+    else
+        i64 ? launch_prep<int64_t, kPayloadSampleW>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSampleW>(a, pb, total_bags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = sort_rounds(L.N) == 16 ? sort_passes<16>(a) : sort_passes<8>(a);
+    const bool big = sort_rounds(L.N) == 16;
+    if (mode == kPayloadSampleW)
+        e = big ? sort_passes<16, uint2>(a) : sort_passes<8, uint2>(a);
+    else
+        e = big ? sort_passes<16, uint32_t>(a) : sort_passes<8, uint32_t>(a);
     if (e != hipSuccess) return e;
 
     const uint32_t* skeys = reinterpret_cast<const uint32_t*>(ws + L.off_keys[a.final_buf]);
@@ -595,8 +642,7 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                        reinterpret_cast<uint32_t*>(ws + L.off_rle_status), ctl + kCtlRleTicket,
                        ctl + kCtlError, p->d_hash_off, p->T,
                        reinterpret_cast<uint4*>(ws + L.off_short_info),
-                       reinterpret_cast<uint4*>(ws + L.off_long_info),
-                       reinterpret_cast<uint32_t*>(ws + L.off_arrive), ctl + kCtlCounts,
+                       reinterpret_cast<uint4*>(ws + L.off_long_info), ctl + kCtlCounts,
                        static_cast<uint32_t>(L.max_long),
                        ctl + kCtlTotals + (L.npasses - 1) * kRadix,
                        reinterpret_cast<uint32_t*>(ws + L.off_unique),

@@ -131,22 +131,22 @@ hipError_t launch_vec(const FwdArgs& a)
     const uint32_t total = static_cast<uint32_t>(p->T) * static_cast<uint32_t>(a.B);
     const uint32_t bpw = static_cast<uint32_t>(max(1, p->tuning.fwd_bags_per_wave));
     const uint32_t waves = (total + bpw - 1) / bpw;
-    const uint32_t wpb = 4;
-    const uint32_t blocks = (waves + wpb - 1) / wpb;
-    constexpr int U = (VEC * sizeof(WT) >= 16) ? 4 : 8;
+    const uint32_t blocks = (waves + 3) / 4;
     if (blocks == 0) return hipSuccess;
+    // rows in flight per lane: 4 with 16-byte loads, 8 with narrower ones
+    constexpr int U = (VEC * sizeof(WT) >= 16) ? 4 : 8;
+    const dim3 grid(blocks), block(256);
+    const auto* w = static_cast<const WT*>(a.weights);
+    const auto* ix = static_cast<const IT*>(a.indices);
+    const auto* of = static_cast<const IT*>(a.offsets);
+    const int ha = a.hist_active ? 1 : 0;
+    const uint32_t Bu = static_cast<uint32_t>(a.B);
     if (a.psw)
-        hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, true>), dim3(blocks), dim3(wpb * 64), 0,
-                           a.stream, p->d_tables, static_cast<uint32_t>(a.B), total, p->sum_D,
-                           static_cast<const WT*>(a.weights), static_cast<const IT*>(a.indices),
-                           static_cast<const IT*>(a.offsets), a.psw, a.out, bpw,
-                           a.hist_active ? 1 : 0);
+        hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, true>), grid, block, 0, a.stream,
+                           p->d_tables, Bu, total, p->sum_D, w, ix, of, a.psw, a.out, bpw, ha);
     else
-        hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, false>), dim3(blocks), dim3(wpb * 64), 0,
-                           a.stream, p->d_tables, static_cast<uint32_t>(a.B), total, p->sum_D,
-                           static_cast<const WT*>(a.weights), static_cast<const IT*>(a.indices),
-                           static_cast<const IT*>(a.offsets), a.psw, a.out, bpw,
-                           a.hist_active ? 1 : 0);
+        hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, false>), grid, block, 0, a.stream,
+                           p->d_tables, Bu, total, p->sum_D, w, ix, of, a.psw, a.out, bpw, ha);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ constexpr int64_t kMaxD = 4096;
 tbe_tuning default_tuning()
 {
     tbe_tuning t{};
-    t.tau = 256;              // long-run threshold (runs >= tau are split)
+    t.tau = 64;               // long-run threshold (runs >= tau are split); measured
     t.chunk = 256;            // lookups per long-run chunk
     t.hist_mode = 0;          // auto
     t.hist_min_mean_len = 64; // histogram path pays once bags are this long
@@ -232,6 +232,7 @@ static tbe_status prepare_bwd(const tbe_plan* p, int32_t B, const void* indices,
     a.L = bwd_layout(p, B, num_indices);
     a.stream = static_cast<hipStream_t>(stream);
     a.final_buf = 0;
+    a.payload_pairs = 0;
     if (workspace_bytes < a.L.total) return TBE_EINVAL;
     return TBE_OK;
 }

@@ -81,8 +81,9 @@ constexpr int kCtlTicket = 0;      // [4] tile tickets of the radix passes
 constexpr int kCtlRleTicket = 4;   // tile ticket of the run-length encode
 constexpr int kCtlError = 12;      // nonzero: a look-back wait gave up (sticky)
 constexpr int kCtlCounts = 8;      // [4] runs, short runs, long runs, long-run chunks
-constexpr int kCtlTotals = 16;     // [4][256] digit totals of every radix pass
-constexpr int kCtlWords = 16 + 4 * 256;
+constexpr int kTotCopies = 8;      // digit totals are kept in this many copies
+constexpr int kCtlTotals = 16;     // [kTotCopies][4][256] digit totals of every radix pass
+constexpr int kCtlWords = 16 + kTotCopies * 4 * 256;
 
 // Workspace carve-up (byte offsets), computed on the host.
 struct BwdLayout {
@@ -99,7 +100,6 @@ struct BwdLayout {
     int64_t max_chunks = 0;     // bound on long-run chunks
     int64_t max_long = 0;       // bound on long runs
     size_t off_keys[2], off_vals[2];
-    size_t off_sample, off_sorted_sample, off_sorted_psw;
     size_t off_status;          // [npasses][sort_blocks][256] look-back words
     size_t off_rle_status;      // [3][rle_blocks]
     size_t status_words = 0;    // words cleared by k_prep from off_status on
@@ -107,7 +107,6 @@ struct BwdLayout {
     size_t off_unique, off_run_start, off_run_len, off_short, off_long;
     size_t off_short_info;      // [N] {key, start, len, table}
     size_t off_long_info;       // [max_long] {key, start, len, first chunk}
-    size_t off_arrive;          // [max_long] chunks of each long run already summed
     size_t off_partials;        // [max_chunks * max_D] (fp64 or fp32)
     size_t total = 0;
 };
@@ -126,8 +125,10 @@ struct BwdArgs {
     char* ws;
     BwdLayout L;
     hipStream_t stream;
-    // filled by run_sort_rle: which ping-pong buffer holds the sorted result
+    // filled by run_sort_rle: which ping-pong buffer holds the sorted result,
+    // and whether its payload is (sample, weight) pairs or sample ids
     int final_buf;
+    int payload_pairs;
 };
 // api_outputs: also write unique keys, run starts / lengths and run-id lists.
 hipError_t run_sort_rle(BwdArgs& a, bool api_outputs);
