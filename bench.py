@@ -1,20 +1,33 @@
 #!/usr/bin/env python
-"""Benchmark of the TBE hot path on one MI355X: one step = forward pooled sum
-+ backward with exact SGD over one batch of the uniform workload (8 tables x
-1M rows x D=128 fp32, B=2048, Poisson(20) bags, uniform ids).
+"""Benchmark of the TBE hot path on one MI355X.
 
-Prints ONE JSON line on stdout.  Inputs are resident in HBM before the timed
-region; consecutive steps cycle through several distinct batches over the
-same tables so that no step re-reads the rows of the step before it from
-cache.  `--report` additionally prints per-configuration measurements of the
-forward and the backward (one JSON line each) on stderr.
+One step = forward pooled sum + backward with exact SGD over one batch of the
+uniform workload (8 tables x 1M rows x D=128 fp32, B=2048, Poisson(20) bags,
+uniform ids).  Prints ONE JSON line on stdout.
+
+* Inputs are resident in HBM before the timed region.  Consecutive steps cycle
+  through several distinct batches over the same tables, so no step re-reads
+  the rows of the step before it from cache.
+* Stage times come from HIP events that the library records on its stream at
+  its own stage boundaries (tbe_set_stage_events), so the dominant kernel's
+  duration is measured live inside the timed region.
+* --report also prints one JSON line per configuration (uniform, mixed, hist,
+  stress) with forward / backward stage times on stderr.
+* --calibrate-copy runs a 1 GiB device copy (for scaling rocprofv3 byte
+  counters); --summarize-pmc turns rocprofv3 --pmc CSVs into the traffic
+  summary under profiles/ that the roofline's "traffic" field reads.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import csv
+import glob
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -24,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_segment_uniform.json")
+SEGMENT_SRC = os.path.join(ROOT, "pooling_tbe_forward_amd", "csrc", "bwd_segment.hip")
 
 WORKLOAD_DESC = {
     "uniform": "uniform TBE: T=8 tables x 1,000,000 rows, D=128 fp32, B=2048, "
@@ -35,10 +50,11 @@ WORKLOAD_DESC = {
               "ids per bag, weighted",
     "toy": "toy TBE: T=3, rows {100,50,20}, D {8,16,4}, B=4",
 }
+BWD_STAGES = ["keys", "radix_sort", "rle", "segment_sgd", "long_combine"]
 
 
 def algorithmic_bytes(prob):
-    """Bytes the method must move (index type int32)."""
+    """Bytes the method must move (int32 indices), per launch / per pass."""
     s_i = 4
     s_w = 4 if prob.wdtype == "f32" else 2
     TB = prob.T * prob.B
@@ -55,13 +71,47 @@ def algorithmic_bytes(prob):
     jag = N * s_i + (TB + 1) * s_i + n_w * 4
     bits = max(1, int(np.ceil(np.log2(max(2, int(prob.rows.sum()))))))
     passes = (bits + 7) // 8
-    sort_bytes = passes * N * 16 + passes * N * 4
-    run_bytes = uk.size * 12
+    payload = 8 if prob.psw is not None else 4
+    sort_bytes = passes * N * (4 + payload) * 2
+    run_bytes = uk.size * 16
+    # segment-reduce + SGD kernel: every touched row read and written once,
+    # grad_output read once, the sorted payload and the run records read once
+    seg = 2 * uniq_row_bytes + out_bytes + N * payload + run_bytes
     return dict(N=N, unique_rows=int(uk.size), passes=passes,
                 fwd_min=jag + uniq_row_bytes + out_bytes,
                 fwd_lookup=jag + lookup_row_bytes + out_bytes,
                 bwd_min=jag + out_bytes + 2 * uniq_row_bytes + sort_bytes + run_bytes,
-                bwd_rows=2 * uniq_row_bytes)
+                seg_min=seg)
+
+
+class Hip:
+    """The HIP runtime torch loaded (events for the library's stage hook)."""
+
+    def __init__(self):
+        import torch
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        if not os.path.exists(path):
+            path = "libamdhip64.so"
+        h = ctypes.CDLL(path)
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        self.h = h
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
+        return float(v.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
 
 
 class Workload:
@@ -93,50 +143,52 @@ class Workload:
         self.bytes = [algorithmic_bytes(p) for p in self.probs]
         torch.cuda.synchronize()
 
-    def fwd(self, k):
+    def fwd(self, k, events=None):
         from pooling_tbe_forward_amd import tbe
         p, d = self.probs[k], self.inputs[k]
+        if events:
+            tbe.tbe_set_stage_events(self.plan, events)
         tbe.tbe_forward(self.plan, p.B, self.weights, d["indices"], d["offsets"], d["psw"],
                         self.out)
 
-    def bwd(self, k):
+    def bwd(self, k, events=None):
         from pooling_tbe_forward_amd import tbe
         p, d = self.probs[k], self.inputs[k]
+        if events:
+            tbe.tbe_set_stage_events(self.plan, events)
         tbe.tbe_backward_sgd(self.plan, p.B, self.weights, d["indices"], d["offsets"], d["psw"],
                              d["grad"], p.lr, self.ws)
 
 
-def run_steps(wl, steps, warmup, do_fwd=True, do_bwd=True):
-    """Warm up, then time `steps` steps; per-step HIP events on the stream the
-    library launches on (torch's current stream)."""
+def run_steps(wl, steps, warmup, hip):
+    """Warm up, then time `steps` steps (barrier + synchronize on both sides);
+    per-stage HIP events recorded by the library on its stream."""
     import torch
     nb = len(wl.probs)
     for s in range(warmup):
-        if do_fwd:
-            wl.fwd(s % nb)
-        if do_bwd:
-            wl.bwd(s % nb)
+        wl.fwd(s % nb)
+        wl.bwd(s % nb)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    fe = [[hip.event() for _ in range(2)] for _ in range(steps)]
+    be = [[hip.event() for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         k = s % nb
-        ev[s][0].record()
-        if do_fwd:
-            wl.fwd(k)
-        ev[s][1].record()
-        if do_bwd:
-            wl.bwd(k)
-        ev[s][2].record()
+        wl.fwd(k, fe[s])
+        wl.bwd(k, be[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    f_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(steps)])
-    b_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(steps)])
+    f_ms = np.array([hip.ms(fe[s][0], fe[s][1]) for s in range(steps)])
+    b_ms = np.array([hip.ms(be[s][0], be[s][5]) for s in range(steps)])
+    stage_ms = np.array([[hip.ms(be[s][i], be[s][i + 1]) for i in range(5)]
+                         for s in range(steps)])
+    for s in range(steps):
+        hip.destroy(fe[s] + be[s])
     ks = [s % nb for s in range(steps)]
-    n = np.array([wl.bytes[k]["N"] for k in ks], dtype=np.float64)
-    fb = np.array([wl.bytes[k]["fwd_min"] for k in ks], dtype=np.float64)
-    bb = np.array([wl.bytes[k]["bwd_min"] for k in ks], dtype=np.float64)
-    return dict(wall_s=wall, fwd_ms=f_ms, bwd_ms=b_ms, lookups=n, fwd_bytes=fb, bwd_bytes=bb)
+    pick = lambda key: np.array([wl.bytes[k][key] for k in ks], dtype=np.float64)
+    return dict(wall_s=wall, fwd_ms=f_ms, bwd_ms=b_ms, stage_ms=stage_ms, lookups=pick("N"),
+                fwd_bytes=pick("fwd_min"), bwd_bytes=pick("bwd_min"), seg_bytes=pick("seg_min"))
 
 
 def cpu_baseline(budget_s=20.0):
@@ -161,7 +213,7 @@ def cpu_baseline(budget_s=20.0):
         oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
                        prob.offsets, prob.psw, prob.weighted)
         t1 = time.perf_counter()
-        r = oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, 256)
+        r = oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, 64)
         t2 = time.perf_counter()
         oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
                             prob.offsets, prob.psw, prob.weighted, prob.grad, prob.lr,
@@ -189,31 +241,106 @@ def cpu_baseline(budget_s=20.0):
                 host_cpu=cpu, host_threads=os.cpu_count())
 
 
-def report_configs(steps, warmup):
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per k_segment launch from the committed PMC summary, or None
+    when the kernel source changed since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash(SEGMENT_SRC):
+        return None
+    return t.get("traffic_bytes")
+
+
+def summarize(r):
+    f = float(np.mean(r["fwd_ms"]))
+    b = float(np.mean(r["bwd_ms"]))
+    st = r["stage_ms"].mean(axis=0)
+    lk = float(np.mean(r["lookups"]))
+    return dict(fwd_ms=f, bwd_ms=b, fwd_lookups_per_s=lk / (f * 1e-3),
+                bwd_lookups_per_s=lk / (b * 1e-3),
+                fwd_hbm_gbps_min=float(np.mean(r["fwd_bytes"])) / (f * 1e-3) / 1e9,
+                bwd_hbm_gbps_min=float(np.mean(r["bwd_bytes"])) / (b * 1e-3) / 1e9,
+                bwd_stage_us={k: round(1e3 * float(v), 2) for k, v in zip(BWD_STAGES, st)})
+
+
+def report_configs(steps, warmup, hip):
     import torch
     for name in ("uniform", "mixed", "hist", "stress"):
         wl = Workload(name, nbatches=3 if name != "mixed" else 2)
-        r = run_steps(wl, steps, warmup)
-        b = wl.bytes[0]
-        f = float(np.median(r["fwd_ms"]))
-        g = float(np.median(r["bwd_ms"]))
-        line = dict(config=name, N=b["N"], unique_rows=b["unique_rows"],
-                    fwd_ms=f, bwd_ms=g,
-                    fwd_lookups_per_s=float(np.mean(r["lookups"]) / (f * 1e-3)),
-                    bwd_lookups_per_s=float(np.mean(r["lookups"]) / (g * 1e-3)),
-                    fwd_gbps_min=float(np.mean(r["fwd_bytes"]) / (f * 1e-3) / 1e9),
-                    bwd_gbps_min=float(np.mean(r["bwd_bytes"]) / (g * 1e-3) / 1e9),
-                    fwd_bytes_min=b["fwd_min"], fwd_bytes_lookup=b["fwd_lookup"],
-                    bwd_bytes_min=b["bwd_min"])
-        line["fwd_pct_peak"] = 100 * line["fwd_gbps_min"] / PEAK_HBM_GBPS
-        line["bwd_pct_peak"] = 100 * line["bwd_gbps_min"] / PEAK_HBM_GBPS
+        r = run_steps(wl, steps, warmup, hip)
+        line = dict(config=name, N=wl.bytes[0]["N"], unique_rows=wl.bytes[0]["unique_rows"],
+                    fwd_bytes_min=wl.bytes[0]["fwd_min"],
+                    fwd_bytes_lookup=wl.bytes[0]["fwd_lookup"],
+                    bwd_bytes_min=wl.bytes[0]["bwd_min"], **summarize(r))
+        line["fwd_pct_peak"] = 100 * line["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS
+        line["bwd_pct_peak"] = 100 * line["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS
         print(json.dumps(line), file=sys.stderr, flush=True)
         del wl
         torch.cuda.empty_cache()
 
 
+def calibrate_copy(reps=5, nbytes=1 << 30):
+    """A plain device copy of known size, to scale the byte counters."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes=nbytes, reps=reps)))
+
+
+def _pmc_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _kernel_avg(rows, pattern, counter):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if re.search(pattern, r["Kernel_Name"]) and r["Counter_Name"] == counter]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out, command):
+    """Per-launch HBM bytes of k_segment from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the ratio of a 1 GiB copy's known bytes to what
+    the same counter reported for it."""
+    copy_pat = r"copyBuffer|direct_copy"
+    cf, _ = _kernel_avg(_pmc_rows(copy_fetch_dir), copy_pat, "FETCH_SIZE")
+    cw, _ = _kernel_avg(_pmc_rows(copy_write_dir), copy_pat, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / cf if cf else None
+    w_scale = gib_kib / cw if cw else None
+    res = dict(kernel="k_segment", workload="uniform", command=command,
+               copy_fetch_kib=cf, copy_write_kib=cw, fetch_scale=f_scale, write_scale=w_scale,
+               source_sha256_16=source_hash(SEGMENT_SRC), kernels={})
+    fetch_rows, write_rows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    for name, pat in [("k_segment", r"k_segment"), ("k_fwd_gather", r"k_fwd_gather"),
+                      ("k_onesweep", r"k_onesweep"), ("k_rle", r"k_rle"),
+                      ("k_prep", r"k_prep"), ("k_long_combine", r"k_long_combine")]:
+        fv, nf = _kernel_avg(fetch_rows, pat, "FETCH_SIZE")
+        wv, nw = _kernel_avg(write_rows, pat, "WRITE_SIZE")
+        ent = dict(fetch_kib=fv, write_kib=wv, dispatches=[nf, nw])
+        if fv is not None and wv is not None and f_scale and w_scale:
+            ent["traffic_bytes"] = int((fv * f_scale + wv * w_scale) * 1024)
+        res["kernels"][name] = ent
+    res["traffic_bytes"] = res["kernels"]["k_segment"].get("traffic_bytes")
+    json.dump(res, open(out, "w"), indent=1)
+    print(json.dumps(res))
+
+
 def main():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
@@ -222,8 +349,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--report", action="store_true",
-                    help="also print per-configuration fwd/bwd measurements on stderr")
+                    help="also print per-configuration measurements on stderr")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"))
+    ap.add_argument("--pmc-out", default=TRAFFIC_FILE)
+    ap.add_argument("--pmc-command", default="")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.pmc_out, args.pmc_command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this operator's hot path runs on a single "
               "MI355X here (sharding across GPUs is described, not built); use --gpus 1.",
@@ -236,23 +370,25 @@ def main():
         from pooling_tbe_forward_amd import build
         build.build()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    hip = Hip()
 
     wl = Workload(args.config, nbatches=args.batches)
-    r = run_steps(wl, args.steps, args.warmup)
+    r = run_steps(wl, args.steps, args.warmup, hip)
     step_ms = 1e3 * r["wall_s"] / args.steps
     lookups = float(np.sum(r["lookups"]))
     value = lookups / r["wall_s"]
-    f_ms = float(np.mean(r["fwd_ms"]))
-    b_ms = float(np.mean(r["bwd_ms"]))
-    f_gbps = float(np.mean(r["fwd_bytes"])) / (f_ms * 1e-3) / 1e9
-    b_gbps = float(np.mean(r["bwd_bytes"])) / (b_ms * 1e-3) / 1e9
+    sm = summarize(r)
     p0 = wl.probs[0]
-    # Dominant kernel: the forward gather (one launch per tbe_forward on this
-    # workload); its algorithmic bytes per launch are the forward's B_min.
-    roof = dict(bound="hbm", kernel="k_fwd_gather", achieved=round(f_gbps, 1),
-                peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(f_gbps / PEAK_HBM_GBPS, 4),
-                traffic=None, avg_launch_us=round(1e3 * f_ms, 2),
-                bytes_per_launch=int(np.mean(r["fwd_bytes"])))
+    seg_us = float(np.mean(r["stage_ms"][:, 3])) * 1e3
+    seg_bytes = float(np.mean(r["seg_bytes"]))
+    seg_gbps = seg_bytes / (seg_us * 1e-6) / 1e9
+    roof = dict(bound="hbm", kernel="k_segment (backward segment-reduce + SGD)",
+                achieved=round(seg_gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                frac=round(seg_gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(),
+                avg_launch_us=round(seg_us, 2), bytes_per_launch=int(seg_bytes))
     out = dict(metric="TBE fwd/bwd lookups/s and achieved HBM GB/s (% of peak) on 1 MI355X",
                value=value, unit="lookups/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=step_ms, higher_is_better=True, scaling="weak", vs_baseline=None,
@@ -260,18 +396,14 @@ def main():
                config=dict(workload=WORKLOAD_DESC[args.config], T=int(p0.T), B=int(p0.B),
                            lookups_per_step=int(np.mean(r["lookups"])),
                            batches_cycled=args.batches, index_dtype="int32",
-                           bwd_accumulation="f64", parallelism="single GPU"),
-               fwd_ms=f_ms, bwd_ms=b_ms,
-               fwd_lookups_per_s=float(np.mean(r["lookups"])) / (f_ms * 1e-3),
-               bwd_lookups_per_s=float(np.mean(r["lookups"])) / (b_ms * 1e-3),
-               fwd_hbm_gbps_min=f_gbps, bwd_hbm_gbps_min=b_gbps,
-               fwd_pct_peak=100 * f_gbps / PEAK_HBM_GBPS,
-               bwd_pct_peak=100 * b_gbps / PEAK_HBM_GBPS,
+                           parallelism="single GPU"),
+               fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
+               bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
                roofline=roof)
     del wl
     torch.cuda.empty_cache()
     if args.report:
-        report_configs(max(10, args.steps // 2), 3)
+        report_configs(max(10, args.steps // 2), 3, hip)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -180,6 +180,19 @@ tbe_status tbe_bounds_check(const tbe_plan* plan, int32_t B, const void* indices
 tbe_status tbe_get_tuning(const tbe_plan* plan, tbe_tuning* tuning);
 tbe_status tbe_set_tuning(tbe_plan* plan, const tbe_tuning* tuning);
 
+/*
+ * Optional per-stage timing, for profilers and benchmarks.  events: host array
+ * of n hipEvent_t handles the caller created; the NEXT tbe_forward or
+ * tbe_backward_sgd call on this plan records them on its stream at its stage
+ * boundaries, then forgets them (one-shot).  Forward: [0] before its first
+ * kernel, [1] after its last.  Backward: [0] start, [1] after the key/payload
+ * pass, [2] after the radix passes, [3] after run-length encoding, [4] after
+ * the segment-reduce + SGD kernel, [5] after the long-run combine.  Events
+ * beyond n are not recorded.  events = NULL (or n = 0) clears.  Not for plans
+ * shared by concurrent calls.
+ */
+tbe_status tbe_set_stage_events(tbe_plan* plan, void* const* events, int32_t n);
+
 /* Static English text for a status code. */
 const char* tbe_status_string(tbe_status status);
 

@@ -401,8 +401,10 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     // (measured best of S in {1,2,4} x U in {4,8} on the uniform, stress and
     // mixed workloads)
     launch_seg<WT, ACC, VEC, 2, 4>(a, grid, c, w, partials);
+    stage_mark(a.plan, 4, a.stream);
     hipLaunchKernelGGL((k_long_combine<WT, ACC, VEC>), dim3(b_long), dim3(256), 0, a.stream, c, w,
                        static_cast<const ACC*>(partials));
+    stage_mark(a.plan, 5, a.stream);
     return hipGetLastError();
 }
 

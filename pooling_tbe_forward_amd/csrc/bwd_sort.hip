@@ -626,12 +626,14 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
             : launch_prep<int32_t, kPayloadSampleW>(a, pb, total_bags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    stage_mark(p, 1, a.stream);
     const bool big = sort_rounds(L.N) == 16;
     if (mode == kPayloadSampleW)
         e = big ? sort_passes<16, uint2>(a) : sort_passes<8, uint2>(a);
     else
         e = big ? sort_passes<16, uint32_t>(a) : sort_passes<8, uint32_t>(a);
     if (e != hipSuccess) return e;
+    stage_mark(p, 2, a.stream);
 
     const uint32_t* skeys = reinterpret_cast<const uint32_t*>(ws + L.off_keys[a.final_buf]);
     const uint32_t tau = static_cast<uint32_t>(p->tuning.tau);
@@ -650,6 +652,7 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                        reinterpret_cast<uint32_t*>(ws + L.off_run_len),
                        reinterpret_cast<uint32_t*>(ws + L.off_short),
                        reinterpret_cast<uint32_t*>(ws + L.off_long));
+    stage_mark(p, 3, a.stream);
     return hipGetLastError();
 }
 

@@ -197,11 +197,13 @@ tbe_status tbe_forward(const tbe_plan* p, int32_t B, const void* weights, const 
         vec >>= 1;
     FwdArgs a{p, B, weights, indices, offsets, psw, output, vec, use_hist(p, B, num_indices),
               static_cast<hipStream_t>(stream)};
-    if (a.hist_active) {
-        if (launch_fwd_hist(a) != hipSuccess) return TBE_EHIP;
-    }
-    if (launch_fwd_gather(a) != hipSuccess) return TBE_EHIP;
-    return TBE_OK;
+    stage_mark(p, 0, a.stream);
+    tbe_status st2 = TBE_OK;
+    if (a.hist_active && launch_fwd_hist(a) != hipSuccess) st2 = TBE_EHIP;
+    if (st2 == TBE_OK && launch_fwd_gather(a) != hipSuccess) st2 = TBE_EHIP;
+    stage_mark(p, 1, a.stream);
+    const_cast<tbe_plan*>(p)->n_stage_ev = 0;
+    return st2;
 }
 
 size_t tbe_backward_workspace_bytes(const tbe_plan* p, int32_t B, int64_t num_indices)
@@ -253,9 +255,12 @@ tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const v
     a.grad = grad_output;
     a.weights = weights;
     a.lr = lr;
-    if (run_sort_rle(a, false) != hipSuccess) return TBE_EHIP;
-    if (run_segment_sgd(a) != hipSuccess) return TBE_EHIP;
-    return TBE_OK;
+    stage_mark(p, 0, a.stream);
+    tbe_status st2 = TBE_OK;
+    if (run_sort_rle(a, false) != hipSuccess) st2 = TBE_EHIP;
+    else if (run_segment_sgd(a) != hipSuccess) st2 = TBE_EHIP;
+    const_cast<tbe_plan*>(p)->n_stage_ev = 0;
+    return st2;
 }
 
 tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64_t num_indices,
@@ -267,7 +272,9 @@ tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64
     tbe_status st = prepare_bwd(p, B, indices, num_indices, offsets, workspace,
                                 workspace_bytes, stream, a);
     if (st != TBE_OK) return st;
-    if (run_sort_rle(a, true) != hipSuccess) return TBE_EHIP;
+    const hipError_t e = run_sort_rle(a, true);
+    const_cast<tbe_plan*>(p)->n_stage_ev = 0;
+    if (e != hipSuccess) return TBE_EHIP;
     char* ws = a.ws;
     const BwdLayout& L = a.L;
     view->sorted_keys = reinterpret_cast<uint32_t*>(ws + L.off_keys[a.final_buf]);
@@ -278,6 +285,16 @@ tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64
     view->short_runs = reinterpret_cast<uint32_t*>(ws + L.off_short);
     view->long_runs = reinterpret_cast<uint32_t*>(ws + L.off_long);
     view->counts = reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlCounts;
+    return TBE_OK;
+}
+
+tbe_status tbe_set_stage_events(tbe_plan* p, void* const* events, int32_t n)
+{
+    if (!p || n < 0) return TBE_EINVAL;
+    if (!events) n = 0;
+    if (n > 8) n = 8;
+    for (int k = 0; k < 8; ++k) p->stage_ev[k] = k < n ? static_cast<hipEvent_t>(events[k]) : nullptr;
+    p->n_stage_ev = n;
     return TBE_OK;
 }
 

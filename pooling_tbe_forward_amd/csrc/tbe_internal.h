@@ -52,6 +52,9 @@ struct tbe_plan {
     uint32_t* d_hash_off = nullptr;       // device [T+1]
     tbe_tuning tuning{};
     int device = 0;
+    // one-shot stage events of the next call (tbe_set_stage_events)
+    hipEvent_t stage_ev[8] = {};
+    int32_t n_stage_ev = 0;
 };
 
 namespace tbe {
@@ -133,6 +136,12 @@ struct BwdArgs {
 // api_outputs: also write unique keys, run starts / lengths and run-id lists.
 hipError_t run_sort_rle(BwdArgs& a, bool api_outputs);
 hipError_t run_segment_sgd(const BwdArgs& a);
+
+// Record stage event k of the next call, if the caller asked for it.
+inline void stage_mark(const tbe_plan* p, int k, hipStream_t s)
+{
+    if (k < p->n_stage_ev && p->stage_ev[k]) (void)hipEventRecord(p->stage_ev[k], s);
+}
 
 // Zero the control block (first kCtlWords words) of a fresh workspace.
 hipError_t launch_workspace_init(void* ws, hipStream_t s);

@@ -64,6 +64,8 @@ def lib():
         L.tbe_backward_sgd.restype = I32
         L.tbe_sort_rle.argtypes = [P, I32, P, I64, P, P, SZ, ctypes.POINTER(tbe_sort_view), P]
         L.tbe_sort_rle.restype = I32
+        L.tbe_set_stage_events.argtypes = [P, ctypes.POINTER(ctypes.c_void_p), I32]
+        L.tbe_set_stage_events.restype = I32
         L.tbe_workspace_init.argtypes = [P, SZ, P]
         L.tbe_workspace_init.restype = I32
         L.tbe_bounds_check.argtypes = [P, I32, P, I64, P, P, P]
@@ -189,6 +191,15 @@ def tbe_forward(plan: Plan, B: int, weights, indices, offsets, per_sample_weight
 
 def tbe_backward_workspace_bytes(plan: Plan, B: int, num_indices: int) -> int:
     return int(lib().tbe_backward_workspace_bytes(plan.handle, int(B), int(num_indices)))
+
+
+def tbe_set_stage_events(plan: Plan, events):
+    """events: sequence of raw hipEvent_t handles (ints); None clears."""
+    if not events:
+        _check(lib().tbe_set_stage_events(plan.handle, None, 0), "tbe_set_stage_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib().tbe_set_stage_events(plan.handle, arr, len(events)), "tbe_set_stage_events")
 
 
 def tbe_workspace_init(workspace, stream=None):

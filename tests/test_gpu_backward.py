@@ -337,3 +337,32 @@ def test_workspace_reused_across_calls_and_sizes():
         rep = _sampled_backward_check(prob, None, w0, _key_sample(prob, o, n_short=500, seed=k))
         assert rep["ok"], (k, rep)
         assert int(_u32(ws[48:52].view(torch.int32))[0]) == 0   # error word stays clear
+
+
+def test_stage_events_bracket_the_backward():
+    """Stage events are recorded in order on the call's stream, their gaps add
+    up to the whole call, and they are consumed by one call only."""
+    prob = dg.make_problem("stress", seed=40, B=256)
+    plan = H.make_plan(prob)
+    d = H.device_inputs(prob)
+    ws = _workspace(plan, prob)
+    w = dg.packed_weights_torch(prob, "cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()          # torch creates its events lazily, on first record
+    torch.cuda.synchronize()
+    tbe.tbe_set_stage_events(plan, [e.cuda_event for e in evs])
+    tbe.tbe_backward_sgd(plan, prob.B, w, d["indices"], d["offsets"], d["psw"], d["grad"],
+                         prob.lr, ws)
+    torch.cuda.synchronize()
+    gaps = [evs[k].elapsed_time(evs[k + 1]) for k in range(5)]
+    assert all(g >= 0.0 for g in gaps), gaps
+    total = evs[0].elapsed_time(evs[5])
+    assert total > 0.0 and abs(sum(gaps) - total) <= 1e-3 + 1e-3 * total
+    # one-shot: a second call must not touch the events again
+    late = torch.cuda.Event(enable_timing=True)
+    late.record()
+    tbe.tbe_backward_sgd(plan, prob.B, w, d["indices"], d["offsets"], d["psw"], d["grad"],
+                         prob.lr, ws)
+    torch.cuda.synchronize()
+    assert evs[5].elapsed_time(late) >= 0.0
