@@ -8,7 +8,12 @@ uniform ids).  Prints ONE JSON line on stdout.
 * Inputs are resident in HBM before the timed region.  Consecutive steps cycle
   through several distinct batches over the same tables, so no step re-reads
   the rows of the step before it from cache.
-* Stage times come from HIP events that the library records on its stream at
+* The step's schedule: by default the backward's integer stage (key pass,
+  radix sort, run-length encode; it reads only the batch's indices) runs on a
+  second stream while the forward runs, and the segment reduce + SGD follows
+  both (--schedule serial: forward, then the whole backward, on one stream).
+  Both schedules are timed; the JSON line carries both step times.
+* Stage times come from HIP events that the library records on its streams at
   its own stage boundaries (tbe_set_stage_events), so the dominant kernel's
   duration is measured live inside the timed region.
 * --report also prints one JSON line per configuration (uniform, mixed, hist,
@@ -51,6 +56,11 @@ WORKLOAD_DESC = {
     "toy": "toy TBE: T=3, rows {100,50,20}, D {8,16,4}, B=4",
 }
 BWD_STAGES = ["keys", "radix_sort", "rle", "segment_sgd", "long_combine"]
+SCHEDULE_DESC = {
+    "overlap": "backward integer stage (tbe_backward_prepare) on a second stream concurrently "
+               "with tbe_forward, then tbe_backward_apply",
+    "serial": "tbe_forward then tbe_backward_sgd on one stream",
+}
 
 
 def algorithmic_bytes(prob):
@@ -97,12 +107,16 @@ class Hip:
         h.hipEventDestroy.argtypes = [ctypes.c_void_p]
         h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                           ctypes.c_void_p]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.h = h
 
     def event(self):
         e = ctypes.c_void_p()
         assert self.h.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
+
+    def record(self, ev, stream):
+        assert self.h.hipEventRecord(ev, ctypes.c_void_p(stream.cuda_stream)) == 0
 
     def ms(self, a, b):
         v = ctypes.c_float()
@@ -141,6 +155,9 @@ class Workload:
         self.ws = tbe.tbe_workspace_init(torch.empty(ws, dtype=torch.uint8, device="cuda"))
         self.out = torch.empty(p0.B, p0.sum_D, dtype=torch.float32, device="cuda")
         self.bytes = [algorithmic_bytes(p) for p in self.probs]
+        self.side = torch.cuda.Stream()          # default priority
+        self.ev_start = torch.cuda.Event()
+        self.ev_ready = torch.cuda.Event()
         torch.cuda.synchronize()
 
     def fwd(self, k, events=None):
@@ -159,30 +176,61 @@ class Workload:
         tbe.tbe_backward_sgd(self.plan, p.B, self.weights, d["indices"], d["offsets"], d["psw"],
                              d["grad"], p.lr, self.ws)
 
+    def step_overlapped(self, k, hip=None, fe=None, be=None):
+        """The backward's integer stage on a second stream while the forward
+        runs; the segment reduce + SGD follows both.  be[6] (if given) is
+        recorded on the main stream right before the apply half starts."""
+        import torch
+        from pooling_tbe_forward_amd import tbe
+        p, d = self.probs[k], self.inputs[k]
+        main = torch.cuda.current_stream()
+        self.ev_start.record(main)
+        self.side.wait_event(self.ev_start)
+        if be:
+            tbe.tbe_set_stage_events(self.plan, be[:4])
+        tbe.tbe_backward_prepare(self.plan, p.B, d["indices"], d["offsets"], d["psw"], self.ws,
+                                 stream=self.side)
+        if fe:
+            tbe.tbe_set_stage_events(self.plan, fe)
+        tbe.tbe_forward(self.plan, p.B, self.weights, d["indices"], d["offsets"], d["psw"],
+                        self.out, stream=main)
+        self.ev_ready.record(self.side)
+        main.wait_event(self.ev_ready)
+        if be:
+            hip.record(be[6], main)
+            tbe.tbe_set_stage_events(self.plan, [None] * 4 + be[4:6])
+        tbe.tbe_backward_apply(self.plan, p.B, p.N, d["psw"] is not None, self.weights,
+                               d["grad"], p.lr, self.ws, stream=main)
 
-def run_steps(wl, steps, warmup, hip):
-    """Warm up, then time `steps` steps (barrier + synchronize on both sides);
-    per-stage HIP events recorded by the library on its stream."""
+
+def run_steps(wl, steps, warmup, hip, overlap=False):
+    """Warm up, then time `steps` steps (synchronize on both sides); per-stage
+    HIP events recorded by the library on the streams it runs on.
+
+    overlap=False: forward, then the whole backward, on one stream.
+    overlap=True: the backward's integer stage (key pass, radix sort, RLE) on a
+    second stream concurrently with the forward, then segment reduce + SGD."""
     import torch
     nb = len(wl.probs)
+    one = (lambda k, fe=None, be=None: wl.step_overlapped(k, hip, fe, be)) if overlap else \
+        (lambda k, fe=None, be=None: (wl.fwd(k, fe), wl.bwd(k, be)))
     for s in range(warmup):
-        wl.fwd(s % nb)
-        wl.bwd(s % nb)
+        one(s % nb)
     torch.cuda.synchronize()
     fe = [[hip.event() for _ in range(2)] for _ in range(steps)]
-    be = [[hip.event() for _ in range(6)] for _ in range(steps)]
+    be = [[hip.event() for _ in range(7)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        k = s % nb
-        wl.fwd(k, fe[s])
-        wl.bwd(k, be[s])
+        one(s % nb, fe[s], be[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     f_ms = np.array([hip.ms(fe[s][0], fe[s][1]) for s in range(steps)])
     b_ms = np.array([hip.ms(be[s][0], be[s][5]) for s in range(steps)])
     stage_ms = np.array([[hip.ms(be[s][i], be[s][i + 1]) for i in range(5)]
                          for s in range(steps)])
+    if overlap:   # the segment stage starts at the apply half, on the main stream
+        stage_ms[:, 3] = [hip.ms(be[s][6], be[s][4]) for s in range(steps)]
     for s in range(steps):
         hip.destroy(fe[s] + be[s])
     ks = [s % nb for s in range(steps)]
@@ -274,7 +322,10 @@ def report_configs(steps, warmup, hip):
     for name in ("uniform", "mixed", "hist", "stress"):
         wl = Workload(name, nbatches=3 if name != "mixed" else 2)
         r = run_steps(wl, steps, warmup, hip)
+        r2 = run_steps(wl, steps, warmup, hip, overlap=True)
         line = dict(config=name, N=wl.bytes[0]["N"], unique_rows=wl.bytes[0]["unique_rows"],
+                    step_ms_serial=1e3 * r["wall_s"] / steps,
+                    step_ms_overlap=1e3 * r2["wall_s"] / steps,
                     fwd_bytes_min=wl.bytes[0]["fwd_min"],
                     fwd_bytes_lookup=wl.bytes[0]["fwd_lookup"],
                     bwd_bytes_min=wl.bytes[0]["bwd_min"], **summarize(r))
@@ -345,6 +396,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batches", type=int, default=4)
+    ap.add_argument("--schedule", default="serial", choices=sorted(SCHEDULE_DESC))
     ap.add_argument("--config", default="uniform", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -376,11 +428,16 @@ def main():
     hip = Hip()
 
     wl = Workload(args.config, nbatches=args.batches)
-    r = run_steps(wl, args.steps, args.warmup, hip)
+    # the reported step: integer stage overlapped with the forward (default),
+    # or everything on one stream; the other schedule is timed too, for its
+    # per-stage breakdown and as a cross-check
+    r_serial = run_steps(wl, args.steps, args.warmup, hip, overlap=False)
+    r_over = run_steps(wl, args.steps, args.warmup, hip, overlap=True)
+    r = r_over if args.schedule == "overlap" else r_serial
     step_ms = 1e3 * r["wall_s"] / args.steps
     lookups = float(np.sum(r["lookups"]))
     value = lookups / r["wall_s"]
-    sm = summarize(r)
+    sm = summarize(r_serial)
     p0 = wl.probs[0]
     seg_us = float(np.mean(r["stage_ms"][:, 3])) * 1e3
     seg_bytes = float(np.mean(r["seg_bytes"]))
@@ -397,6 +454,9 @@ def main():
                            lookups_per_step=int(np.mean(r["lookups"])),
                            batches_cycled=args.batches, index_dtype="int32",
                            parallelism="single GPU"),
+               schedule=SCHEDULE_DESC[args.schedule],
+               ms_per_step_serial=1e3 * r_serial["wall_s"] / args.steps,
+               ms_per_step_overlap=1e3 * r_over["wall_s"] / args.steps,
                fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
                bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
                roofline=roof)

@@ -158,6 +158,33 @@ tbe_status tbe_backward_sgd(const tbe_plan* plan, int32_t B, void* weights,
                             float lr, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The backward in two halves, for callers that overlap its integer stage with
+ * other work.  The integer stage reads only indices, offsets and per-sample
+ * weights, so it can run on a second stream while the forward of the same
+ * batch runs; tbe_backward_sgd is exactly prepare followed by apply on one
+ * stream.
+ *
+ * tbe_backward_prepare: linearize, stable radix sort (payload: sample id and
+ * per-sample weight), run-length encode and classify runs, into the
+ * workspace (section "Why the backward is the hard half"; classification
+ * from section "Three tiers, routed by run length").  Arguments as for
+ * tbe_backward_sgd.
+ *
+ * tbe_backward_apply: segment reduce + exact SGD from a workspace that
+ * tbe_backward_prepare filled for the same plan, B and num_indices, with the
+ * plan's tuning unchanged in between.  weighted: nonzero iff prepare was
+ * given per-sample weights.  The caller orders apply after prepare (same
+ * stream, or an event); errors as for tbe_backward_sgd.
+ */
+tbe_status tbe_backward_prepare(const tbe_plan* plan, int32_t B, const void* indices,
+                                int64_t num_indices, const void* offsets,
+                                const float* per_sample_weights, void* workspace,
+                                size_t workspace_bytes, void* stream);
+tbe_status tbe_backward_apply(const tbe_plan* plan, int32_t B, int64_t num_indices,
+                              int32_t weighted, void* weights, const float* grad_output,
+                              float lr, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The backward's integer stage alone: linearize, stable radix sort,
  * run-length encode, classify against tuning.tau.  Fills *view (host struct)
  * with device pointers into the workspace.
@@ -182,12 +209,13 @@ tbe_status tbe_set_tuning(tbe_plan* plan, const tbe_tuning* tuning);
 
 /*
  * Optional per-stage timing, for profilers and benchmarks.  events: host array
- * of n hipEvent_t handles the caller created; the NEXT tbe_forward or
- * tbe_backward_sgd call on this plan records them on its stream at its stage
- * boundaries, then forgets them (one-shot).  Forward: [0] before its first
- * kernel, [1] after its last.  Backward: [0] start, [1] after the key/payload
- * pass, [2] after the radix passes, [3] after run-length encoding, [4] after
- * the segment-reduce + SGD kernel, [5] after the long-run combine.  Events
+ * of n hipEvent_t handles (NULL entries allowed) the caller created; the NEXT
+ * call on this plan records them on its stream at its stage boundaries, then
+ * forgets them (one-shot).  Forward: [0] before its first kernel, [1] after
+ * its last.  Backward: [0] start, [1] after the key/payload pass, [2] after
+ * the radix passes, [3] after run-length encoding, [4] after the
+ * segment-reduce + SGD kernel, [5] after the long-run combine;
+ * tbe_backward_prepare records [0]-[3], tbe_backward_apply [4]-[5].  Events
  * beyond n are not recorded.  events = NULL (or n = 0) clears.  Not for plans
  * shared by concurrent calls.
  */

@@ -38,13 +38,26 @@ struct alignas(sizeof(T) * N) Pack {
     T v[N];
 };
 
+// Load through a global-address-space pointer: the pointers here come out of
+// a by-value argument struct, where the compiler would otherwise emit flat
+// loads (which also count against the LDS counter).
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p)
+{
+#if __HIP_DEVICE_COMPILE__
+    return *(const __attribute__((address_space(1))) T*)(p);
+#else
+    return *p;   // host pass: never executed
+#endif
+}
+
 __device__ __forceinline__ int find_table(const uint32_t* __restrict__ hash_off, int T,
                                           uint32_t key)
 {
     int lo = 0, hi = T;  // hash_off[lo] <= key < hash_off[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (hash_off[mid] <= key) lo = mid; else hi = mid;
+        if (ldg(hash_off + mid) <= key) lo = mid; else hi = mid;
     }
     return lo;
 }
@@ -59,6 +72,7 @@ struct SegArgs {
     const float* grad;
     const void* sorted_payload;   // sample ids, or (sample, weight) pairs when weighted
     const uint4* short_info;   // {key, start, len, table}
+    const uint2* short_first;  // {sample, weight bits} of each short run's first lookup
     const uint4* long_info;    // {key, start, len, first chunk}
     const uint32_t* counts;    // runs, short, long, chunks
     uint32_t chunk;
@@ -68,16 +82,24 @@ struct SegArgs {
     uint32_t short_blocks;     // blocks [0, short_blocks) take short runs
 };
 
+// w - lr*g in the accumulator type, rounded once to the storage type.
 template <typename WT, typename ACC, int VEC>
-__device__ __forceinline__ void sgd_store(WT* __restrict__ wp, const Pack<WT, VEC>& w_old,
-                                          const ACC (&acc)[VEC], float lr)
+__device__ __forceinline__ Pack<WT, VEC> sgd_row(const Pack<WT, VEC>& w_old,
+                                                 const ACC (&acc)[VEC], float lr)
 {
     Pack<WT, VEC> o;
 #pragma unroll
     for (int k = 0; k < VEC; ++k)
         o.v[k] = static_cast<WT>(static_cast<ACC>(static_cast<float>(w_old.v[k])) -
                                  static_cast<ACC>(lr) * acc[k]);
-    *reinterpret_cast<Pack<WT, VEC>*>(wp) = o;
+    return o;
+}
+
+template <typename WT, typename ACC, int VEC>
+__device__ __forceinline__ void sgd_store(WT* __restrict__ wp, const Pack<WT, VEC>& w_old,
+                                          const ACC (&acc)[VEC], float lr)
+{
+    *reinterpret_cast<Pack<WT, VEC>*>(wp) = sgd_row<WT, ACC, VEC>(w_old, acc, lr);
 }
 
 // Sum, for S runs held by one worker (L lanes), of w_i * grad[sample_i, col..]
@@ -85,10 +107,14 @@ __device__ __forceinline__ void sgd_store(WT* __restrict__ wp, const Pack<WT, VE
 // lanes load L sample ids (and per-sample weights) at once, then U gradient
 // rows are kept in flight at a time, across run boundaries.  pos0/len give
 // each run's first sorted position and length; gcol its gradient column base.
-template <typename ACC, int VEC, int S, int U, bool WEIGHTED>
+//
+// INLINE: the first contribution of each run comes in (fsmp, fw) from the run
+// record, so a batch of one-lookup runs needs no payload load at all.
+template <typename ACC, int VEC, int S, int U, bool WEIGHTED, bool INLINE>
 __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0)[S],
                                          const uint32_t (&len)[S],
                                          const float* const (&gcol)[S], const bool (&tw)[S],
+                                         const uint32_t (&fsmp)[S], const float (&fw)[S],
                                          int sub, int L, int gbase, ACC (&acc)[S][VEC])
 {
     uint32_t pre[S + 1];
@@ -101,28 +127,48 @@ __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0
         const uint32_t ci = cb + sub;
         uint32_t my_smp = 0;
         float my_w = 1.f;
-        if (ci < C) {
-            int sl = 0;
+        int sl = 0;
 #pragma unroll
-            for (int u = 1; u < S; ++u) sl += ci >= pre[u] ? 1 : 0;
-            uint32_t p = 0;
-            bool w_on = false;
+        for (int u = 1; u < S; ++u) sl += ci >= pre[u] ? 1 : 0;
+        uint32_t p = pos0[0], first_smp = 0;
+        float first_w = 1.f;
+        bool w_on = false, is_first = false;
 #pragma unroll
-            for (int u = 0; u < S; ++u)
-                if (u == sl) { p = pos0[u] + (ci - pre[u]); w_on = tw[u]; }
+        for (int u = 0; u < S; ++u)
+            if (u == sl) {
+                p = pos0[u] + (ci - pre[u]);
+                w_on = tw[u];
+                is_first = ci == pre[u];
+                first_smp = fsmp[u];
+                first_w = fw[u];
+            }
+        const bool need = ci < C && !(INLINE && is_first);
+        if (INLINE && ci < C && is_first) {
+            my_smp = first_smp;
+            if (w_on) my_w = first_w;
+        }
+        if (__ballot(need)) {   // one load per lane, unconditional within the wave
+            const uint32_t pp = need ? p : pos0[0];
             if (WEIGHTED) {
-                const uint2 pv = static_cast<const uint2*>(c.sorted_payload)[p];
-                my_smp = pv.x;
-                if (w_on) my_w = __uint_as_float(pv.y);
+                const uint2 pv = ldg(static_cast<const uint2*>(c.sorted_payload) + pp);
+                if (need) {
+                    my_smp = pv.x;
+                    if (w_on) my_w = __uint_as_float(pv.y);
+                }
             } else {
-                my_smp = static_cast<const uint32_t*>(c.sorted_payload)[p];
+                const uint32_t sv = ldg(static_cast<const uint32_t*>(c.sorted_payload) + pp);
+                if (need) my_smp = sv;
             }
         }
         const uint32_t n = min(static_cast<uint32_t>(L), C - cb);
         for (uint32_t j0 = 0; j0 < n; j0 += U) {
+            // all U row loads are issued unconditionally (an idle slot reads
+            // the first gradient row and is masked afterwards), so they are
+            // in flight together
             Pack<float, VEC> g[U];
             float w[U];
             int sl[U];
+            bool on[U];
 #pragma unroll
             for (int q = 0; q < U; ++q) {
                 const uint32_t j = j0 + q;
@@ -134,20 +180,15 @@ __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0
                 const float* base = gcol[0];
 #pragma unroll
                 for (int u = 1; u < S; ++u) base = (sl[q] == u) ? gcol[u] : base;
-                if (j < n && base) {
-                    g[q] = *reinterpret_cast<const Pack<float, VEC>*>(
-                        base + static_cast<int64_t>(smp) * c.sumD);
-                } else {
-                    w[q] = 0.f;
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) g[q].v[k] = 0.f;
-                }
+                on[q] = j < n && base != nullptr;
+                const float* src = on[q] ? base + static_cast<int64_t>(smp) * c.sumD : c.grad;
+                g[q] = ldg(reinterpret_cast<const Pack<float, VEC>*>(src));
             }
 #pragma unroll
             for (int q = 0; q < U; ++q)
 #pragma unroll
                 for (int u = 0; u < S; ++u)
-                    if (sl[q] == u)
+                    if (on[q] && sl[q] == u)
 #pragma unroll
                         for (int k = 0; k < VEC; ++k) {
                             if (WEIGHTED)   // w*g is exact in fp64; explicit fma in fp32
@@ -162,11 +203,28 @@ __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0
 
 // One batch of S short runs per worker: prefetch the S weight rows, sum the
 // runs' contributions, apply SGD.
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED>
-__device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ weights,
-                                            const TableDesc* __restrict__ descs,
-                                            const uint4 (&info)[S], int sub, int L, int gbase)
+// Table descriptor t: from the LDS copy when the block staged one, else from
+// global memory.
+template <bool LDSD>
+__device__ __forceinline__ TableDesc table_desc(const SegArgs& c, const TableDesc* sdesc, int t)
 {
+    if (LDSD) return sdesc[t];
+    return ldg(c.tables + t);
+}
+
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD>
+__device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ weights,
+                                            const TableDesc* sdesc,
+                                            const uint4 (&info)[S], const uint2 (&first)[S],
+                                            int sub, int L, int gbase)
+{
+    uint32_t fsmp[S];
+    float fw[S];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+        fsmp[u] = first[u].x;
+        fw[u] = __uint_as_float(first[u].y);
+    }
     for (int c0 = 0; c0 < c.max_D; c0 += VEC * L) {
         const int col = c0 + sub * VEC;
         Pack<WT, VEC> w_old[S];
@@ -177,7 +235,7 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
         uint32_t len[S], pos0[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const TableDesc& d = descs[info[u].w];
+            const TableDesc d = table_desc<LDSD>(c, sdesc, static_cast<int>(info[u].w));
             // a run whose table is narrower than this column slab contributes
             // nothing here (its lanes keep the loop shape but load no rows)
             const bool act = info[u].z > 0 && col < d.D;
@@ -186,14 +244,21 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
             wrow[u] = weights + d.w_off + static_cast<int64_t>(info[u].x - d.hash_off) * d.D + col;
             gcol[u] = act ? c.grad + d.out_off + col : nullptr;
             tw[u] = WEIGHTED && (d.flags & TD_WEIGHTED);
-            if (act) w_old[u] = *reinterpret_cast<const Pack<WT, VEC>*>(wrow[u]);
+            // unconditional (an idle slot reads the first row of the weights)
+            w_old[u] = ldg(reinterpret_cast<const Pack<WT, VEC>*>(act ? wrow[u] : weights));
 #pragma unroll
             for (int q = 0; q < VEC; ++q) acc[u][q] = ACC(0);
         }
-        flat_sum<ACC, VEC, S, U, WEIGHTED>(c, pos0, len, gcol, tw, sub, L, gbase, acc);
+        flat_sum<ACC, VEC, S, U, WEIGHTED, true>(c, pos0, len, gcol, tw, fsmp, fw, sub, L, gbase,
+                                                 acc);
+        // all S updates first, then the stores (a wait for one row's old
+        // value never includes another row's store)
+        Pack<WT, VEC> o[S];
+#pragma unroll
+        for (int u = 0; u < S; ++u) o[u] = sgd_row<WT, ACC, VEC>(w_old[u], acc[u], c.lr);
 #pragma unroll
         for (int u = 0; u < S; ++u)
-            if (gcol[u]) sgd_store<WT, ACC, VEC>(wrow[u], w_old[u], acc[u], c.lr);
+            if (gcol[u]) *reinterpret_cast<Pack<WT, VEC>*>(wrow[u]) = o[u];
     }
 }
 
@@ -206,10 +271,9 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
 // tau is raised) and fp16 tables use the ACC type.
 constexpr uint32_t kF32Run = 256;
 
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED>
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD>
 __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ weights,
-                                           const TableDesc* __restrict__ descs,
-                                           uint32_t wave, uint32_t nwaves)
+                                           const TableDesc* sdesc, uint32_t wave, uint32_t nwaves)
 {
     const int lane = threadIdx.x & 63;
     const int g_log2 = 6 - c.lpr_log2;
@@ -218,17 +282,28 @@ __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ we
     const int grp = lane >> c.lpr_log2;
     const int sub = lane & (L - 1);
     const int gbase = grp << c.lpr_log2;
-    const uint32_t nshort = c.counts[1];
+    const uint32_t nshort = ldg(c.counts + 1);
     const uint32_t per = static_cast<uint32_t>(G * S);
+    const uint32_t kend = nshort;
     uint32_t k0 = wave * per;
     uint4 nxt = make_uint4(0, 0, 0, 0);
-    if (lane < static_cast<int>(per) && k0 + lane < nshort) nxt = c.short_info[k0 + lane];
-    for (; k0 < nshort; k0 += nwaves * per) {
+    uint2 nxtf = make_uint2(0, 0);
+    if (lane < static_cast<int>(per) && k0 + lane < kend) {
+        nxt = ldg(c.short_info + k0 + lane);
+        nxtf = ldg(c.short_first + k0 + lane);
+    }
+    for (; k0 < kend; k0 += nwaves * per) {
         const uint4 mine = nxt;
+        const uint2 minef = nxtf;
         const uint32_t k1 = k0 + nwaves * per;
         nxt = make_uint4(0, 0, 0, 0);
-        if (lane < static_cast<int>(per) && k1 + lane < nshort) nxt = c.short_info[k1 + lane];
+        nxtf = make_uint2(0, 0);
+        if (lane < static_cast<int>(per) && k1 + lane < kend) {
+            nxt = ldg(c.short_info + k1 + lane);
+            nxtf = ldg(c.short_first + k1 + lane);
+        }
         uint4 info[S];
+        uint2 first[S];
         uint32_t maxlen = 0;
 #pragma unroll
         for (int u = 0; u < S; ++u) {
@@ -237,12 +312,16 @@ __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ we
             info[u].y = __shfl(mine.y, src);
             info[u].z = __shfl(mine.z, src);
             info[u].w = __shfl(mine.w, src);
+            first[u].x = __shfl(minef.x, src);
+            first[u].y = __shfl(minef.y, src);
             maxlen = max(maxlen, info[u].z);
         }
         if (sizeof(ACC) == 8 && maxlen < kF32Run)
-            short_batch<WT, float, VEC, S, U, WEIGHTED>(c, weights, descs, info, sub, L, gbase);
+            short_batch<WT, float, VEC, S, U, WEIGHTED, LDSD>(c, weights, sdesc, info, first, sub,
+                                                              L, gbase);
         else
-            short_batch<WT, ACC, VEC, S, U, WEIGHTED>(c, weights, descs, info, sub, L, gbase);
+            short_batch<WT, ACC, VEC, S, U, WEIGHTED, LDSD>(c, weights, sdesc, info, first, sub, L,
+                                                            gbase);
     }
 }
 
@@ -256,18 +335,18 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
     const int g_log2 = 6 - c.lpr_log2;
     const int grp = lane >> c.lpr_log2;
     const int sub = lane & ((1 << c.lpr_log2) - 1);
-    const uint32_t nlong = min(c.counts[2], c.max_long);
-    const uint32_t nchunks = min(c.counts[3], c.max_chunks);
+    const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
+    const uint32_t nchunks = min(ldg(c.counts + 3), c.max_chunks);
     for (uint32_t q0 = wave << g_log2; q0 < nchunks; q0 += nwaves << g_log2) {
         const uint32_t q = q0 + grp;
         if (q >= nchunks) continue;
         uint32_t lo = 0, hi = nlong;  // long run owning chunk q: last with first chunk <= q
         while (hi - lo > 1) {
             const uint32_t mid = (lo + hi) >> 1;
-            if (c.long_info[mid].w <= q) lo = mid; else hi = mid;
+            if (ldg(c.long_info + mid).w <= q) lo = mid; else hi = mid;
         }
-        const uint4 li = c.long_info[lo];
-        const TableDesc d = c.tables[find_table(c.hash_off, c.T, li.x)];
+        const uint4 li = ldg(c.long_info + lo);
+        const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
         const bool tw = WEIGHTED && (d.flags & TD_WEIGHTED);
         const uint32_t i0 = li.y + (q - li.w) * c.chunk;
         const uint32_t i1 = min(li.y + li.z, i0 + c.chunk);
@@ -281,8 +360,10 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
             ACC acc[1][VEC];
 #pragma unroll
             for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
-            flat_sum<ACC, VEC, 1, 4, WEIGHTED>(c, p0, ln, gc, twa, sub, 1 << c.lpr_log2,
-                                               grp << c.lpr_log2, acc);
+            const uint32_t nof[1] = {0};
+            const float now[1] = {1.f};
+            flat_sum<ACC, VEC, 1, 4, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, sub,
+                                                      1 << c.lpr_log2, grp << c.lpr_log2, acc);
             if (col < d.D) {
                 Pack<ACC, VEC> o;
 #pragma unroll
@@ -304,39 +385,37 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
     const int g_log2 = 6 - c.lpr_log2;
     const int grp = lane >> c.lpr_log2;
     const int sub = lane & ((1 << c.lpr_log2) - 1);
-    const uint32_t nlong = min(c.counts[2], c.max_long);
+    const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
     const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
     for (uint32_t k0 = wave << g_log2; k0 < nlong; k0 += nwaves << g_log2) {
         const uint32_t k = k0 + grp;
         if (k >= nlong) continue;
-        const uint4 li = c.long_info[k];
-        const TableDesc d = c.tables[find_table(c.hash_off, c.T, li.x)];
+        const uint4 li = ldg(c.long_info + k);
+        const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
         WT* __restrict__ wrow = weights + d.w_off + static_cast<int64_t>(li.x - d.hash_off) * d.D;
         const uint32_t nq = (li.z + c.chunk - 1) / c.chunk;
         const uint32_t qend = min(li.w + nq, c.max_chunks);
         for (int c0 = 0; c0 < d.D; c0 += (VEC << c.lpr_log2)) {
             const int col = c0 + sub * VEC;
             if (col >= d.D) continue;
-            const Pack<WT, VEC> w_old = *reinterpret_cast<const Pack<WT, VEC>*>(wrow + col);
+            const Pack<WT, VEC> w_old = ldg(reinterpret_cast<const Pack<WT, VEC>*>(wrow + col));
             ACC acc[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) acc[j] = ACC(0);
             for (uint32_t qq = li.w; qq < qend; qq += 8) {
                 Pack<ACC, VEC> part[8];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    if (qq + m < qend)
-                        part[m] = *reinterpret_cast<const Pack<ACC, VEC>*>(
-                            partials + static_cast<int64_t>(qq + m) * c.max_D + col);
-                    else
-#pragma unroll
-                        for (int j = 0; j < VEC; ++j) part[m].v[j] = ACC(0);
+                for (int m = 0; m < 8; ++m) {   // unconditional: past the end re-reads the last
+                    const uint32_t qm = qq + m < qend ? qq + m : qend - 1;
+                    part[m] = ldg(reinterpret_cast<const Pack<ACC, VEC>*>(
+                        partials + static_cast<int64_t>(qm) * c.max_D + col));
                 }
 #pragma unroll
                 for (int m = 0; m < 8; ++m)
+                    if (qq + m < qend)
 #pragma unroll
-                    for (int j = 0; j < VEC; ++j) acc[j] += part[m].v[j];
+                        for (int j = 0; j < VEC; ++j) acc[j] += part[m].v[j];
             }
             sgd_store<WT, ACC, VEC>(wrow + col, w_old, acc, c.lr);
         }
@@ -352,14 +431,15 @@ __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ wei
     __shared__ TableDesc sdesc[kLdsTables];
     const uint32_t wib = threadIdx.x >> 6;
     if (blockIdx.x < c.short_blocks) {
-        const TableDesc* descs = c.tables;
+        const uint32_t wave = blockIdx.x * 4 + wib;
+        const uint32_t nwaves = c.short_blocks * 4;
         if (c.T <= kLdsTables) {
-            for (int i = threadIdx.x; i < c.T; i += 256) sdesc[i] = c.tables[i];
+            for (int i = threadIdx.x; i < c.T; i += 256) sdesc[i] = ldg(c.tables + i);
             __syncthreads();
-            descs = sdesc;
+            short_runs<WT, ACC, VEC, S, U, WEIGHTED, true>(c, weights, sdesc, wave, nwaves);
+        } else {
+            short_runs<WT, ACC, VEC, S, U, WEIGHTED, false>(c, weights, sdesc, wave, nwaves);
         }
-        short_runs<WT, ACC, VEC, S, U, WEIGHTED>(c, weights, descs, blockIdx.x * 4 + wib,
-                                                 c.short_blocks * 4);
     }
     else
         long_chunks<ACC, VEC, WEIGHTED>(c, partials, (blockIdx.x - c.short_blocks) * 4 + wib,
@@ -377,7 +457,7 @@ uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
 template <typename WT, typename ACC, int VEC, int S, int U>
 void launch_seg(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
 {
-    if (a.psw)
+    if (a.payload_pairs)
         hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true>), grid, dim3(256), 0, a.stream, c,
                            w, partials);
     else
@@ -398,7 +478,7 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     const uint32_t b_long = blocks_for(L.max_long, int64_t(4) * G, 256);
     const dim3 grid(c.short_blocks + b_chunk);
     // short-run batches: S = 2 runs per worker, U = 4 gradient rows in flight
-    // (measured best of S in {1,2,4} x U in {4,8} on the uniform, stress and
+    // (measured best of S in {1,2,4,8} x U in {4,8} on the uniform, stress and
     // mixed workloads)
     launch_seg<WT, ACC, VEC, 2, 4>(a, grid, c, w, partials);
     stage_mark(a.plan, 4, a.stream);
@@ -436,6 +516,7 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.grad = a.grad;
     c.sorted_payload = ws + L.off_vals[a.final_buf];
     c.short_info = reinterpret_cast<const uint4*>(ws + L.off_short_info);
+    c.short_first = reinterpret_cast<const uint2*>(ws + L.off_short_first);
     c.long_info = reinterpret_cast<const uint4*>(ws + L.off_long_info);
     c.counts = reinterpret_cast<const uint32_t*>(ws + L.off_ctl) + kCtlCounts;
     c.chunk = static_cast<uint32_t>(p->tuning.chunk);

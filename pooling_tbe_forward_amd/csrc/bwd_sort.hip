@@ -40,19 +40,22 @@ namespace tbe {
 
 namespace {
 constexpr int kRadix = 256;
-constexpr int kSortWaves = 4;
-constexpr int kRleItems = 4;
-constexpr int kRleTile = 256 * kRleItems;
+constexpr int kSortThreads = 1024;   // 16 waves per radix tile
+constexpr int kRleThreads = 1024;
+constexpr int kRleItems = 8;         // sorted positions per thread (two 16-byte loads)
+constexpr int kRleTile = kRleThreads * kRleItems;
+constexpr int kRleMaxT = 2048;       // hash offsets staged in LDS up to this many tables
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagInc = 2u << 30;
 constexpr uint32_t kValMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 24;
 constexpr int kPrepMaxBags = 2048;   // bags per k_prep block (LDS offsets cache)
 constexpr int kPrepKeys = 1024;      // target keys per k_prep block
+constexpr int kPrepThreads = 1024;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int sort_rounds(int64_t N) { return N > (int64_t(1) << 21) ? 16 : 8; }
+constexpr int kSortRounds = 8;       // keys per thread in a radix tile
 }  // namespace
 
 BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
@@ -69,7 +72,7 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
         L.digit_bits[i] = per < left ? per : left;
         left -= L.digit_bits[i];
     }
-    L.sort_tile = 64 * kSortWaves * sort_rounds(N);
+    L.sort_tile = kSortThreads * kSortRounds;
     L.sort_blocks = static_cast<int32_t>((N + L.sort_tile - 1) / L.sort_tile);
     L.rle_tile = kRleTile;
     L.rle_blocks = static_cast<int32_t>((N + kRleTile - 1) / kRleTile);
@@ -109,6 +112,7 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_short = take(n4);
     L.off_long = take(n4);
     L.off_short_info = take(size_t(N + 1) * 16);
+    L.off_short_first = take(size_t(N + 1) * 8);
     L.off_long_info = take(size_t(ml + 1) * 16);
     const size_t acc = p->wdtype == TBE_F32 ? 8 : 4;
     L.off_partials = take(size_t(mc > 0 ? mc : 1) * p->max_D * acc);
@@ -158,15 +162,17 @@ __device__ __forceinline__ uint32_t lookback(uint32_t* st, uint32_t stride, uint
         st_rel(st, kFlagInc | value);
         return 0;
     }
-    st_rel(st + static_cast<size_t>(tile) * stride, kFlagAgg | value);
     uint32_t excl = 0;
     int64_t tp = static_cast<int64_t>(tile) - 1;
     uint32_t spins = 0;
-    while (true) {
-        uint32_t s[W];
+    uint32_t s[W];
+    // the first window is read before this tile's aggregate is published: a
+    // wait for the loads then does not include the store
 #pragma unroll
-        for (int i = 0; i < W; ++i)
-            s[i] = (tp - i >= 0) ? ld_acq(st + static_cast<size_t>(tp - i) * stride) : kFlagInc;
+    for (int i = 0; i < W; ++i)
+        s[i] = (tp - i >= 0) ? ld_acq(st + static_cast<size_t>(tp - i) * stride) : kFlagInc;
+    st_rel(st + static_cast<size_t>(tile) * stride, kFlagAgg | value);
+    while (true) {
         uint32_t consumed = 0;
         bool stop = false, done = false;
 #pragma unroll
@@ -191,6 +197,9 @@ __device__ __forceinline__ uint32_t lookback(uint32_t* st, uint32_t stride, uint
             }
             __builtin_amdgcn_s_sleep(1);
         }
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            s[i] = (tp - i >= 0) ? ld_acq(st + static_cast<size_t>(tp - i) * stride) : kFlagInc;
     }
     st_rel(st + static_cast<size_t>(tile) * stride, kFlagInc | ((excl + value) & kValMask));
     return excl;
@@ -218,21 +227,6 @@ struct PassBits {
     uint32_t mask[4];
 };
 
-// Add 1 per active lane to hist[d]: lanes with equal digits are found with
-// nbits ballots and the lowest of them adds their count, so a hot digit (Zipf
-// keys) costs one LDS atomic per wavefront instead of one per lane.
-__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t d, bool ok, int nbits,
-                                              uint64_t lt)
-{
-    uint64_t peers = __ballot(ok);
-    for (int bit = 0; bit < nbits; ++bit) {
-        const bool on = (d >> bit) & 1u;
-        const uint64_t bal = __ballot(on);
-        peers &= on ? bal : ~bal;
-    }
-    if (ok && (peers & lt) == 0) atomicAdd(&hist[d], static_cast<uint32_t>(__popcll(peers)));
-}
-
 // Payload carried through the sort next to each key.
 enum PayloadMode : int {
     kPayloadPos = 0,      // lookup position j (the sort_rle entry point)
@@ -240,8 +234,12 @@ enum PayloadMode : int {
     kPayloadSampleW = 2,  // (b, per-sample weight bits) pair
 };
 
+// One block per run of whole bags (about kPrepKeys lookups), one lookup per
+// thread per step: the bag of a lookup comes from a branchless binary search
+// over the block's bag starts in LDS, so the searches of a thread's lookups
+// interleave.
 template <typename IT, int MODE>
-__global__ __launch_bounds__(256) void k_prep(
+__global__ __launch_bounds__(kPrepThreads) void k_prep(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
     const IT* __restrict__ indices, const IT* __restrict__ offsets,
     const float* __restrict__ psw, uint32_t* __restrict__ keys, void* __restrict__ vals,
@@ -249,112 +247,154 @@ __global__ __launch_bounds__(256) void k_prep(
     size_t status_words)
 {
     __shared__ uint32_t hist[4][kRadix];
-    __shared__ int64_t boff[kPrepMaxBags + 1];
+    __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
     __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (size_t i = blockIdx.x * 256ull + tid; i < status_words; i += gridDim.x * 256ull)
-        status[i] = 0u;
-    for (int i = tid; i < 4 * kRadix; i += 256) (&hist[0][0])[i] = 0u;
+    (&hist[0][0])[tid] = 0u;
+    static_assert(4 * kRadix == kPrepThreads, "one histogram word per thread");
     const uint32_t g0 = blockIdx.x * bags_per_block;
     const uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
     const uint32_t t_first = nb ? g0 / B : 0;
     const uint32_t t_count = nb ? (g0 + nb - 1) / B - t_first + 1 : 0;   // <= nb
-    for (uint32_t i = tid; i <= nb && nb > 0; i += 256) boff[i] = static_cast<int64_t>(offsets[g0 + i]);
-    for (uint32_t i = tid; i < t_count; i += 256) hoff[i] = tables[t_first + i].hash_off;
+    const int64_t P0 = nb ? static_cast<int64_t>(offsets[g0]) : 0;
+    for (uint32_t i = tid; i <= nb && nb > 0; i += kPrepThreads)
+        boff[i] = static_cast<uint32_t>(static_cast<int64_t>(offsets[g0 + i]) - P0);
+    for (uint32_t i = tid; i < t_count; i += kPrepThreads) hoff[i] = tables[t_first + i].hash_off;
     __syncthreads();
-    const int64_t P0 = nb ? boff[0] : 0, P1 = nb ? boff[nb] : 0;
+    const uint32_t len = nb ? boff[nb] : 0u;
+    uint32_t top = 1;
+    while (top < nb) top <<= 1;
     constexpr int UN = 8;
-    for (int64_t base = P0; base < P1; base += 256 * UN) {
+    for (uint32_t base = 0; base < len; base += kPrepThreads * UN) {
         IT id[UN];
         float wv[UN];
+        uint32_t g[UN];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
-            const int64_t p = base + u * 256 + tid;
-            id[u] = p < P1 ? indices[p] : IT(0);
-            wv[u] = (MODE == kPayloadSampleW && p < P1) ? psw[p] : 0.f;
+            const uint32_t rp = base + u * kPrepThreads + tid;
+            id[u] = rp < len ? indices[P0 + rp] : IT(0);
+            wv[u] = (MODE == kPayloadSampleW && rp < len) ? psw[P0 + rp] : 0.f;
+            g[u] = 0;
+        }
+        // g[u]: the last bag whose start is <= rp (that bag is not empty);
+        // branch-free, so the searches of the used slots interleave
+        const uint32_t nu = (len - base + kPrepThreads - 1) / kPrepThreads;   // slots in use
+        for (uint32_t st = top; st > 0; st >>= 1) {
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                if (u < nu) {
+                    const uint32_t rp = base + u * kPrepThreads + tid;
+                    const uint32_t c = g[u] + st;
+                    const uint32_t v = boff[c < nb ? c : nb - 1];
+                    g[u] = (c < nb && v <= rp) ? c : g[u];
+                }
+            }
+        }
+        // keys and payloads first, histograms next, stores last: a store's
+        // registers are not reused before the loop ends, so no wait on it
+        uint32_t key[UN], pay[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const uint32_t gg = g0 + g[u];
+            const uint32_t t = gg / B;
+            key[u] = hoff[t - t_first] + static_cast<uint32_t>(id[u]);
+            pay[u] = gg - t * B;
+            if (MODE == kPayloadPos) pay[u] = static_cast<uint32_t>(P0 + base + u * kPrepThreads + tid);
+        }
+        // digit counts: one LDS add per lookup and pass (the order of the
+        // adds does not matter)
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const bool ok = base + u * kPrepThreads + tid < len;
+            if (ok)
+                for (int q = 0; q < pb.npasses; ++q)
+                    atomicAdd(&hist[q][(key[u] >> pb.shift[q]) & pb.mask[q]], 1u);
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
-            const int64_t p = base + u * 256 + tid;
-            const bool ok = p < P1;
-            uint32_t key = 0;
-            if (ok) {
-                uint32_t lo = 0, hi = nb;  // boff[lo] <= p < boff[hi]
-                while (hi - lo > 1) {
-                    const uint32_t mid = (lo + hi) >> 1;
-                    if (boff[mid] <= p) lo = mid; else hi = mid;
-                }
-                const uint32_t g = g0 + lo;
-                const uint32_t t = g / B;
-                key = hoff[t - t_first] + static_cast<uint32_t>(id[u]);
-                keys[p] = key;
-                const uint32_t b = g - t * B;
-                if (MODE == kPayloadPos)
-                    static_cast<uint32_t*>(vals)[p] = static_cast<uint32_t>(p);
-                else if (MODE == kPayloadSample)
-                    static_cast<uint32_t*>(vals)[p] = b;
+            const uint32_t rp = base + u * kPrepThreads + tid;
+            if (rp < len) {
+                const int64_t p = P0 + rp;
+                keys[p] = key[u];
+                if (MODE == kPayloadSampleW)
+                    static_cast<uint2*>(vals)[p] = make_uint2(pay[u], __float_as_uint(wv[u]));
                 else
-                    static_cast<uint2*>(vals)[p] = make_uint2(b, __float_as_uint(wv[u]));
+                    static_cast<uint32_t*>(vals)[p] = pay[u];
             }
-            for (int q = 0; q < pb.npasses; ++q)
-                wave_hist_add(hist[q], (key >> pb.shift[q]) & pb.mask[q], ok, pb.bits[q], lt);
         }
     }
     __syncthreads();
     // digit totals are spread over kTotCopies copies (fewer adds per address)
-    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadix);
-    for (int q = 0; q < pb.npasses; ++q) {
-        const uint32_t c = hist[q][tid];
-        if (c) atomicAdd(&tcopy[q * kRadix + tid], c);
+    {
+        uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadix);
+        const int q = tid >> 8;
+        const uint32_t c = hist[q][tid & (kRadix - 1)];
+        if (q < pb.npasses && c) atomicAdd(&tcopy[tid], c);
     }
+    // the look-back words of the radix passes and the run-length encode
+    for (size_t i = blockIdx.x * size_t(kPrepThreads) + tid; i < status_words;
+         i += size_t(gridDim.x) * kPrepThreads)
+        status[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
+// One radix pass.  A tile is kSortThreads x R keys; wave w ranks rounds of 64
+// keys with ballots (equal digits of a round are found bit by bit) and its own
+// LDS digit counters, so the rank is stable inside the tile.  The ticket and
+// the digit-totals loads are issued together, so they cost one round trip.
 template <int R, typename PT>
-__global__ __launch_bounds__(256) void k_onesweep(
+__global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const PT* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, PT* __restrict__ vals_out, uint32_t N, int shift,
     int nbits, const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ err, uint32_t ntiles,
     uint32_t* __restrict__ prev_totals)
 {
-    __shared__ uint32_t wcnt[kSortWaves][kRadix];
+    constexpr int NW = kSortThreads / 64;
+    __shared__ uint32_t wcnt[NW][kRadix];
+    __shared__ uint32_t part[4][kRadix];
     __shared__ uint32_t gofs[kRadix];
-    __shared__ uint32_t wsum[kSortWaves];
+    __shared__ uint32_t lbase[kRadix];
+    __shared__ uint32_t delta[kRadix];
+    __shared__ uint32_t wsum[4];
     __shared__ uint32_t s_tile;
+    __shared__ uint32_t sk[kSortThreads * R];
+    __shared__ PT sv[kSortThreads * R];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    if (tid == 0) s_tile = take_ticket(ticket, ntiles);
-    for (int i = tid; i < kSortWaves * kRadix; i += 256) (&wcnt[0][0])[i] = 0u;
-    // exclusive scan of the global digit totals: first position of each digit
-    {
-        uint32_t v = 0;
+    // the ticket is taken by a wave that loads no totals, so the two overlap
+    if (tid == kRadix) s_tile = take_ticket(ticket, ntiles);
+    uint32_t tot = 0;
+    if (tid < kRadix) {
 #pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) v += totals[cp * 4 * kRadix + tid];
-        const uint32_t inc = wave_incl_scan(v, lane);
+        for (int cp = 0; cp < kTotCopies; ++cp) tot += totals[cp * 4 * kRadix + tid];
+    }
+    // the previous pass's digit totals are no longer needed: leave them zero
+    if (blockIdx.x == 0 && prev_totals && tid < kRadix)
+#pragma unroll
+        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
+    for (int i = tid; i < NW * kRadix; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
+    uint32_t inc = 0;
+    if (tid < kRadix) {
+        inc = wave_incl_scan(tot, lane);
         if (lane == 63) wsum[wave] = inc;
-        __syncthreads();
-        uint32_t pre = 0;
-        for (int w = 0; w < wave; ++w) pre += wsum[w];
-        gofs[tid] = pre + inc - v;
     }
     __syncthreads();
+    if (tid < kRadix) {
+        uint32_t pre = 0;
+        for (int w = 0; w < wave; ++w) pre += wsum[w];
+        gofs[tid] = pre + inc - tot;   // first output position of digit tid
+    }
     const uint32_t tile = s_tile;
     if (tile >= ntiles) {          // only with an uninitialised control block
         if (tid == 0) atomicOr(err, 2u);
         return;
     }
-    // the previous pass's digit totals are no longer needed: leave them zero
-    if (tile == 0 && prev_totals)
-#pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
 
     const uint32_t mask = (1u << nbits) - 1u;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const uint32_t wbase = tile * (256u * R) + static_cast<uint32_t>(wave) * (64u * R);
+    const uint32_t wbase = tile * (uint32_t(kSortThreads) * R) + static_cast<uint32_t>(wave) * (64u * R);
     uint32_t k[R], dg[R], rk[R];
     PT v[R];
 #pragma unroll
@@ -369,8 +409,10 @@ __global__ __launch_bounds__(256) void k_onesweep(
         const uint32_t i = wbase + r * 64u + lane;
         const bool ok = i < N;
         const uint32_t d = (k[r] >> shift) & mask;
+        // digits have at most 8 bits; bits above nbits are zero in every lane
         uint64_t peers = __ballot(ok);
-        for (int bit = 0; bit < nbits; ++bit) {
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
             const bool on = (d >> bit) & 1u;
             const uint64_t bal = __ballot(on);
             peers &= on ? bal : ~bal;
@@ -383,51 +425,125 @@ __global__ __launch_bounds__(256) void k_onesweep(
         rk[r] = base + below;
     }
     __syncthreads();
+    // per digit: exclusive prefix over the waves (four groups of NW/4 waves),
+    // the tile's digit total, and its exclusive prefix over digits (lbase)
+    const int d = tid & (kRadix - 1), q = tid >> 8;
+    uint32_t all = 0, dinc = 0;
     {
-        const int d = tid;
+        constexpr int G = NW / 4;
         uint32_t run = 0;
 #pragma unroll
-        for (int w = 0; w < kSortWaves; ++w) {
-            const uint32_t c = wcnt[w][d];
-            wcnt[w][d] = run;
+        for (int j = 0; j < G; ++j) {
+            const uint32_t c = wcnt[q * G + j][d];
+            wcnt[q * G + j][d] = run;
             run += c;
         }
-        const uint32_t excl = lookback<16>(status + d, kRadix, tile, run, err);
-        gofs[d] += excl;
+        part[q][d] = run;
+        __syncthreads();
+        uint32_t pre = 0;
+        for (int j = 0; j < q; ++j) pre += part[j][d];
+        if (q > 0)
+#pragma unroll
+            for (int j = 0; j < G; ++j) wcnt[q * G + j][d] += pre;
+        if (q == 0) {
+            all = part[0][d] + part[1][d] + part[2][d] + part[3][d];
+            dinc = wave_incl_scan(all, lane);
+            if (lane == 63) wsum[wave] = dinc;
+        }
     }
     __syncthreads();
+    uint32_t lb = 0;
+    if (q == 0) {
+        for (int w = 0; w < wave; ++w) lb += wsum[w];
+        lb += dinc - all;
+        lbase[d] = lb;
+    }
+    __syncthreads();
+    // stage the tile in LDS in output order; meanwhile waves 0-3 look back
+    // for the tile's global digit offsets
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = wbase + r * 64u + lane;
         if (i < N) {
-            const uint32_t pos = gofs[dg[r]] + wcnt[wave][dg[r]] + rk[r];
+            const uint32_t lp = lbase[dg[r]] + wcnt[wave][dg[r]] + rk[r];
+            sk[lp] = k[r];
+            sv[lp] = v[r];
+        }
+    }
+    if (q == 0) delta[d] = gofs[d] + lookback<16>(status + d, kRadix, tile, all, err) - lb;
+    __syncthreads();
+    // write out: consecutive threads store consecutive positions of a digit
+    const uint32_t t0 = tile * (uint32_t(kSortThreads) * R);
+    const uint32_t cnt = (N - t0) < uint32_t(kSortThreads * R) ? N - t0 : uint32_t(kSortThreads * R);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t e = r * kSortThreads + tid;
+        if (e < cnt) {
+            const uint32_t key = sk[e];
+            const uint32_t pos = delta[(key >> shift) & mask] + e;
             if (pos >= N) continue;  // unreachable when the counts are consistent
-            keys_out[pos] = k[r];
-            vals_out[pos] = v[r];
+            keys_out[pos] = key;
+            vals_out[pos] = sv[e];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Length of the run whose head is at i: galloping then binary search.
-__device__ __forceinline__ uint32_t run_length(const uint32_t* __restrict__ keys, uint32_t N,
-                                               uint32_t i, uint32_t key)
+// Exclusive prefix over tiles 0..tile-1, computed by one whole wavefront: lane l
+// reads the word of tile tp-l, so one memory round trip crosses up to 64
+// published tiles.  Same flags and publication order as lookback().
+__device__ __forceinline__ uint32_t lookback_wave(uint32_t* st, uint32_t tile, uint32_t value,
+                                                  uint32_t* err, int lane)
 {
-    uint32_t lo = i, step = 1;
-    while (lo + step < N && keys[lo + step] == key) {
-        lo += step;
-        step <<= 1;
+    if (tile == 0) {
+        if (lane == 0) st_rel(st, kFlagInc | value);
+        return 0;
     }
-    uint32_t hi = (lo + step < N) ? lo + step : N;  // keys[hi] != key or hi == N
-    while (hi - lo > 1) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (keys[mid] == key) lo = mid; else hi = mid;
+    uint32_t excl = 0;
+    int64_t tp = static_cast<int64_t>(tile) - 1;
+    uint32_t spins = 0;
+    // first window before publishing (see lookback())
+    uint32_t s = (tp - lane >= 0) ? ld_acq(st + (tp - lane)) : kFlagInc;
+    if (lane == 0) st_rel(st + tile, kFlagAgg | value);
+    while (true) {
+        const uint32_t f = s & ~kValMask;
+        const uint64_t unpub = __ballot(f == 0);
+        const uint64_t incl = __ballot(f == kFlagInc);
+        const int first_unpub = unpub ? __builtin_ctzll(unpub) : 64;
+        const int first_inc = incl ? __builtin_ctzll(incl) : 64;
+        if (first_inc < first_unpub) {
+            excl += wave_sum(lane <= first_inc ? (s & kValMask) : 0u);
+            break;
+        }
+        excl += wave_sum(lane < first_unpub ? (s & kValMask) : 0u);
+        tp -= first_unpub;
+        if (first_unpub == 0) {
+            if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(err, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        s = (tp - lane >= 0) ? ld_acq(st + (tp - lane)) : kFlagInc;
     }
-    return lo - i + 1;
+    if (lane == 0) st_rel(st + tile, kFlagInc | ((excl + value) & kValMask));
+    return excl;
 }
 
-__device__ __forceinline__ int find_table_g(const uint32_t* __restrict__ hash_off, int T,
-                                            uint32_t key)
+// In-place exclusive scan of a [kRleItems][kRleThreads / 64] table of counts
+// (round-major), by one wavefront; returns the table total on every lane.
+__device__ __forceinline__ uint32_t scan_table(uint32_t* tab, int lane)
+{
+    static_assert(kRleItems * (kRleThreads / 64) == 128, "two entries per lane");
+    const uint32_t x = tab[2 * lane], y = tab[2 * lane + 1];
+    const uint32_t inc = wave_incl_scan(x + y, lane);
+    const uint32_t ex = inc - x - y;
+    tab[2 * lane] = ex;
+    tab[2 * lane + 1] = ex + x;
+    return __shfl(inc, 63);
+}
+
+__device__ __forceinline__ int find_table(const uint32_t* hash_off, int T, uint32_t key)
 {
     int lo = 0, hi = T;  // hash_off[lo] <= key < hash_off[hi]
     while (hi - lo > 1) {
@@ -437,9 +553,49 @@ __device__ __forceinline__ int find_table_g(const uint32_t* __restrict__ hash_of
     return lo;
 }
 
-template <bool API>
-__global__ __launch_bounds__(256) void k_rle(
-    const uint32_t* __restrict__ keys, uint32_t N, uint32_t tau, uint32_t chunk, uint32_t ntiles,
+// First position >= from whose key differs from `key` (N if none), found by
+// one wavefront: 32 exponentially spaced probes, then rounds of 64 evenly
+// spaced probes inside the bracket.  Keys are sorted, so "differs" is monotone.
+__device__ __forceinline__ uint32_t run_end_wave(const uint32_t* __restrict__ keys, uint32_t N,
+                                                 uint32_t from, uint32_t key, int lane)
+{
+    if (from >= N) return N;
+    uint64_t p = from + ((lane < 32) ? ((uint64_t(1) << lane) - 1) : (uint64_t(1) << 40));
+    bool diff = p >= N || keys[p] != key;
+    uint64_t bal = __ballot(diff);   // lane 63 probes past N, so bal != 0
+    const int l = __builtin_ctzll(bal);
+    if (l == 0) return from;
+    uint64_t lo = from + ((uint64_t(1) << (l - 1)) - 1);   // same key
+    uint64_t hi = from + ((uint64_t(1) << l) - 1);         // differs or past N
+    if (hi > N) hi = N;
+    while (hi - lo > 1) {
+        const uint64_t step = (hi - lo + 63) / 64;
+        uint64_t q = lo + (lane + 1) * step;
+        if (q > hi) q = hi;
+        diff = q >= hi || keys[q] != key;   // hi itself is known to differ
+        bal = __ballot(diff);
+        const int m = __builtin_ctzll(bal);
+        const uint64_t nhi = lo + (m + 1) * step;
+        hi = nhi < hi ? nhi : hi;
+        lo = lo + m * step;
+    }
+    return static_cast<uint32_t>(hi);
+}
+
+// Run-length encode of the sorted keys.  A tile is kRleItems rounds of
+// kRleThreads consecutive positions (round q, thread i: position
+// tile*kRleTile + q*kRleThreads + i), so every store of a round is coalesced.
+// Run indices come from per-(round, wave) ballot counts scanned in position
+// order; run lengths from the next head's position (kept in LDS), except for
+// the tile's last run, which one wavefront follows past the tile's end.
+// FIRST: 0 = no payload (the sort_rle entry point), 1 = payload is the sample
+// id, 2 = payload is (sample id, per-sample weight).  With a payload, each
+// short run's first (sample, weight) is stored next to its record, so a run of
+// one lookup needs no payload load in the segment kernel.
+template <bool API, int FIRST>
+__global__ __launch_bounds__(kRleThreads) void k_rle(
+    const uint32_t* __restrict__ keys, const void* __restrict__ payload,
+    uint2* __restrict__ short_first, uint32_t N, uint32_t tau, uint32_t chunk, uint32_t ntiles,
     uint32_t* __restrict__ rstatus, uint32_t* __restrict__ ticket, uint32_t* __restrict__ err,
     const uint32_t* __restrict__ hash_off, int32_t T, uint4* __restrict__ short_info,
     uint4* __restrict__ long_info, uint32_t* __restrict__ counts,
@@ -448,79 +604,128 @@ __global__ __launch_bounds__(256) void k_rle(
     uint32_t* __restrict__ run_len, uint32_t* __restrict__ short_ids,
     uint32_t* __restrict__ long_ids)
 {
-    __shared__ uint32_t wsum[3][4];
+    constexpr int NW = kRleThreads / 64;
+    constexpr int Q = kRleItems;
+    __shared__ uint32_t hp[kRleTile + 1];        // head positions in run order
+    __shared__ uint32_t s_hash[kRleMaxT + 1];
+    __shared__ uint32_t cnt[3][Q * NW];          // heads, long runs, chunks per (round, wave)
+    __shared__ uint32_t s_tot[3];
     __shared__ uint32_t texcl[3];
-    __shared__ uint32_t s_tile;
+    __shared__ uint32_t s_tile, s_end;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (tid == 0) s_tile = take_ticket(ticket, ntiles);
+    if (blockIdx.x == 0 && prev_totals && tid < kRadix)   // the last radix pass is done with them
+#pragma unroll
+        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
+    const bool lds_hash = T <= kRleMaxT;
+    if (lds_hash)
+        for (int i = tid; i <= T; i += kRleThreads) s_hash[i] = hash_off[i];
     __syncthreads();
     const uint32_t tile = s_tile;
     if (tile >= ntiles) {          // only with an uninitialised control block
         if (tid == 0) atomicOr(err, 2u);
         return;
     }
-    if (tile == 0 && prev_totals)   // the last radix pass is done with its totals
-#pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
-    const uint32_t i0 = tile * kRleTile + tid * kRleItems;
+    const uint32_t t0 = tile * kRleTile;
+    const uint32_t tend = (N - t0) < uint32_t(kRleTile) ? N : t0 + kRleTile;
 
-    uint32_t kk[kRleItems], len[kRleItems];
-    uint32_t v[3] = {0, 0, 0};
+    uint32_t kk[Q];
+    uint2 pay[Q];
+    bool head[Q];
 #pragma unroll
-    for (int q = 0; q < kRleItems; ++q) {
-        const uint32_t i = i0 + q;
-        len[q] = 0;
-        kk[q] = 0;
-        if (i < N) {
-            kk[q] = keys[i];
-            if (i == 0 || keys[i - 1] != kk[q]) {
-                len[q] = run_length(keys, N, i, kk[q]);
-                v[0] += 1;
-                if (len[q] >= tau) {
-                    v[1] += 1;
-                    v[2] += (len[q] + chunk - 1) / chunk;
-                }
-            }
-        }
+    for (int q = 0; q < Q; ++q) {
+        const uint32_t p = t0 + q * kRleThreads + tid;
+        const bool ok = p < tend;
+        kk[q] = ok ? keys[p] : 0u;
+        pay[q] = make_uint2(0u, 0x3f800000u);   // weight 1.0 unless the payload has one
+        if (FIRST == 1 && ok) pay[q].x = static_cast<const uint32_t*>(payload)[p];
+        if (FIRST == 2 && ok) pay[q] = static_cast<const uint2*>(payload)[p];
+        const uint32_t kp = (ok && p > 0) ? keys[p - 1] : 0u;
+        head[q] = ok && (p == 0 || kk[q] != kp);
     }
-    uint32_t inc[3];
+    // the tile's last run may continue into later tiles: the wave holding the
+    // tile's last position finds where it ends (a full tile ends at round Q-1,
+    // thread kRleThreads-1)
+    if (wave == NW - 1) {
+        const uint32_t klast = __shfl(kk[Q - 1], 63);
+        const uint32_t e = tend == N ? N : run_end_wave(keys, N, tend, klast, lane);
+        if (lane == 0) s_end = e;
+    }
+    uint64_t hb[Q];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-        inc[c] = wave_incl_scan(v[c], lane);
-        if (lane == 63) wsum[c][wave] = inc[c];
+    for (int q = 0; q < Q; ++q) {
+        hb[q] = __ballot(head[q]);
+        if (lane == 0) cnt[0][q * NW + wave] = static_cast<uint32_t>(__popcll(hb[q]));
     }
     __syncthreads();
-    if (tid < 3) {
-        const uint32_t tot = wsum[tid][0] + wsum[tid][1] + wsum[tid][2] + wsum[tid][3];
-        const uint32_t ex =
-            lookback<32>(rstatus + static_cast<size_t>(tid) * ntiles, 1, tile, tot, err);
-        texcl[tid] = ex;
-        if (tile == ntiles - 1) {
-            // the last tile knows the totals
-            counts[tid == 0 ? 0 : (tid == 1 ? 2 : 3)] = ex + tot;
+    if (wave == 0) {
+        const uint32_t tot = scan_table(cnt[0], lane);
+        if (lane == 0) {
+            s_tot[0] = tot;
+            hp[tot] = s_end;
         }
     }
     __syncthreads();
-    uint32_t base[3];
+    uint32_t lh[Q];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-        uint32_t pre = texcl[c];
-        for (int w = 0; w < wave; ++w) pre += wsum[c][w];
-        base[c] = pre + inc[c] - v[c];
+    for (int q = 0; q < Q; ++q) {
+        lh[q] = cnt[0][q * NW + wave] + static_cast<uint32_t>(__popcll(hb[q] & lt));
+        if (head[q]) hp[lh[q]] = t0 + q * kRleThreads + tid;
     }
-    if (tile == ntiles - 1 && tid == 255) {
-        const uint32_t R = base[0] + v[0], Lg = base[1] + v[1];
-        counts[1] = R - Lg;
+    __syncthreads();
+    uint32_t len[Q], ce[Q];
+    uint64_t lbal[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const uint32_t p = t0 + q * kRleThreads + tid;
+        len[q] = head[q] ? hp[lh[q] + 1] - p : 0u;
+        const bool isl = head[q] && len[q] >= tau;
+        const uint32_t nc = isl ? (len[q] + chunk - 1) / chunk : 0u;
+        lbal[q] = __ballot(isl);
+        uint32_t wtot = 0;
+        ce[q] = 0;
+        if (lbal[q]) {   // chunk prefix only where this wave has a long run
+            const uint32_t inc = wave_incl_scan(nc, lane);
+            ce[q] = inc - nc;
+            wtot = __shfl(inc, 63);
+        }
+        if (lane == 0) {
+            cnt[1][q * NW + wave] = static_cast<uint32_t>(__popcll(lbal[q]));
+            cnt[2][q * NW + wave] = wtot;
+        }
+    }
+    __syncthreads();
+    if (wave == 1 || wave == 2) {
+        const uint32_t tot = scan_table(cnt[wave], lane);
+        if (lane == 0) s_tot[wave] = tot;
+    }
+    __syncthreads();
+    if (wave < 3) {
+        const uint32_t val = s_tot[wave];
+        const uint32_t ex = lookback_wave(rstatus + static_cast<size_t>(wave) * ntiles, tile, val,
+                                          err, lane);
+        if (lane == 0) {
+            texcl[wave] = ex;
+            if (tile == ntiles - 1) counts[wave == 0 ? 0 : (wave == 1 ? 2 : 3)] = ex + val;
+        }
+    }
+    __syncthreads();
+    if (tile == ntiles - 1 && tid == 0) {
+        const uint32_t R = texcl[0] + s_tot[0];
+        counts[1] = R - (texcl[1] + s_tot[1]);
         if (API) run_start[R] = N;
     }
-    uint32_t r = base[0], lb = base[1], cb = base[2];
 #pragma unroll
-    for (int q = 0; q < kRleItems; ++q) {
-        if (len[q] == 0) continue;
-        if (r >= N || lb > r) break;  // guards: unreachable when consistent
-        const uint32_t i = i0 + q;
+    for (int q = 0; q < Q; ++q) {
+        if (!head[q]) continue;
+        const uint32_t i = t0 + q * kRleThreads + tid;
+        const uint32_t r = texcl[0] + lh[q];
+        const uint32_t lb = texcl[1] + cnt[1][q * NW + wave] +
+                            static_cast<uint32_t>(__popcll(lbal[q] & lt));
+        if (r >= N || lb > r) continue;  // guards: unreachable when consistent
         const uint32_t key = kk[q];
         if (API) {
             unique[r] = key;
@@ -528,16 +733,16 @@ __global__ __launch_bounds__(256) void k_rle(
             run_len[r] = len[q];
         }
         if (len[q] >= tau) {
+            const uint32_t cb = texcl[2] + cnt[2][q * NW + wave] + ce[q];
             if (lb < max_long) long_info[lb] = make_uint4(key, i, len[q], cb);
             if (API) long_ids[lb] = r;
-            ++lb;
-            cb += (len[q] + chunk - 1) / chunk;
         } else {
-            const uint32_t t = static_cast<uint32_t>(find_table_g(hash_off, T, key));
+            const uint32_t t = static_cast<uint32_t>(
+                lds_hash ? find_table(s_hash, T, key) : find_table(hash_off, T, key));
             short_info[r - lb] = make_uint4(key, i, len[q], t);
+            if (FIRST) short_first[r - lb] = pay[q];
             if (API) short_ids[r - lb] = r;
         }
-        ++r;
     }
 }
 
@@ -558,7 +763,7 @@ hipError_t sort_passes(BwdArgs& a)
     int shift = 0;
     for (int pass = 0; pass < L.npasses; ++pass) {
         const int nbits = L.digit_bits[pass];
-        hipLaunchKernelGGL((k_onesweep<R, PT>), dim3(nb), dim3(256), 0, a.stream, keys[cur],
+        hipLaunchKernelGGL((k_onesweep<R, PT>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys[cur],
                            vals[cur], keys[cur ^ 1], vals[cur ^ 1], N, shift, nbits,
                            ctl + kCtlTotals + pass * kRadix,
                            status + static_cast<size_t>(pass) * kRadix * nb,
@@ -576,7 +781,7 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
 {
     const BwdLayout& L = a.L;
     char* ws = a.ws;
-    hipLaunchKernelGGL((k_prep<IT, MODE>), dim3(L.prep_blocks), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((k_prep<IT, MODE>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
                        a.plan->d_tables, static_cast<uint32_t>(a.B), total_bags,
                        static_cast<uint32_t>(L.prep_bags), static_cast<const IT*>(a.indices),
                        static_cast<const IT*>(a.offsets), a.psw,
@@ -627,11 +832,9 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     stage_mark(p, 1, a.stream);
-    const bool big = sort_rounds(L.N) == 16;
-    if (mode == kPayloadSampleW)
-        e = big ? sort_passes<16, uint2>(a) : sort_passes<8, uint2>(a);
-    else
-        e = big ? sort_passes<16, uint32_t>(a) : sort_passes<8, uint32_t>(a);
+    static_assert(kSortRounds == 8, "one tile shape is instantiated");
+    e = mode == kPayloadSampleW ? sort_passes<kSortRounds, uint2>(a)
+                                : sort_passes<kSortRounds, uint32_t>(a);
     if (e != hipSuccess) return e;
     stage_mark(p, 2, a.stream);
 
@@ -639,8 +842,11 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
     const uint32_t tau = static_cast<uint32_t>(p->tuning.tau);
     const uint32_t chunk = static_cast<uint32_t>(p->tuning.chunk);
     const uint32_t nt = static_cast<uint32_t>(L.rle_blocks);
-    auto kern = api_outputs ? k_rle<true> : k_rle<false>;
-    hipLaunchKernelGGL(kern, dim3(nt), dim3(256), 0, a.stream, skeys, N, tau, chunk, nt,
+    auto kern = api_outputs ? k_rle<true, 0>
+                            : (a.payload_pairs ? k_rle<false, 2> : k_rle<false, 1>);
+    hipLaunchKernelGGL(kern, dim3(nt), dim3(kRleThreads), 0, a.stream, skeys,
+                       static_cast<const void*>(ws + L.off_vals[a.final_buf]),
+                       reinterpret_cast<uint2*>(ws + L.off_short_first), N, tau, chunk, nt,
                        reinterpret_cast<uint32_t*>(ws + L.off_rle_status), ctl + kCtlRleTicket,
                        ctl + kCtlError, p->d_hash_off, p->T,
                        reinterpret_cast<uint4*>(ws + L.off_short_info),

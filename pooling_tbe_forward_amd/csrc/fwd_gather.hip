@@ -34,10 +34,55 @@ __device__ __forceinline__ int64_t lane_bcast(IT v, int src) {
     return static_cast<int64_t>(__shfl(v, src));
 }
 
+// Issue the U row loads of one round: slot grp of row r0 + u*G + grp.  Rows
+// past the bag's end (or lanes past D) read the table's first row and are
+// masked out when summed, so every load is unconditional and all U stay in
+// flight.
+template <typename WT, typename IT, int VEC, int U>
+__device__ __forceinline__ void issue_round(Pack<WT, VEC> (&v)[U], float (&w)[U], bool (&on)[U],
+                                            const WT* tcol, int D, IT my_id,
+                                            float my_w, int r0, int n, int g_log2, int grp,
+                                            bool active, bool tw)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = r0 + (u << g_log2) + grp;
+        on[u] = r < n && active;
+        const int64_t id = lane_bcast(my_id, r & 63);
+        const int64_t row = on[u] ? id : 0;
+        w[u] = tw ? __shfl(my_w, r & 63) : 1.f;
+        v[u] = *reinterpret_cast<const Pack<WT, VEC>*>(tcol + row * D);
+    }
+}
+
+// Nothing moves across this point: neither memory operations (the empty asm)
+// nor arithmetic (the scheduling barrier).
+__device__ __forceinline__ void issue_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename WT, int VEC, int U>
+__device__ __forceinline__ void sum_round(float (&acc)[VEC], const Pack<WT, VEC> (&v)[U],
+                                          const float (&w)[U], const bool (&on)[U], bool tw)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float x = on[u] ? to_f32(v[u].v[k]) : 0.f;
+            if (tw)
+                acc[k] = fmaf(w[u], x, acc[k]);
+            else
+                acc[k] += x;
+        }
+}
+
 template <typename WT, typename IT, int VEC, int U, bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_fwd_gather(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, int32_t sumD,
-    const WT* __restrict__ weights, const IT* __restrict__ indices,
+    const WT* weights, const IT* __restrict__ indices,
     const IT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
     uint32_t bags_per_wave, int32_t hist_active)
 {
@@ -63,7 +108,9 @@ __global__ __launch_bounds__(256) void k_fwd_gather(
         const int g_log2 = 6 - lpr_log2;
         const int grp = lane >> lpr_log2;
         const int col = (lane & ((1 << lpr_log2) - 1)) * VEC;
-        const WT* __restrict__ tb = weights + d.w_off;
+        // (weights is not restrict-qualified: loads through it must stay
+        // ordered by issue_fence)
+        const WT* tb = weights + d.w_off;
         float* __restrict__ orow = out + static_cast<int64_t>(b) * sumD + d.out_off;
 
         for (int c0 = 0; c0 < D; c0 += 64 * VEC) {
@@ -72,41 +119,48 @@ __global__ __launch_bounds__(256) void k_fwd_gather(
             float acc[VEC];
 #pragma unroll
             for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
+            const WT* tcol = tb + (active ? c : 0);
 
+            // ids of the next 64 lookups are fetched while the current ones are
+            // gathered; row rounds are double-buffered (round r+1 is issued
+            // before round r is summed), so 2*U row loads per lane are in flight
+            IT nid = 0;
+            float nw = 1.f;
+            if (lane < e - s) {
+                nid = indices[s + lane];
+                if (tw) nw = psw[s + lane];
+            }
             for (int64_t base = s; base < e; base += 64) {
                 const int n = (e - base) < 64 ? static_cast<int>(e - base) : 64;
-                IT my_id = 0;
-                float my_w = 1.f;
-                if (lane < n) {
-                    my_id = indices[base + lane];
-                    if (tw) my_w = psw[base + lane];
+                const IT my_id = nid;
+                const float my_w = nw;
+                if (base + 64 + lane < e) {
+                    nid = indices[base + 64 + lane];
+                    if (tw) nw = psw[base + 64 + lane];
                 }
-                for (int r0 = 0; r0 < n; r0 += (U << g_log2)) {
-                    Pack<WT, VEC> v[U];
-                    float w[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int r = r0 + (u << g_log2) + grp;
-                        const int64_t row = lane_bcast(my_id, r & 63);
-                        w[u] = tw ? __shfl(my_w, r & 63) : 1.f;
-                        if (r < n && active) {
-                            v[u] = *reinterpret_cast<const Pack<WT, VEC>*>(tb + row * D + c);
-                        } else {
-#pragma unroll
-                            for (int k = 0; k < VEC; ++k) v[u].v[k] = WT(0);
-                            w[u] = 0.f;
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-#pragma unroll
-                        for (int k = 0; k < VEC; ++k) {
-                            if (tw)
-                                acc[k] = fmaf(w[u], to_f32(v[u].v[k]), acc[k]);
-                            else
-                                acc[k] += to_f32(v[u].v[k]);
-                        }
-                    }
+                const int step = U << g_log2;
+                Pack<WT, VEC> va[U], vb[U];
+                float wa[U], wb[U];
+                bool oa[U], ob[U];
+                issue_round<WT, IT, VEC, U>(va, wa, oa, tcol, D, my_id, my_w, 0, n, g_log2, grp,
+                                            active, tw);
+                issue_fence();
+                // the next round is always issued (past the end it reads row 0,
+                // masked): a load under a branch would make the compiler wait
+                // for every outstanding load where the branches meet
+                // (issue_fence keeps the compiler from moving a round's loads down
+                // to their use, or a sum above the next round's loads, which
+                // would undo the double buffering)
+                for (int r0 = 0; r0 < n; r0 += 2 * step) {
+                    issue_round<WT, IT, VEC, U>(vb, wb, ob, tcol, D, my_id, my_w, r0 + step, n,
+                                                g_log2, grp, active, tw);
+                    issue_fence();
+                    sum_round<WT, VEC, U>(acc, va, wa, oa, tw);
+                    if (r0 + step >= n) break;
+                    issue_round<WT, IT, VEC, U>(va, wa, oa, tcol, D, my_id, my_w, r0 + 2 * step, n,
+                                                g_log2, grp, active, tw);
+                    issue_fence();
+                    sum_round<WT, VEC, U>(acc, vb, wb, ob, tw);
                 }
             }
             // fold the G row slots: lanes that differ only in the slot bits

@@ -239,6 +239,45 @@ static tbe_status prepare_bwd(const tbe_plan* p, int32_t B, const void* indices,
     return TBE_OK;
 }
 
+tbe_status tbe_backward_prepare(const tbe_plan* p, int32_t B, const void* indices,
+                                int64_t num_indices, const void* offsets, const float* psw,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (p && B == 0 && num_indices >= 0) return TBE_OK;
+    BwdArgs a;
+    tbe_status st = prepare_bwd(p, B, indices, num_indices, offsets, workspace,
+                                workspace_bytes, stream, a);
+    if (st != TBE_OK) return st;
+    if (num_indices == 0) return TBE_OK;
+    a.psw = psw;
+    stage_mark(p, 0, a.stream);
+    st = run_sort_rle(a, false) == hipSuccess ? TBE_OK : TBE_EHIP;
+    const_cast<tbe_plan*>(p)->n_stage_ev = 0;
+    return st;
+}
+
+tbe_status tbe_backward_apply(const tbe_plan* p, int32_t B, int64_t num_indices, int32_t weighted,
+                              void* weights, const float* grad_output, float lr,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (p && B == 0 && num_indices >= 0) return TBE_OK;
+    BwdArgs a;
+    // indices / offsets are not read here; any non-null stand-in passes the checks
+    tbe_status st = prepare_bwd(p, B, workspace, num_indices, workspace, workspace,
+                                workspace_bytes, stream, a);
+    if (st != TBE_OK) return st;
+    if (!weights || !grad_output) return TBE_EINVAL;
+    if (num_indices == 0) return TBE_OK;
+    a.grad = grad_output;
+    a.weights = weights;
+    a.lr = lr;
+    a.final_buf = a.L.npasses & 1;   // each radix pass swaps the ping-pong buffers
+    a.payload_pairs = weighted != 0;
+    st = run_segment_sgd(a) == hipSuccess ? TBE_OK : TBE_EHIP;
+    const_cast<tbe_plan*>(p)->n_stage_ev = 0;
+    return st;
+}
+
 tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const void* indices,
                             int64_t num_indices, const void* offsets, const float* psw,
                             const float* grad_output, float lr, void* workspace,

@@ -109,6 +109,7 @@ struct BwdLayout {
     size_t off_ctl;             // [kCtlWords]
     size_t off_unique, off_run_start, off_run_len, off_short, off_long;
     size_t off_short_info;      // [N] {key, start, len, table}
+    size_t off_short_first;     // [N] {sample, per-sample weight bits} of each short run's first lookup
     size_t off_long_info;       // [max_long] {key, start, len, first chunk}
     size_t off_partials;        // [max_chunks * max_D] (fp64 or fp32)
     size_t total = 0;

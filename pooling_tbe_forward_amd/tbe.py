@@ -62,6 +62,10 @@ def lib():
         L.tbe_backward_workspace_bytes.restype = SZ
         L.tbe_backward_sgd.argtypes = [P, I32, P, P, I64, P, P, P, ctypes.c_float, P, SZ, P]
         L.tbe_backward_sgd.restype = I32
+        L.tbe_backward_prepare.argtypes = [P, I32, P, I64, P, P, P, SZ, P]
+        L.tbe_backward_prepare.restype = I32
+        L.tbe_backward_apply.argtypes = [P, I32, I64, I32, P, P, ctypes.c_float, P, SZ, P]
+        L.tbe_backward_apply.restype = I32
         L.tbe_sort_rle.argtypes = [P, I32, P, I64, P, P, SZ, ctypes.POINTER(tbe_sort_view), P]
         L.tbe_sort_rle.restype = I32
         L.tbe_set_stage_events.argtypes = [P, ctypes.POINTER(ctypes.c_void_p), I32]
@@ -194,7 +198,8 @@ def tbe_backward_workspace_bytes(plan: Plan, B: int, num_indices: int) -> int:
 
 
 def tbe_set_stage_events(plan: Plan, events):
-    """events: sequence of raw hipEvent_t handles (ints); None clears."""
+    """events: sequence of raw hipEvent_t handles (ints, None for a stage not
+    recorded); an empty sequence or None clears."""
     if not events:
         _check(lib().tbe_set_stage_events(plan.handle, None, 0), "tbe_set_stage_events")
         return
@@ -225,6 +230,24 @@ def tbe_backward_sgd(plan: Plan, B: int, weights, indices, offsets, per_sample_w
                                   _ptr(grad_output), float(lr), _ptr(workspace),
                                   int(workspace.numel() * workspace.element_size()),
                                   _stream(stream)), "tbe_backward_sgd")
+    return weights
+
+
+def tbe_backward_prepare(plan: Plan, B: int, indices, offsets, per_sample_weights, workspace,
+                         stream=None):
+    _check(lib().tbe_backward_prepare(plan.handle, int(B), _ptr(indices), int(indices.numel()),
+                                      _ptr(offsets), _ptr(per_sample_weights), _ptr(workspace),
+                                      int(workspace.numel() * workspace.element_size()),
+                                      _stream(stream)), "tbe_backward_prepare")
+    return workspace
+
+
+def tbe_backward_apply(plan: Plan, B: int, num_indices: int, weighted: bool, weights,
+                       grad_output, lr: float, workspace, stream=None):
+    _check(lib().tbe_backward_apply(plan.handle, int(B), int(num_indices), 1 if weighted else 0,
+                                    _ptr(weights), _ptr(grad_output), float(lr), _ptr(workspace),
+                                    int(workspace.numel() * workspace.element_size()),
+                                    _stream(stream)), "tbe_backward_apply")
     return weights
 
 

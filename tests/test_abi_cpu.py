@@ -56,6 +56,8 @@ def test_null_plan_calls():
     assert L.tbe_plan_layout(None, None, None, None) == tbe.TBE_EINVAL
     assert L.tbe_workspace_init(None, 1 << 20, None) == tbe.TBE_EINVAL
     assert L.tbe_set_stage_events(None, None, 0) == tbe.TBE_EINVAL
+    assert L.tbe_backward_prepare(None, 1, None, 0, None, None, None, 0, None) == tbe.TBE_EINVAL
+    assert L.tbe_backward_apply(None, 1, 0, 0, None, None, 0.1, None, 0, None) == tbe.TBE_EINVAL
     L.tbe_plan_destroy(None)
 
 

@@ -366,3 +366,40 @@ def test_stage_events_bracket_the_backward():
                          prob.lr, ws)
     torch.cuda.synchronize()
     assert evs[5].elapsed_time(late) >= 0.0
+
+
+@pytest.mark.parametrize("name,B,tau", [("stress", 512, 64), ("mixed", 64, 16), ("uniform", 256, 64),
+                                        ("toy", None, 2)])
+def test_prepare_apply_overlapped_matches_backward_sgd(name, B, tau):
+    """Integer stage on a second stream while the forward runs on the first,
+    then the apply half: bit-identical weights to one tbe_backward_sgd call,
+    and the forward output is unaffected."""
+    prob = dg.make_problem(name, B=B) if B else dg.make_problem(name)
+    plan = H.make_plan(prob)
+    tbe.tbe_set_tuning(plan, tau=tau)
+    d = H.device_inputs(prob)
+    w_ref = dg.packed_weights_torch(prob, "cuda")
+    w_new = w_ref.clone()
+    out_ref = torch.empty(prob.B, prob.sum_D, device="cuda")
+    tbe.tbe_forward(plan, prob.B, w_ref, d["indices"], d["offsets"], d["psw"], out_ref)
+    ws1 = _workspace(plan, prob)
+    tbe.tbe_backward_sgd(plan, prob.B, w_ref, d["indices"], d["offsets"], d["psw"], d["grad"],
+                         prob.lr, ws1)
+    ws2 = _workspace(plan, prob)
+    out = torch.full((prob.B, prob.sum_D), float("nan"), device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    tbe.tbe_backward_prepare(plan, prob.B, d["indices"], d["offsets"], d["psw"], ws2, stream=side)
+    tbe.tbe_forward(plan, prob.B, w_new, d["indices"], d["offsets"], d["psw"], out, stream=main)
+    ready = torch.cuda.Event()
+    ready.record(side)
+    main.wait_event(ready)
+    tbe.tbe_backward_apply(plan, prob.B, prob.N, d["psw"] is not None, w_new, d["grad"], prob.lr,
+                           ws2, stream=main)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    assert torch.equal(w_new, w_ref)
+    assert int(_u32(ws2[48:52].view(torch.int32))[0]) == 0
