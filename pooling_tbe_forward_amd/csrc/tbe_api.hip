@@ -199,8 +199,15 @@ tbe_status tbe_forward(const tbe_plan* p, int32_t B, const void* weights, const 
               static_cast<hipStream_t>(stream)};
     stage_mark(p, 0, a.stream);
     tbe_status st2 = TBE_OK;
+    // the gather kernel is launched only if some table is not pooled by the
+    // histogram kernel (the same routing as in both kernels)
+    bool gather = !a.hist_active;
+    for (int t = 0; t < p->T && !gather; ++t) {
+        const int32_t f = p->h_tables[t].flags;
+        gather = !(f & TD_HIST_OK) || (psw && (f & TD_WEIGHTED));
+    }
     if (a.hist_active && launch_fwd_hist(a) != hipSuccess) st2 = TBE_EHIP;
-    if (st2 == TBE_OK && launch_fwd_gather(a) != hipSuccess) st2 = TBE_EHIP;
+    if (st2 == TBE_OK && gather && launch_fwd_gather(a) != hipSuccess) st2 = TBE_EHIP;
     stage_mark(p, 1, a.stream);
     const_cast<tbe_plan*>(p)->n_stage_ev = 0;
     return st2;

@@ -175,3 +175,18 @@ def test_deterministic_repeats():
     for _ in range(5):
         assert np.array_equal(_run_forward(prob, w_dev, plan=plan).view(np.uint32),
                               first.view(np.uint32))
+
+
+def test_hist_large_table_unstaged_and_mixed_launch():
+    """Histogram tables too large to copy into LDS (rows x D above 32768
+    elements) read their MFMA operands from global memory; a launch mixing
+    them with small tables stays exact too."""
+    seed = next(s for s in range(100, 200)
+                if dg.exact_problem(s, T=2, B=50, dims=(256, 16), wdtype="f16", weighted=False,
+                                    max_len=300, max_rows=256)[0].rows[0] > 160)
+    prob, packed = dg.exact_problem(seed, T=2, B=50, dims=(256, 16), wdtype="f16",
+                                    weighted=False, max_len=300, max_rows=256)
+    assert prob.rows[0] * 256 > 32768
+    out = _run_forward(prob, H.device_weights_from_host(packed), hist_mode=2)
+    ref = H.oracle_forward(prob, packed)
+    assert np.array_equal(out.astype(np.float64), ref)
