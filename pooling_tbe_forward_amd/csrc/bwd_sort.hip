@@ -632,19 +632,26 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     const uint32_t t0 = tile * kRleTile;
     const uint32_t tend = (N - t0) < uint32_t(kRleTile) ? N : t0 + kRleTile;
 
-    uint32_t kk[Q];
+    // every load is issued unconditionally (positions past the end are
+    // clamped to N-1 and ignored), so all 2-3 x Q of them are in flight at once
+    uint32_t kk[Q], kp[Q];
     uint2 pay[Q];
     bool head[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const uint32_t p = t0 + q * kRleThreads + tid;
-        const bool ok = p < tend;
-        kk[q] = ok ? keys[p] : 0u;
+        const uint32_t pc = p < N ? p : N - 1;
+        kk[q] = keys[pc];
+        kp[q] = keys[pc > 0 ? pc - 1 : 0];
         pay[q] = make_uint2(0u, 0x3f800000u);   // weight 1.0 unless the payload has one
-        if (FIRST == 1 && ok) pay[q].x = static_cast<const uint32_t*>(payload)[p];
-        if (FIRST == 2 && ok) pay[q] = static_cast<const uint2*>(payload)[p];
-        const uint32_t kp = (ok && p > 0) ? keys[p - 1] : 0u;
-        head[q] = ok && (p == 0 || kk[q] != kp);
+        if (FIRST == 1) pay[q].x = static_cast<const uint32_t*>(payload)[pc];
+        if (FIRST == 2) pay[q] = static_cast<const uint2*>(payload)[pc];
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const uint32_t p = t0 + q * kRleThreads + tid;
+        head[q] = p < tend && (p == 0 || kk[q] != kp[q]);
+        if (p >= tend) kk[q] = 0u;
     }
     // the tile's last run may continue into later tiles: the wave holding the
     // tile's last position finds where it ends (a full tile ends at round Q-1,
