@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 matrix peak of an MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_segment_uniform.json")
 SEGMENT_SRC = os.path.join(ROOT, "pooling_tbe_forward_amd", "csrc", "bwd_segment.hip")
 
@@ -317,6 +318,24 @@ def summarize(r):
                 bwd_stage_us={k: round(1e3 * float(v), 2) for k, v in zip(BWD_STAGES, st)})
 
 
+def hist_mfma_flops(wl):
+    """Matrix-unit work of one forward when the histogram x table path runs:
+    2 * B * rows * D per eligible table (fp16, unweighted, rows and D <= 256,
+    mean bag length >= the plan's threshold)."""
+    from pooling_tbe_forward_amd import tbe
+    p = wl.probs[0]
+    if p.wdtype != "f16":
+        return 0
+    t = tbe.tbe_get_tuning(wl.plan)
+    if t.hist_mode == 1 or (t.hist_mode == 0 and p.N < t.hist_min_mean_len * p.T * p.B):
+        return 0
+    flops = 0
+    for k in range(p.T):
+        if p.rows[k] <= 256 and p.dims[k] <= 256 and not (p.psw is not None and p.weighted[k]):
+            flops += 2 * p.B * int(p.rows[k]) * int(p.dims[k])
+    return flops
+
+
 def report_configs(steps, warmup, hip):
     import torch
     for name in ("uniform", "mixed", "hist", "stress"):
@@ -331,6 +350,11 @@ def report_configs(steps, warmup, hip):
                     bwd_bytes_min=wl.bytes[0]["bwd_min"], **summarize(r))
         line["fwd_pct_peak"] = 100 * line["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS
         line["bwd_pct_peak"] = 100 * line["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS
+        hist_flops = hist_mfma_flops(wl)
+        if hist_flops:   # counts x table on the matrix unit (fp16 in, fp32 accumulate)
+            tf = hist_flops / (line["fwd_ms"] * 1e-3) / 1e12
+            line["mfma_tflops"] = tf
+            line["mfma_pct_peak_fp16"] = 100 * tf / PEAK_MFMA_F16_TFLOPS
         print(json.dumps(line), file=sys.stderr, flush=True)
         del wl
         torch.cuda.empty_cache()
