@@ -8,11 +8,13 @@ uniform ids).  Prints ONE JSON line on stdout.
 * Inputs are resident in HBM before the timed region.  Consecutive steps cycle
   through several distinct batches over the same tables, so no step re-reads
   the rows of the step before it from cache.
-* The step's schedule: by default the backward's integer stage (key pass,
-  radix sort, run-length encode; it reads only the batch's indices) runs on a
-  second stream while the forward runs, and the segment reduce + SGD follows
-  both (--schedule serial: forward, then the whole backward, on one stream).
-  Both schedules are timed; the JSON line carries both step times.
+* The step's schedule (--schedule): by default each batch's step (forward,
+  then backward-SGD) is captured once in a HIP graph and replayed; "serial"
+  launches the same kernels eagerly on one stream; "overlap" runs the
+  backward's integer stage (key pass, radix sort, run-length encode; it reads
+  only the batch's indices) on a second stream while the forward runs.  All
+  three are timed; the JSON line carries every step time, and the per-stage
+  times (stage events) come from the eager serial run.
 * Stage times come from HIP events that the library records on its streams at
   its own stage boundaries (tbe_set_stage_events), so the dominant kernel's
   duration is measured live inside the timed region.
@@ -58,9 +60,11 @@ WORKLOAD_DESC = {
 }
 BWD_STAGES = ["keys", "radix_sort", "rle", "segment_sgd", "long_combine"]
 SCHEDULE_DESC = {
+    "graph": "tbe_forward then tbe_backward_sgd, captured once per batch in a HIP graph and "
+             "replayed",
     "overlap": "backward integer stage (tbe_backward_prepare) on a second stream concurrently "
                "with tbe_forward, then tbe_backward_apply",
-    "serial": "tbe_forward then tbe_backward_sgd on one stream",
+    "serial": "tbe_forward then tbe_backward_sgd on one stream, launched eagerly",
 }
 
 
@@ -240,6 +244,40 @@ def run_steps(wl, steps, warmup, hip, overlap=False):
                 fwd_bytes=pick("fwd_min"), bwd_bytes=pick("bwd_min"), seg_bytes=pick("seg_min"))
 
 
+def capture_steps(wl):
+    """One HIP graph per batch, each holding that batch's whole step (forward,
+    then backward-SGD: the library's kernels only, no host work)."""
+    import torch
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()          # default priority
+    graphs = []
+    for k in range(len(wl.probs)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            wl.fwd(k)
+            wl.bwd(k)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def run_graph_steps(wl, graphs, steps, warmup):
+    """Replay the captured steps: warm-up, then `steps` timed replays between
+    two synchronizations."""
+    import torch
+    nb = len(graphs)
+    for s in range(warmup):
+        graphs[s % nb].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        graphs[s % nb].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ks = [s % nb for s in range(steps)]
+    return dict(wall_s=wall, lookups=np.array([wl.bytes[k]["N"] for k in ks], dtype=np.float64))
+
+
 def cpu_baseline(budget_s=20.0):
     """The CPU oracle, as it stands, on the uniform workload's batch 0:
     forward of every bag, the integer stage, and backward-SGD of every touched
@@ -342,7 +380,9 @@ def report_configs(steps, warmup, hip):
         wl = Workload(name, nbatches=3 if name != "mixed" else 2)
         r = run_steps(wl, steps, warmup, hip)
         r2 = run_steps(wl, steps, warmup, hip, overlap=True)
+        r3 = run_graph_steps(wl, capture_steps(wl), steps, warmup)
         line = dict(config=name, N=wl.bytes[0]["N"], unique_rows=wl.bytes[0]["unique_rows"],
+                    step_ms_graph=1e3 * r3["wall_s"] / steps,
                     step_ms_serial=1e3 * r["wall_s"] / steps,
                     step_ms_overlap=1e3 * r2["wall_s"] / steps,
                     fwd_bytes_min=wl.bytes[0]["fwd_min"],
@@ -420,7 +460,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batches", type=int, default=4)
-    ap.add_argument("--schedule", default="serial", choices=sorted(SCHEDULE_DESC))
+    ap.add_argument("--schedule", default="graph", choices=sorted(SCHEDULE_DESC))
     ap.add_argument("--config", default="uniform", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -457,14 +497,16 @@ def main():
     # per-stage breakdown and as a cross-check
     r_serial = run_steps(wl, args.steps, args.warmup, hip, overlap=False)
     r_over = run_steps(wl, args.steps, args.warmup, hip, overlap=True)
-    r = r_over if args.schedule == "overlap" else r_serial
+    r_graph = run_graph_steps(wl, capture_steps(wl), args.steps, args.warmup)
+    r = dict(serial=r_serial, overlap=r_over, graph=r_graph)[args.schedule]
     step_ms = 1e3 * r["wall_s"] / args.steps
     lookups = float(np.sum(r["lookups"]))
     value = lookups / r["wall_s"]
     sm = summarize(r_serial)
     p0 = wl.probs[0]
-    seg_us = float(np.mean(r["stage_ms"][:, 3])) * 1e3
-    seg_bytes = float(np.mean(r["seg_bytes"]))
+    # the dominant kernel's duration: stage events of the eagerly launched steps
+    seg_us = float(np.mean(r_serial["stage_ms"][:, 3])) * 1e3
+    seg_bytes = float(np.mean(r_serial["seg_bytes"]))
     seg_gbps = seg_bytes / (seg_us * 1e-6) / 1e9
     roof = dict(bound="hbm", kernel="k_segment (backward segment-reduce + SGD)",
                 achieved=round(seg_gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
@@ -481,6 +523,7 @@ def main():
                schedule=SCHEDULE_DESC[args.schedule],
                ms_per_step_serial=1e3 * r_serial["wall_s"] / args.steps,
                ms_per_step_overlap=1e3 * r_over["wall_s"] / args.steps,
+               ms_per_step_graph=1e3 * r_graph["wall_s"] / args.steps,
                fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
                bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
                roofline=roof)
