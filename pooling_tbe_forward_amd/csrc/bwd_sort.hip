@@ -51,7 +51,7 @@ constexpr uint32_t kValMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 24;
 constexpr int kPrepMaxBags = 2048;   // bags per k_prep block (LDS offsets cache)
 constexpr int kPrepKeys = 1024;      // target keys per k_prep block
-constexpr int kPrepThreads = 1024;
+constexpr int kPrepThreads = 512;    // measured: 512 or 256 threads per block beat 1024
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -250,8 +250,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
     __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
     const int tid = threadIdx.x;
-    (&hist[0][0])[tid] = 0u;
-    static_assert(4 * kRadix == kPrepThreads, "one histogram word per thread");
+    for (int i = tid; i < 4 * kRadix; i += kPrepThreads) (&hist[0][0])[i] = 0u;
     const uint32_t g0 = blockIdx.x * bags_per_block;
     const uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
     const uint32_t t_first = nb ? g0 / B : 0;
@@ -325,11 +324,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     }
     __syncthreads();
     // digit totals are spread over kTotCopies copies (fewer adds per address)
-    {
-        uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadix);
-        const int q = tid >> 8;
-        const uint32_t c = hist[q][tid & (kRadix - 1)];
-        if (q < pb.npasses && c) atomicAdd(&tcopy[tid], c);
+    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadix);
+    for (int i = tid; i < 4 * kRadix; i += kPrepThreads) {
+        const int q = i >> 8;
+        const uint32_t c = hist[q][i & (kRadix - 1)];
+        if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
     }
     // the look-back words of the radix passes and the run-length encode
     for (size_t i = blockIdx.x * size_t(kPrepThreads) + tid; i < status_words;
