@@ -337,15 +337,16 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 }
 
 // ---------------------------------------------------------------------------
-// One radix pass.  A tile is kSortThreads x R keys; wave w ranks rounds of 64
-// keys with ballots (equal digits of a round are found bit by bit) and its own
-// LDS digit counters, so the rank is stable inside the tile.  The ticket and
-// the digit-totals loads are issued together, so they cost one round trip.
-template <int R, typename PT>
+// One radix pass over NB-bit digits.  A tile is kSortThreads x R keys; wave w
+// ranks rounds of 64 keys with ballots (equal digits of a round are found bit
+// by bit) and its own LDS digit counters, so the rank is stable inside the
+// tile.  The ticket and the digit-totals loads are issued together, so they
+// cost one round trip.
+template <int R, typename PT, int NB>
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const PT* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, PT* __restrict__ vals_out, uint32_t N, int shift,
-    int nbits, const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
+    const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ err, uint32_t ntiles,
     uint32_t* __restrict__ prev_totals)
 {
@@ -391,8 +392,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
         return;
     }
 
-    const uint32_t mask = (1u << nbits) - 1u;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    constexpr uint32_t mask = (1u << NB) - 1u;
     const uint32_t wbase = tile * (uint32_t(kSortThreads) * R) + static_cast<uint32_t>(wave) * (64u * R);
     uint32_t k[R], dg[R], rk[R];
     PT v[R];
@@ -408,18 +408,26 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
         const uint32_t i = wbase + r * 64u + lane;
         const bool ok = i < N;
         const uint32_t d = (k[r] >> shift) & mask;
-        // digits have at most 8 bits; bits above nbits are zero in every lane
-        uint64_t peers = __ballot(ok);
+        // lanes whose digit differs from this lane's in some bit, as two
+        // 32-bit halves: per bit, the ballot of the bit xor this lane's bit
+        // spread over a word (this shape compiles to three-input bit ops)
+        uint32_t xlo = 0u, xhi = 0u;
 #pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const bool on = (d >> bit) & 1u;
-            const uint64_t bal = __ballot(on);
-            peers &= on ? bal : ~bal;
+        for (int bit = 0; bit < NB; ++bit) {
+            const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(d << (31 - bit)) >> 31);
+            const uint64_t bal = __ballot(m != 0u);
+            xlo |= static_cast<uint32_t>(bal) ^ m;
+            xhi |= static_cast<uint32_t>(bal >> 32) ^ m;
         }
-        const uint32_t below = static_cast<uint32_t>(__popcll(peers & lt));
+        const uint64_t okm = __ballot(ok);
+        const uint32_t plo = ~xlo & static_cast<uint32_t>(okm);
+        const uint32_t phi = ~xhi & static_cast<uint32_t>(okm >> 32);
+        // peers in lower lanes, and all peers
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
+        const uint32_t npeer = static_cast<uint32_t>(__popc(plo) + __popc(phi));
         uint32_t base = 0;
         if (ok) base = wcnt[wave][d];
-        if (ok && below == 0) wcnt[wave][d] = base + static_cast<uint32_t>(__popcll(peers));
+        if (ok && below == 0) wcnt[wave][d] = base + npeer;
         dg[r] = d;
         rk[r] = base + below;
     }
@@ -752,6 +760,18 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     }
 }
 
+template <int R, typename PT, int NB>
+void launch_onesweep(BwdArgs& a, uint32_t nb, const uint32_t* keys_in, const PT* vals_in,
+                     uint32_t* keys_out, PT* vals_out, uint32_t N, int shift, int pass,
+                     uint32_t* ctl, uint32_t* status)
+{
+    hipLaunchKernelGGL((k_onesweep<R, PT, NB>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys_in,
+                       vals_in, keys_out, vals_out, N, shift, ctl + kCtlTotals + pass * kRadix,
+                       status + static_cast<size_t>(pass) * kRadix * nb,
+                       ctl + kCtlTicket + pass, ctl + kCtlError, nb,
+                       pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadix : nullptr);
+}
+
 template <int R, typename PT>
 hipError_t sort_passes(BwdArgs& a)
 {
@@ -769,12 +789,12 @@ hipError_t sort_passes(BwdArgs& a)
     int shift = 0;
     for (int pass = 0; pass < L.npasses; ++pass) {
         const int nbits = L.digit_bits[pass];
-        hipLaunchKernelGGL((k_onesweep<R, PT>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys[cur],
-                           vals[cur], keys[cur ^ 1], vals[cur ^ 1], N, shift, nbits,
-                           ctl + kCtlTotals + pass * kRadix,
-                           status + static_cast<size_t>(pass) * kRadix * nb,
-                           ctl + kCtlTicket + pass, ctl + kCtlError, nb,
-                           pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadix : nullptr);
+        // one instantiation per digit width: the rank tests only the digit's bits
+        auto* const f = nbits <= 1 ? launch_onesweep<R, PT, 1> : nbits == 2 ? launch_onesweep<R, PT, 2>
+                      : nbits == 3 ? launch_onesweep<R, PT, 3> : nbits == 4 ? launch_onesweep<R, PT, 4>
+                      : nbits == 5 ? launch_onesweep<R, PT, 5> : nbits == 6 ? launch_onesweep<R, PT, 6>
+                      : nbits == 7 ? launch_onesweep<R, PT, 7> : launch_onesweep<R, PT, 8>;
+        f(a, nb, keys[cur], vals[cur], keys[cur ^ 1], vals[cur ^ 1], N, shift, pass, ctl, status);
         cur ^= 1;
         shift += nbits;
     }
