@@ -8,13 +8,14 @@ uniform ids).  Prints ONE JSON line on stdout.
 * Inputs are resident in HBM before the timed region.  Consecutive steps cycle
   through several distinct batches over the same tables, so no step re-reads
   the rows of the step before it from cache.
-* The step's schedule (--schedule): by default each batch's step (forward,
-  then backward-SGD) is captured once in a HIP graph and replayed; "serial"
-  launches the same kernels eagerly on one stream; "overlap" runs the
-  backward's integer stage (key pass, radix sort, run-length encode; it reads
-  only the batch's indices) on a second stream while the forward runs.  All
-  three are timed; the JSON line carries every step time, and the per-stage
-  times (stage events) come from the eager serial run.
+* The step's schedule (--schedule): by default each step (forward, then
+  backward-SGD) is launched eagerly on one stream ("eager"); "graph" captures
+  each batch's step once in a HIP graph and replays it; "serial" is the eager
+  schedule with the library's stage events recorded (they add a few
+  microseconds per event); "overlap" runs the backward's integer stage (key
+  pass, radix sort, run-length encode; it reads only the batch's indices) on a
+  second stream while the forward runs.  All four are timed; the JSON line
+  carries every step time, and the per-stage times come from the "serial" run.
 * Stage times come from HIP events that the library records on its streams at
   its own stage boundaries (tbe_set_stage_events), so the dominant kernel's
   duration is measured live inside the timed region.
@@ -60,11 +61,13 @@ WORKLOAD_DESC = {
 }
 BWD_STAGES = ["keys", "radix_sort", "rle", "segment_sgd", "long_combine"]
 SCHEDULE_DESC = {
+    "eager": "tbe_forward then tbe_backward_sgd on one stream, launched eagerly",
     "graph": "tbe_forward then tbe_backward_sgd, captured once per batch in a HIP graph and "
              "replayed",
     "overlap": "backward integer stage (tbe_backward_prepare) on a second stream concurrently "
                "with tbe_forward, then tbe_backward_apply",
-    "serial": "tbe_forward then tbe_backward_sgd on one stream, launched eagerly",
+    "serial": "tbe_forward then tbe_backward_sgd on one stream, launched eagerly, with the "
+              "library's stage events recorded (per-stage times)",
 }
 
 
@@ -244,6 +247,25 @@ def run_steps(wl, steps, warmup, hip, overlap=False):
                 fwd_bytes=pick("fwd_min"), bwd_bytes=pick("bwd_min"), seg_bytes=pick("seg_min"))
 
 
+def run_plain_steps(wl, steps, warmup):
+    """Forward then backward-SGD per step on the current stream, no timing
+    events: warm-up, then `steps` timed steps between two synchronizations."""
+    import torch
+    nb = len(wl.probs)
+    for s in range(warmup):
+        wl.fwd(s % nb)
+        wl.bwd(s % nb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        wl.fwd(s % nb)
+        wl.bwd(s % nb)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ks = [s % nb for s in range(steps)]
+    return dict(wall_s=wall, lookups=np.array([wl.bytes[k]["N"] for k in ks], dtype=np.float64))
+
+
 def capture_steps(wl):
     """One HIP graph per batch, each holding that batch's whole step (forward,
     then backward-SGD: the library's kernels only, no host work)."""
@@ -381,7 +403,9 @@ def report_configs(steps, warmup, hip):
         r = run_steps(wl, steps, warmup, hip)
         r2 = run_steps(wl, steps, warmup, hip, overlap=True)
         r3 = run_graph_steps(wl, capture_steps(wl), steps, warmup)
+        r4 = run_plain_steps(wl, steps, warmup)
         line = dict(config=name, N=wl.bytes[0]["N"], unique_rows=wl.bytes[0]["unique_rows"],
+                    step_ms_eager=1e3 * r4["wall_s"] / steps,
                     step_ms_graph=1e3 * r3["wall_s"] / steps,
                     step_ms_serial=1e3 * r["wall_s"] / steps,
                     step_ms_overlap=1e3 * r2["wall_s"] / steps,
@@ -460,7 +484,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batches", type=int, default=4)
-    ap.add_argument("--schedule", default="graph", choices=sorted(SCHEDULE_DESC))
+    ap.add_argument("--schedule", default="eager", choices=sorted(SCHEDULE_DESC))
     ap.add_argument("--config", default="uniform", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -492,13 +516,13 @@ def main():
     hip = Hip()
 
     wl = Workload(args.config, nbatches=args.batches)
-    # the reported step: integer stage overlapped with the forward (default),
-    # or everything on one stream; the other schedule is timed too, for its
-    # per-stage breakdown and as a cross-check
+    # the reported step is --schedule's; the others are timed too, for the
+    # per-stage breakdown (stage events of the serial run) and as cross-checks
     r_serial = run_steps(wl, args.steps, args.warmup, hip, overlap=False)
     r_over = run_steps(wl, args.steps, args.warmup, hip, overlap=True)
     r_graph = run_graph_steps(wl, capture_steps(wl), args.steps, args.warmup)
-    r = dict(serial=r_serial, overlap=r_over, graph=r_graph)[args.schedule]
+    r_eager = run_plain_steps(wl, args.steps, args.warmup)
+    r = dict(serial=r_serial, overlap=r_over, graph=r_graph, eager=r_eager)[args.schedule]
     step_ms = 1e3 * r["wall_s"] / args.steps
     lookups = float(np.sum(r["lookups"]))
     value = lookups / r["wall_s"]
@@ -524,6 +548,7 @@ def main():
                ms_per_step_serial=1e3 * r_serial["wall_s"] / args.steps,
                ms_per_step_overlap=1e3 * r_over["wall_s"] / args.steps,
                ms_per_step_graph=1e3 * r_graph["wall_s"] / args.steps,
+               ms_per_step_eager=1e3 * r_eager["wall_s"] / args.steps,
                fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
                bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
                roofline=roof)
