@@ -58,6 +58,10 @@ def lib():
         L.oracle_backward_sgd.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
                                           P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_int64,
                                           P, P, ctypes.c_int32]
+        L.oracle_backward_adagrad.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P,
+                                              ctypes.c_int32, P, P, P, P, P, P, ctypes.c_float,
+                                              ctypes.c_float, P, ctypes.c_int64, P, P, P, P,
+                                              ctypes.c_int32]
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
         L.oracle_double_to_half.argtypes = [ctypes.c_double]
@@ -195,6 +199,40 @@ def backward_sgd(T, B, rows, dims, wdtype, tables, indices, offsets, psw, weight
                                      _p(gr), _p(nr), 1 if write_back else 0))
     del keep
     return gr, nr
+
+
+def backward_adagrad(T, B, rows, dims, wdtype, tables, indices, offsets, psw, weighted,
+                      grad_output, lr, eps, keys, state_in, write_back=False):
+    """Finished row gradients, exact row-wise Adagrad rows (float64) and the
+    rows' new fp32 state for ``keys``; ``state_in`` is the state of each
+    key's row before the step.
+
+    Returns (grad_rows [nkeys, Dmax], new_rows [nkeys, Dmax], state_out
+    [nkeys] float32).  With write_back, the rounded rows are stored into the
+    tables' host arrays."""
+    rows = _i64(rows)
+    dims = np.ascontiguousarray(dims, dtype=np.int32)
+    indices = _i64(indices)
+    offsets = _i64(offsets)
+    psw = None if psw is None else np.ascontiguousarray(psw, dtype=np.float32)
+    wm = None if weighted is None else np.ascontiguousarray(weighted, dtype=np.uint8)
+    g = np.ascontiguousarray(grad_output, dtype=np.float32)
+    keys = _i64(keys)
+    s_in = np.ascontiguousarray(state_in, dtype=np.float32)
+    if s_in.shape != keys.shape:
+        raise ValueError("state_in needs one value per key")
+    tarr, keep = _tables(tables, dims, wdtype)
+    Dmax = int(dims.max())
+    gr = np.zeros((keys.size, Dmax), np.float64)
+    nr = np.zeros((keys.size, Dmax), np.float64)
+    s_out = np.zeros(keys.size, np.float32)
+    _check(lib().oracle_backward_adagrad(T, B, _p(rows), _p(dims), wdtype,
+                                         ctypes.cast(tarr, ctypes.c_void_p), _p(indices),
+                                         _p(offsets), _p(psw), _p(wm), _p(g), float(lr),
+                                         float(eps), _p(keys), keys.size, _p(s_in), _p(s_out),
+                                         _p(gr), _p(nr), 1 if write_back else 0))
+    del keep
+    return gr, nr, s_out
 
 
 def half_to_double(bits):

@@ -322,3 +322,59 @@ int oracle_backward_sgd(int32_t T, int32_t B, const int64_t* rows, const int32_t
     free(Doff);
     return rc;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Backward + exact row-wise Adagrad for the requested rows (section "Why the
+ * backward is the hard half", where the article reads the update out of the
+ * Triton kernel).  The row gradient G is the same finished sum as for SGD.
+ * The row's one state value is raised by the mean over its D elements of
+ * G[d]^2; that new value is kept in fp32 (the state's storage type, rounded
+ * once) and the row steps by lr / (sqrt(state) + eps) times G.  eps is not
+ * given on the pages; the caller passes it. */
+int oracle_backward_adagrad(int32_t T, int32_t B, const int64_t* rows, const int32_t* dims,
+                            int32_t wdtype, oracle_table* tables,
+                            const int64_t* indices, const int64_t* offsets,
+                            const float* psw, const uint8_t* weighted,
+                            const float* grad_output, float lr, float eps,
+                            const int64_t* keys, int64_t nkeys,
+                            const float* state_in, float* state_out,
+                            double* grad_rows, double* new_rows, int32_t write_back)
+{
+    if (nkeys > 0 && (!state_in || !state_out))
+        return 1;
+    int32_t Dmax = 0;
+    for (int32_t t = 0; dims && t < T; ++t)
+        if (dims[t] > Dmax) Dmax = dims[t];
+    /* the finished row gradients, exactly as the SGD definition sums them
+     * (lr = 0 there: nothing is written back, only G is wanted) */
+    double* G = (double*)calloc((size_t)(nkeys ? nkeys : 1) * (Dmax ? Dmax : 1), sizeof(double));
+    int rc = oracle_backward_sgd(T, B, rows, dims, wdtype, tables, indices, offsets, psw,
+                                 weighted, grad_output, 0.0f, keys, nkeys, G, NULL, 0);
+    if (rc) { free(G); return rc; }
+    int64_t* hcs = (int64_t*)malloc(sizeof(int64_t) * (T + 1));
+    oracle_layout(T, rows, dims, NULL, NULL, hcs);
+    for (int64_t k = 0; k < nkeys && rc == 0; ++k) {
+        int32_t t = 0;
+        while (t + 1 < T && hcs[t + 1] <= keys[k])
+            ++t;
+        int64_t pos = held_row(&tables[t], keys[k] - hcs[t]);
+        if (pos < 0) { rc = 3; break; }
+        int32_t D = dims[t];
+        double sq = 0.0;
+        for (int32_t d = 0; d < D; ++d)
+            sq += G[k * Dmax + d] * G[k * Dmax + d];
+        float state = (float)((double)state_in[k] + sq / (double)D);
+        state_out[k] = state;
+        double rate = (double)lr / (sqrt((double)state) + (double)eps);
+        for (int32_t d = 0; d < D; ++d) {
+            double g = G[k * Dmax + d];
+            double w_new = load_elem(tables[t].data, pos * D + d, wdtype) - rate * g;
+            if (grad_rows) grad_rows[k * Dmax + d] = g;
+            if (new_rows) new_rows[k * Dmax + d] = w_new;
+            if (write_back) store_elem(tables[t].data, pos * D + d, wdtype, w_new);
+        }
+    }
+    free(hcs);
+    free(G);
+    return rc;
+}

@@ -22,7 +22,9 @@
  *  - backward, section "Why the backward is the hard half": a read row's
  *    gradient is the sum of the output gradients of every bag that read it
  *    (times the per-sample weight), and exact SGD applies w <- w - lr * g once
- *    the sum is finished.
+ *    the sum is finished; exact row-wise Adagrad (same section) keeps one
+ *    fp32 state value per row, raises it by the row's mean squared gradient
+ *    and steps the row by lr / (sqrt(state) + eps) times the gradient.
  *
  * All accumulation is in double precision.  fp16 storage is IEEE binary16,
  * decoded exactly and re-encoded with round-to-nearest-even.
@@ -80,6 +82,21 @@ int oracle_backward_sgd(int32_t T, int32_t B, const int64_t* rows, const int32_t
                         const float* grad_output, float lr,
                         const int64_t* keys, int64_t nkeys,
                         double* grad_rows, double* new_rows, int32_t write_back);
+
+/* Backward + exact row-wise Adagrad for keys[0..nkeys) (strictly ascending).
+ * state_in[k] is the fp32 state of key k's row before the step, state_out[k]
+ * receives the new one: state_in + mean_d(G[d]^2), rounded once to fp32.
+ * The row steps by lr / (sqrt(new state) + eps) * G.  grad_rows, new_rows and
+ * write_back as for oracle_backward_sgd.  Section "Why the backward is the
+ * hard half" (the update read out of the Triton kernel; eps is the caller's). */
+int oracle_backward_adagrad(int32_t T, int32_t B, const int64_t* rows, const int32_t* dims,
+                            int32_t wdtype, oracle_table* tables,
+                            const int64_t* indices, const int64_t* offsets,
+                            const float* psw, const uint8_t* weighted,
+                            const float* grad_output, float lr, float eps,
+                            const int64_t* keys, int64_t nkeys,
+                            const float* state_in, float* state_out,
+                            double* grad_rows, double* new_rows, int32_t write_back);
 
 /* IEEE binary16 helpers (exposed so the tests can pin them). */
 double   oracle_half_to_double(uint16_t h);
