@@ -19,6 +19,9 @@ uniform ids).  Prints ONE JSON line on stdout.
 * Stage times come from HIP events that the library records on its streams at
   its own stage boundaries (tbe_set_stage_events), so the dominant kernel's
   duration is measured live inside the timed region.
+* The JSON line also carries "adagrad": the same steps with exact row-wise
+  Adagrad in the backward (tbe_backward_adagrad, one fp32 state per row): the
+  eager step time, the backward's stage times and its segment kernel's rate.
 * --report also prints one JSON line per configuration (uniform, mixed, hist,
   stress) with forward / backward stage times on stderr.
 * --calibrate-copy runs a 1 GiB device copy (for scaling rocprofv3 byte
@@ -95,7 +98,8 @@ def algorithmic_bytes(prob):
     # segment-reduce + SGD kernel: every touched row read and written once,
     # grad_output read once, the sorted payload and the run records read once
     seg = 2 * uniq_row_bytes + out_bytes + N * payload + run_bytes
-    return dict(N=N, unique_rows=int(uk.size), passes=passes,
+    # row-wise Adagrad adds one fp32 state read + write per touched row
+    return dict(N=N, unique_rows=int(uk.size), passes=passes, seg_min_adagrad=seg + 8 * uk.size,
                 fwd_min=jag + uniq_row_bytes + out_bytes,
                 fwd_lookup=jag + lookup_row_bytes + out_bytes,
                 bwd_min=jag + out_bytes + 2 * uniq_row_bytes + sort_bytes + run_bytes,
@@ -162,6 +166,8 @@ class Workload:
         ws = max(tbe.tbe_backward_workspace_bytes(self.plan, p.B, p.N) for p in self.probs)
         self.ws = tbe.tbe_workspace_init(torch.empty(ws, dtype=torch.uint8, device="cuda"))
         self.out = torch.empty(p0.B, p0.sum_D, dtype=torch.float32, device="cuda")
+        # row-wise Adagrad state: one fp32 value per row of every table
+        self.state = torch.zeros(int(np.sum(p0.rows)), dtype=torch.float32, device="cuda")
         self.bytes = [algorithmic_bytes(p) for p in self.probs]
         self.side = torch.cuda.Stream()          # default priority
         self.ev_start = torch.cuda.Event()
@@ -183,6 +189,14 @@ class Workload:
             tbe.tbe_set_stage_events(self.plan, events)
         tbe.tbe_backward_sgd(self.plan, p.B, self.weights, d["indices"], d["offsets"], d["psw"],
                              d["grad"], p.lr, self.ws)
+
+    def bwd_adagrad(self, k, events=None):
+        from pooling_tbe_forward_amd import tbe
+        p, d = self.probs[k], self.inputs[k]
+        if events:
+            tbe.tbe_set_stage_events(self.plan, events)
+        tbe.tbe_backward_adagrad(self.plan, p.B, self.weights, self.state, d["indices"],
+                                 d["offsets"], d["psw"], d["grad"], p.lr, self.ws)
 
     def step_overlapped(self, k, hip=None, fe=None, be=None):
         """The backward's integer stage on a second stream while the forward
@@ -211,7 +225,7 @@ class Workload:
                                d["grad"], p.lr, self.ws, stream=main)
 
 
-def run_steps(wl, steps, warmup, hip, overlap=False):
+def run_steps(wl, steps, warmup, hip, overlap=False, adagrad=False):
     """Warm up, then time `steps` steps (synchronize on both sides); per-stage
     HIP events recorded by the library on the streams it runs on.
 
@@ -220,8 +234,9 @@ def run_steps(wl, steps, warmup, hip, overlap=False):
     second stream concurrently with the forward, then segment reduce + SGD."""
     import torch
     nb = len(wl.probs)
+    bwd = wl.bwd_adagrad if adagrad else wl.bwd
     one = (lambda k, fe=None, be=None: wl.step_overlapped(k, hip, fe, be)) if overlap else \
-        (lambda k, fe=None, be=None: (wl.fwd(k, fe), wl.bwd(k, be)))
+        (lambda k, fe=None, be=None: (wl.fwd(k, fe), bwd(k, be)))
     for s in range(warmup):
         one(s % nb)
     torch.cuda.synchronize()
@@ -244,26 +259,46 @@ def run_steps(wl, steps, warmup, hip, overlap=False):
     ks = [s % nb for s in range(steps)]
     pick = lambda key: np.array([wl.bytes[k][key] for k in ks], dtype=np.float64)
     return dict(wall_s=wall, fwd_ms=f_ms, bwd_ms=b_ms, stage_ms=stage_ms, lookups=pick("N"),
-                fwd_bytes=pick("fwd_min"), bwd_bytes=pick("bwd_min"), seg_bytes=pick("seg_min"))
+                fwd_bytes=pick("fwd_min"), bwd_bytes=pick("bwd_min"),
+                seg_bytes=pick("seg_min_adagrad" if adagrad else "seg_min"))
 
 
-def run_plain_steps(wl, steps, warmup):
-    """Forward then backward-SGD per step on the current stream, no timing
-    events: warm-up, then `steps` timed steps between two synchronizations."""
+def run_plain_steps(wl, steps, warmup, adagrad=False):
+    """Forward then backward (exact SGD, or row-wise Adagrad) per step on the
+    current stream, no timing events: warm-up, then `steps` timed steps
+    between two synchronizations."""
     import torch
     nb = len(wl.probs)
+    bwd = wl.bwd_adagrad if adagrad else wl.bwd
     for s in range(warmup):
         wl.fwd(s % nb)
-        wl.bwd(s % nb)
+        bwd(s % nb)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         wl.fwd(s % nb)
-        wl.bwd(s % nb)
+        bwd(s % nb)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ks = [s % nb for s in range(steps)]
     return dict(wall_s=wall, lookups=np.array([wl.bytes[k]["N"] for k in ks], dtype=np.float64))
+
+
+def adagrad_summary(wl, steps, warmup, hip):
+    """The same steps with row-wise Adagrad in the backward: plain eager step
+    time, and the backward's stage times and segment-kernel rate from a run
+    with stage events."""
+    r = run_steps(wl, steps, warmup, hip, adagrad=True)
+    rp = run_plain_steps(wl, steps, warmup, adagrad=True)
+    seg_us = float(np.mean(r["stage_ms"][:, 3])) * 1e3
+    seg_gbps = float(np.mean(r["seg_bytes"])) / (seg_us * 1e-6) / 1e9
+    return dict(step_ms_eager=1e3 * rp["wall_s"] / steps,
+                lookups_per_s=float(np.sum(rp["lookups"])) / rp["wall_s"],
+                bwd_ms=float(np.mean(r["bwd_ms"])),
+                bwd_stage_us={k: round(1e3 * float(v), 2)
+                              for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))},
+                segment_gbps_min=round(seg_gbps, 1),
+                segment_pct_peak=round(100 * seg_gbps / PEAK_HBM_GBPS, 2))
 
 
 def capture_steps(wl):
@@ -404,8 +439,10 @@ def report_configs(steps, warmup, hip):
         r2 = run_steps(wl, steps, warmup, hip, overlap=True)
         r3 = run_graph_steps(wl, capture_steps(wl), steps, warmup)
         r4 = run_plain_steps(wl, steps, warmup)
+        a = adagrad_summary(wl, steps, warmup, hip)
         line = dict(config=name, N=wl.bytes[0]["N"], unique_rows=wl.bytes[0]["unique_rows"],
                     step_ms_eager=1e3 * r4["wall_s"] / steps,
+                    adagrad=a,
                     step_ms_graph=1e3 * r3["wall_s"] / steps,
                     step_ms_serial=1e3 * r["wall_s"] / steps,
                     step_ms_overlap=1e3 * r2["wall_s"] / steps,
@@ -522,6 +559,7 @@ def main():
     r_over = run_steps(wl, args.steps, args.warmup, hip, overlap=True)
     r_graph = run_graph_steps(wl, capture_steps(wl), args.steps, args.warmup)
     r_eager = run_plain_steps(wl, args.steps, args.warmup)
+    ada = adagrad_summary(wl, args.steps, args.warmup, hip)
     r = dict(serial=r_serial, overlap=r_over, graph=r_graph, eager=r_eager)[args.schedule]
     step_ms = 1e3 * r["wall_s"] / args.steps
     lookups = float(np.sum(r["lookups"]))
@@ -551,7 +589,7 @@ def main():
                ms_per_step_eager=1e3 * r_eager["wall_s"] / args.steps,
                fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
                bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
-               roofline=roof)
+               roofline=roof, adagrad=ada)
     del wl
     torch.cuda.empty_cache()
     if args.report:

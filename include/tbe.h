@@ -185,6 +185,38 @@ tbe_status tbe_backward_apply(const tbe_plan* plan, int32_t B, int64_t num_indic
                               float lr, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward + exact row-wise Adagrad, in place (section "Why the backward is
+ * the hard half", where the article reads the update out of the Triton
+ * kernel).  For every row r of table t read by some lookup, with g the same
+ * finished row gradient as in tbe_backward_sgd:
+ *   state[k] <- state[k] + (1/D_t) * sum_d g[d]^2   (rounded once to fp32)
+ *   W_t[r]   <- W_t[r] - lr / (sqrt(state[k]) + eps) * g
+ * where k = hash_size_cumsum[t] + r (tbe_plan_layout) indexes `state`, a
+ * caller-owned device array of sum(rows) fp32 values (zero before the first
+ * step), 4-byte aligned.  eps >= 0 (the pages do not give a value; 1e-8 is
+ * this library's suggestion).  Rows nobody read keep their weights and
+ * state.  Accumulation as for tbe_backward_sgd; the state step and the rate
+ * are computed in the accumulator type.  The update needs a row's whole sum
+ * of squares inside one group of lanes, so every table needs D <= 64 * v,
+ * where v (1, 2 or 4) is the widest vector width that every D, grad_output
+ * and the weights are aligned to: TBE_ENOTSUP otherwise.  TBE_EINVAL also
+ * for a NULL or misaligned state and for eps < 0 or NaN.  Workspace and
+ * ordering rules as for tbe_backward_sgd.
+ *
+ * tbe_backward_apply_adagrad: the same update from a workspace that
+ * tbe_backward_prepare filled (see tbe_backward_apply).
+ */
+tbe_status tbe_backward_adagrad(const tbe_plan* plan, int32_t B, void* weights, float* state,
+                                const void* indices, int64_t num_indices, const void* offsets,
+                                const float* per_sample_weights, const float* grad_output,
+                                float lr, float eps, void* workspace, size_t workspace_bytes,
+                                void* stream);
+tbe_status tbe_backward_apply_adagrad(const tbe_plan* plan, int32_t B, int64_t num_indices,
+                                      int32_t weighted, void* weights, float* state,
+                                      const float* grad_output, float lr, float eps,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The backward's integer stage alone: linearize, stable radix sort,
  * run-length encode, classify against tuning.tau.  Fills *view (host struct)
  * with device pointers into the workspace.

@@ -27,6 +27,10 @@
 //  * accumulation is fp64 for fp32 tables (long Zipf runs would otherwise
 //    drift past 1e-5 relative) and fp32 for fp16 tables; w - lr*g is rounded
 //    once to the storage type;
+//  * row-wise Adagrad (same section: one state value per row, raised by the
+//    row's mean squared gradient, step lr / (sqrt(state) + eps)): the row's
+//    sum of squares is reduced across the worker's lanes with lane swaps, so
+//    a row must fit one worker (D <= 64 * VEC); one lane stores the state;
 //  * work counts are read from device memory; grids are persistent loops.
 #include "tbe_internal.h"
 
@@ -79,8 +83,12 @@ struct SegArgs {
     uint32_t max_chunks;
     uint32_t max_long;
     float lr;
+    float eps;                 // row-wise Adagrad only
+    float* state;              // row-wise Adagrad: fp32 state per row, by key
     uint32_t short_blocks;     // blocks [0, short_blocks) take short runs
 };
+
+enum Opt : int { kSgd = 0, kAdagrad = 1 };
 
 // w - lr*g in the accumulator type, rounded once to the storage type.
 template <typename WT, typename ACC, int VEC>
@@ -100,6 +108,35 @@ __device__ __forceinline__ void sgd_store(WT* __restrict__ wp, const Pack<WT, VE
                                           const ACC (&acc)[VEC], float lr)
 {
     *reinterpret_cast<Pack<WT, VEC>*>(wp) = sgd_row<WT, ACC, VEC>(w_old, acc, lr);
+}
+
+// Row-wise Adagrad for a row held by L lanes (VEC elements each; lanes past
+// the row's D hold zeros): the row's sum of squares by lane swaps inside the
+// worker, new state = old + sum / D kept in fp32, then
+// w - lr / (sqrt(state) + eps) * g with g and the subtraction in the
+// accumulator type, rounded once to the storage type.  The state and the
+// rate are fp32 whatever the accumulator (relative error ~1e-7; the fp64
+// forms cost registers, and occupancy, in the common fp32-sum path too).
+// Every lane of the worker must call it.
+template <typename WT, typename ACC, int VEC>
+__device__ __forceinline__ Pack<WT, VEC> adagrad_row(const Pack<WT, VEC>& w_old,
+                                                     const ACC (&acc)[VEC], float s_old, int D,
+                                                     int L, float lr, float eps, float& s_new)
+{
+    float sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        const float g = static_cast<float>(acc[k]);
+        sq = fmaf(g, g, sq);
+    }
+    for (int m = L >> 1; m > 0; m >>= 1) sq += __shfl_xor(sq, m);
+    s_new = s_old + sq / static_cast<float>(D);
+    const ACC rate = static_cast<ACC>(lr / (sqrtf(s_new) + eps));
+    Pack<WT, VEC> o;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k)
+        o.v[k] = static_cast<WT>(static_cast<ACC>(static_cast<float>(w_old.v[k])) - rate * acc[k]);
+    return o;
 }
 
 // Sum, for S runs held by one worker (L lanes), of w_i * grad[sample_i, col..]
@@ -212,7 +249,7 @@ __device__ __forceinline__ TableDesc table_desc(const SegArgs& c, const TableDes
     return ldg(c.tables + t);
 }
 
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD>
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD, int OPT>
 __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ weights,
                                             const TableDesc* sdesc,
                                             const uint4 (&info)[S], const uint2 (&first)[S],
@@ -233,6 +270,8 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
         const float* gcol[S];
         bool tw[S];
         uint32_t len[S], pos0[S];
+        float s_old[S];
+        int Dr[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const TableDesc d = table_desc<LDSD>(c, sdesc, static_cast<int>(info[u].w));
@@ -246,6 +285,9 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
             tw[u] = WEIGHTED && (d.flags & TD_WEIGHTED);
             // unconditional (an idle slot reads the first row of the weights)
             w_old[u] = ldg(reinterpret_cast<const Pack<WT, VEC>*>(act ? wrow[u] : weights));
+            Dr[u] = d.D;
+            if (OPT == kAdagrad)   // every lane of the worker: the state feeds all of them
+                s_old[u] = ldg(c.state + (info[u].z > 0 ? info[u].x : 0u));
 #pragma unroll
             for (int q = 0; q < VEC; ++q) acc[u][q] = ACC(0);
         }
@@ -254,11 +296,20 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
         // all S updates first, then the stores (a wait for one row's old
         // value never includes another row's store)
         Pack<WT, VEC> o[S];
+        float s_new[S];
 #pragma unroll
-        for (int u = 0; u < S; ++u) o[u] = sgd_row<WT, ACC, VEC>(w_old[u], acc[u], c.lr);
+        for (int u = 0; u < S; ++u) {
+            if (OPT == kAdagrad)
+                o[u] = adagrad_row<WT, ACC, VEC>(w_old[u], acc[u], s_old[u], Dr[u], L, c.lr,
+                                                 c.eps, s_new[u]);
+            else
+                o[u] = sgd_row<WT, ACC, VEC>(w_old[u], acc[u], c.lr);
+        }
 #pragma unroll
-        for (int u = 0; u < S; ++u)
+        for (int u = 0; u < S; ++u) {
             if (gcol[u]) *reinterpret_cast<Pack<WT, VEC>*>(wrow[u]) = o[u];
+            if (OPT == kAdagrad && sub == 0 && info[u].z > 0) c.state[info[u].x] = s_new[u];
+        }
     }
 }
 
@@ -271,7 +322,7 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
 // tau is raised) and fp16 tables use the ACC type.
 constexpr uint32_t kF32Run = 256;
 
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD>
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD, int OPT>
 __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ weights,
                                            const TableDesc* sdesc, uint32_t wave, uint32_t nwaves)
 {
@@ -317,11 +368,11 @@ __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ we
             maxlen = max(maxlen, info[u].z);
         }
         if (sizeof(ACC) == 8 && maxlen < kF32Run)
-            short_batch<WT, float, VEC, S, U, WEIGHTED, LDSD>(c, weights, sdesc, info, first, sub,
-                                                              L, gbase);
+            short_batch<WT, float, VEC, S, U, WEIGHTED, LDSD, OPT>(c, weights, sdesc, info, first,
+                                                                   sub, L, gbase);
         else
-            short_batch<WT, ACC, VEC, S, U, WEIGHTED, LDSD>(c, weights, sdesc, info, first, sub, L,
-                                                            gbase);
+            short_batch<WT, ACC, VEC, S, U, WEIGHTED, LDSD, OPT>(c, weights, sdesc, info, first,
+                                                                 sub, L, gbase);
     }
 }
 
@@ -378,8 +429,10 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
 
 // Long runs, step 2 (next launch, so every partial is visible without a
 // device-wide cache flush): one worker per long run adds its chunks'
-// partials in chunk order -- 8 loads in flight -- and applies SGD.
-template <typename WT, typename ACC, int VEC>
+// partials in chunk order -- 8 loads in flight -- and applies the update.
+// Row-wise Adagrad: one slab per row, and lanes past the row's D keep zeros
+// so the whole worker takes part in the sum of squares.
+template <typename WT, typename ACC, int VEC, int OPT>
 __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict__ weights,
                                                       const ACC* __restrict__ partials)
 {
@@ -398,6 +451,36 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
         WT* __restrict__ wrow = weights + d.w_off + static_cast<int64_t>(li.x - d.hash_off) * d.D;
         const uint32_t nq = (li.z + c.chunk - 1) / c.chunk;
         const uint32_t qend = min(li.w + nq, c.max_chunks);
+        if (OPT == kAdagrad) {
+            const int col = sub * VEC;
+            const bool act = col < d.D;
+            const int cc = act ? col : 0;
+            const Pack<WT, VEC> w_old = ldg(reinterpret_cast<const Pack<WT, VEC>*>(wrow + cc));
+            const float s_old = ldg(c.state + li.x);
+            ACC acc[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) acc[j] = ACC(0);
+            for (uint32_t qq = li.w; qq < qend; qq += 8) {
+                Pack<ACC, VEC> part[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const uint32_t qm = qq + m < qend ? qq + m : qend - 1;
+                    part[m] = ldg(reinterpret_cast<const Pack<ACC, VEC>*>(
+                        partials + static_cast<int64_t>(qm) * c.max_D + cc));
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    if (act && qq + m < qend)
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) acc[j] += part[m].v[j];
+            }
+            float s_new;
+            const Pack<WT, VEC> o = adagrad_row<WT, ACC, VEC>(w_old, acc, s_old, d.D,
+                                                              1 << c.lpr_log2, c.lr, c.eps, s_new);
+            if (act) *reinterpret_cast<Pack<WT, VEC>*>(wrow + col) = o;
+            if (sub == 0) c.state[li.x] = s_new;
+            continue;
+        }
         for (int c0 = 0; c0 < d.D; c0 += (VEC << c.lpr_log2)) {
             const int col = c0 + sub * VEC;
             if (col >= d.D) continue;
@@ -426,7 +509,7 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
 
 constexpr int kLdsTables = 256;   // table descriptors staged in LDS
 
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED>
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, int OPT>
 __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ weights,
                                                  ACC* __restrict__ partials)
 {
@@ -438,9 +521,9 @@ __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ wei
         if (c.T <= kLdsTables) {
             for (int i = threadIdx.x; i < c.T; i += 256) sdesc[i] = ldg(c.tables + i);
             __syncthreads();
-            short_runs<WT, ACC, VEC, S, U, WEIGHTED, true>(c, weights, sdesc, wave, nwaves);
+            short_runs<WT, ACC, VEC, S, U, WEIGHTED, true, OPT>(c, weights, sdesc, wave, nwaves);
         } else {
-            short_runs<WT, ACC, VEC, S, U, WEIGHTED, false>(c, weights, sdesc, wave, nwaves);
+            short_runs<WT, ACC, VEC, S, U, WEIGHTED, false, OPT>(c, weights, sdesc, wave, nwaves);
         }
     }
     else
@@ -456,18 +539,18 @@ uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
     return static_cast<uint32_t>(b);
 }
 
-template <typename WT, typename ACC, int VEC, int S, int U>
+template <typename WT, typename ACC, int VEC, int S, int U, int OPT>
 void launch_seg(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
 {
     if (a.payload_pairs)
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true>), grid, dim3(256), 0, a.stream, c,
-                           w, partials);
+        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true, OPT>), grid, dim3(256), 0,
+                           a.stream, c, w, partials);
     else
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, false>), grid, dim3(256), 0, a.stream,
-                           c, w, partials);
+        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, false, OPT>), grid, dim3(256), 0,
+                           a.stream, c, w, partials);
 }
 
-template <typename WT, typename ACC, int VEC>
+template <typename WT, typename ACC, int VEC, int OPT>
 hipError_t launch_all(const BwdArgs& a, SegArgs c)
 {
     const BwdLayout& L = a.L;
@@ -482,27 +565,60 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     // short-run batches: S = 2 runs per worker, U = 4 gradient rows in flight
     // (measured best of S in {1,2,4,8} x U in {4,8} on the uniform, stress and
     // mixed workloads)
-    launch_seg<WT, ACC, VEC, 2, 4>(a, grid, c, w, partials);
+    launch_seg<WT, ACC, VEC, 2, 4, OPT>(a, grid, c, w, partials);
     stage_mark(a.plan, 4, a.stream);
-    hipLaunchKernelGGL((k_long_combine<WT, ACC, VEC>), dim3(b_long), dim3(256), 0, a.stream, c, w,
-                       static_cast<const ACC*>(partials));
+    hipLaunchKernelGGL((k_long_combine<WT, ACC, VEC, OPT>), dim3(b_long), dim3(256), 0, a.stream,
+                       c, w, static_cast<const ACC*>(partials));
     stage_mark(a.plan, 5, a.stream);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t run_segment_sgd(const BwdArgs& a)
+namespace {
+// Elements per lane of the segment kernels: the widest load every table's D,
+// grad_output and the weights allow.
+int segment_vec(const BwdArgs& a)
 {
     const tbe_plan* p = a.plan;
-    const BwdLayout& L = a.L;
-    if (L.N == 0) return hipSuccess;
     int vec = 4;
     for (int t = 0; t < p->T; ++t)
         while (p->dims[t] % vec) vec >>= 1;
     if (reinterpret_cast<uintptr_t>(a.grad) % (vec * 4)) vec = 1;
     const size_t wbytes = p->wdtype == TBE_F32 ? 4 : 2;
     while (vec > 1 && reinterpret_cast<uintptr_t>(a.weights) % (vec * wbytes)) vec >>= 1;
+    return vec;
+}
+
+template <int OPT>
+hipError_t dispatch_segment(const BwdArgs& a, const SegArgs& c, int vec)
+{
+    if (a.plan->wdtype == TBE_F32) {
+        switch (vec) {
+        case 4: return launch_all<float, double, 4, OPT>(a, c);
+        case 2: return launch_all<float, double, 2, OPT>(a, c);
+        default: return launch_all<float, double, 1, OPT>(a, c);
+        }
+    }
+    switch (vec) {
+    case 4: return launch_all<_Float16, float, 4, OPT>(a, c);
+    case 2: return launch_all<_Float16, float, 2, OPT>(a, c);
+    default: return launch_all<_Float16, float, 1, OPT>(a, c);
+    }
+}
+}  // namespace
+
+bool adagrad_supported(const BwdArgs& a)
+{
+    return (a.plan->max_D + segment_vec(a) - 1) / segment_vec(a) <= 64;
+}
+
+hipError_t run_segment_sgd(const BwdArgs& a)
+{
+    const tbe_plan* p = a.plan;
+    const BwdLayout& L = a.L;
+    if (L.N == 0) return hipSuccess;
+    const int vec = segment_vec(a);
     const int lanes = (p->max_D + vec - 1) / vec;
     int lpr_log2 = 0;
     while ((1 << lpr_log2) < lanes && lpr_log2 < 6) ++lpr_log2;
@@ -525,19 +641,11 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.max_chunks = static_cast<uint32_t>(L.max_chunks);
     c.max_long = static_cast<uint32_t>(L.max_long);
     c.lr = a.lr;
+    c.eps = a.eps;
+    c.state = a.state;
     c.short_blocks = 0;
-    if (p->wdtype == TBE_F32) {
-        switch (vec) {
-        case 4: return launch_all<float, double, 4>(a, c);
-        case 2: return launch_all<float, double, 2>(a, c);
-        default: return launch_all<float, double, 1>(a, c);
-        }
-    }
-    switch (vec) {
-    case 4: return launch_all<_Float16, float, 4>(a, c);
-    case 2: return launch_all<_Float16, float, 2>(a, c);
-    default: return launch_all<_Float16, float, 1>(a, c);
-    }
+    if (a.state) return dispatch_segment<kAdagrad>(a, c, vec);
+    return dispatch_segment<kSgd>(a, c, vec);
 }
 
 }  // namespace tbe

@@ -237,6 +237,8 @@ static tbe_status prepare_bwd(const tbe_plan* p, int32_t B, const void* indices,
     a.grad = nullptr;
     a.weights = nullptr;
     a.lr = 0.f;
+    a.state = nullptr;
+    a.eps = 0.f;
     a.ws = static_cast<char*>(workspace);
     a.L = bwd_layout(p, B, num_indices);
     a.stream = static_cast<hipStream_t>(stream);
@@ -263,9 +265,25 @@ tbe_status tbe_backward_prepare(const tbe_plan* p, int32_t B, const void* indice
     return st;
 }
 
-tbe_status tbe_backward_apply(const tbe_plan* p, int32_t B, int64_t num_indices, int32_t weighted,
-                              void* weights, const float* grad_output, float lr,
-                              void* workspace, size_t workspace_bytes, void* stream)
+// The update's own arguments: SGD (state == nullptr) or row-wise Adagrad.
+static tbe_status set_update(BwdArgs& a, void* weights, const float* grad_output, float lr,
+                             float* state, float eps, bool adagrad)
+{
+    if (!weights || !grad_output) return TBE_EINVAL;
+    a.grad = grad_output;
+    a.weights = weights;
+    a.lr = lr;
+    if (!adagrad) return TBE_OK;
+    if (!state || (reinterpret_cast<uintptr_t>(state) & 3) || !(eps >= 0.f)) return TBE_EINVAL;
+    a.state = state;
+    a.eps = eps;
+    return adagrad_supported(a) ? TBE_OK : TBE_ENOTSUP;
+}
+
+static tbe_status apply_half(const tbe_plan* p, int32_t B, int64_t num_indices, int32_t weighted,
+                             void* weights, float* state, const float* grad_output, float lr,
+                             float eps, bool adagrad, void* workspace, size_t workspace_bytes,
+                             void* stream)
 {
     if (p && B == 0 && num_indices >= 0) return TBE_OK;
     BwdArgs a;
@@ -273,11 +291,9 @@ tbe_status tbe_backward_apply(const tbe_plan* p, int32_t B, int64_t num_indices,
     tbe_status st = prepare_bwd(p, B, workspace, num_indices, workspace, workspace,
                                 workspace_bytes, stream, a);
     if (st != TBE_OK) return st;
-    if (!weights || !grad_output) return TBE_EINVAL;
+    st = set_update(a, weights, grad_output, lr, state, eps, adagrad);
+    if (st != TBE_OK) return st;
     if (num_indices == 0) return TBE_OK;
-    a.grad = grad_output;
-    a.weights = weights;
-    a.lr = lr;
     a.final_buf = a.L.npasses & 1;   // each radix pass swaps the ping-pong buffers
     a.payload_pairs = weighted != 0;
     st = run_segment_sgd(a) == hipSuccess ? TBE_OK : TBE_EHIP;
@@ -285,28 +301,62 @@ tbe_status tbe_backward_apply(const tbe_plan* p, int32_t B, int64_t num_indices,
     return st;
 }
 
-tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const void* indices,
-                            int64_t num_indices, const void* offsets, const float* psw,
-                            const float* grad_output, float lr, void* workspace,
-                            size_t workspace_bytes, void* stream)
+static tbe_status backward_whole(const tbe_plan* p, int32_t B, void* weights, float* state,
+                                 const void* indices, int64_t num_indices, const void* offsets,
+                                 const float* psw, const float* grad_output, float lr, float eps,
+                                 bool adagrad, void* workspace, size_t workspace_bytes,
+                                 void* stream)
 {
     if (p && B == 0 && num_indices >= 0) return TBE_OK;
     BwdArgs a;
     tbe_status st = prepare_bwd(p, B, indices, num_indices, offsets, workspace,
                                 workspace_bytes, stream, a);
     if (st != TBE_OK) return st;
-    if (!weights || !grad_output) return TBE_EINVAL;
+    st = set_update(a, weights, grad_output, lr, state, eps, adagrad);
+    if (st != TBE_OK) return st;
     if (num_indices == 0) return TBE_OK;
     a.psw = psw;
-    a.grad = grad_output;
-    a.weights = weights;
-    a.lr = lr;
     stage_mark(p, 0, a.stream);
     tbe_status st2 = TBE_OK;
     if (run_sort_rle(a, false) != hipSuccess) st2 = TBE_EHIP;
     else if (run_segment_sgd(a) != hipSuccess) st2 = TBE_EHIP;
     const_cast<tbe_plan*>(p)->n_stage_ev = 0;
     return st2;
+}
+
+tbe_status tbe_backward_apply(const tbe_plan* p, int32_t B, int64_t num_indices, int32_t weighted,
+                              void* weights, const float* grad_output, float lr,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    return apply_half(p, B, num_indices, weighted, weights, nullptr, grad_output, lr, 0.f, false,
+                      workspace, workspace_bytes, stream);
+}
+
+tbe_status tbe_backward_apply_adagrad(const tbe_plan* p, int32_t B, int64_t num_indices,
+                                      int32_t weighted, void* weights, float* state,
+                                      const float* grad_output, float lr, float eps,
+                                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    return apply_half(p, B, num_indices, weighted, weights, state, grad_output, lr, eps, true,
+                      workspace, workspace_bytes, stream);
+}
+
+tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const void* indices,
+                            int64_t num_indices, const void* offsets, const float* psw,
+                            const float* grad_output, float lr, void* workspace,
+                            size_t workspace_bytes, void* stream)
+{
+    return backward_whole(p, B, weights, nullptr, indices, num_indices, offsets, psw, grad_output,
+                          lr, 0.f, false, workspace, workspace_bytes, stream);
+}
+
+tbe_status tbe_backward_adagrad(const tbe_plan* p, int32_t B, void* weights, float* state,
+                                const void* indices, int64_t num_indices, const void* offsets,
+                                const float* psw, const float* grad_output, float lr, float eps,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    return backward_whole(p, B, weights, state, indices, num_indices, offsets, psw, grad_output,
+                          lr, eps, true, workspace, workspace_bytes, stream);
 }
 
 tbe_status tbe_sort_rle(const tbe_plan* p, int32_t B, const void* indices, int64_t num_indices,

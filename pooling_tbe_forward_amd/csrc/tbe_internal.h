@@ -126,6 +126,10 @@ struct BwdArgs {
     const float* grad;
     void* weights;
     float lr;
+    // row-wise Adagrad (state != nullptr): one fp32 state value per row,
+    // indexed by the row's key; eps is added after the square root
+    float* state;
+    float eps;
     char* ws;
     BwdLayout L;
     hipStream_t stream;
@@ -136,7 +140,13 @@ struct BwdArgs {
 };
 // api_outputs: also write unique keys, run starts / lengths and run-id lists.
 hipError_t run_sort_rle(BwdArgs& a, bool api_outputs);
+// Segment reduce and the row update: exact SGD, or row-wise Adagrad when
+// a.state is set (then every table must fit one worker slab: see
+// adagrad_supported).
 hipError_t run_segment_sgd(const BwdArgs& a);
+// Whether the row-wise Adagrad kernels cover this plan and buffers: the
+// update needs a row's whole sum of squares inside one worker.
+bool adagrad_supported(const BwdArgs& a);
 
 // Record stage event k of the next call, if the caller asked for it.
 inline void stage_mark(const tbe_plan* p, int k, hipStream_t s)

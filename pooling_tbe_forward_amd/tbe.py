@@ -66,6 +66,11 @@ def lib():
         L.tbe_backward_prepare.restype = I32
         L.tbe_backward_apply.argtypes = [P, I32, I64, I32, P, P, ctypes.c_float, P, SZ, P]
         L.tbe_backward_apply.restype = I32
+        F = ctypes.c_float
+        L.tbe_backward_adagrad.argtypes = [P, I32, P, P, P, I64, P, P, P, F, F, P, SZ, P]
+        L.tbe_backward_adagrad.restype = I32
+        L.tbe_backward_apply_adagrad.argtypes = [P, I32, I64, I32, P, P, P, F, F, P, SZ, P]
+        L.tbe_backward_apply_adagrad.restype = I32
         L.tbe_sort_rle.argtypes = [P, I32, P, I64, P, P, SZ, ctypes.POINTER(tbe_sort_view), P]
         L.tbe_sort_rle.restype = I32
         L.tbe_set_stage_events.argtypes = [P, ctypes.POINTER(ctypes.c_void_p), I32]
@@ -248,6 +253,35 @@ def tbe_backward_apply(plan: Plan, B: int, num_indices: int, weighted: bool, wei
                                     _ptr(weights), _ptr(grad_output), float(lr), _ptr(workspace),
                                     int(workspace.numel() * workspace.element_size()),
                                     _stream(stream)), "tbe_backward_apply")
+    return weights
+
+
+ADAGRAD_EPS = 1e-8   # the pages give no value for eps
+
+
+def tbe_backward_adagrad(plan: Plan, B: int, weights, state, indices, offsets,
+                         per_sample_weights, grad_output, lr: float, workspace,
+                         eps: float = ADAGRAD_EPS, stream=None):
+    """Backward + exact row-wise Adagrad in place; ``state`` is the fp32 row
+    state, one value per row of every table (indexed by the row's key)."""
+    _check(lib().tbe_backward_adagrad(plan.handle, int(B), _ptr(weights), _ptr(state),
+                                      _ptr(indices), int(indices.numel()), _ptr(offsets),
+                                      _ptr(per_sample_weights), _ptr(grad_output), float(lr),
+                                      float(eps), _ptr(workspace),
+                                      int(workspace.numel() * workspace.element_size()),
+                                      _stream(stream)), "tbe_backward_adagrad")
+    return weights
+
+
+def tbe_backward_apply_adagrad(plan: Plan, B: int, num_indices: int, weighted: bool, weights,
+                               state, grad_output, lr: float, workspace,
+                               eps: float = ADAGRAD_EPS, stream=None):
+    _check(lib().tbe_backward_apply_adagrad(plan.handle, int(B), int(num_indices),
+                                            1 if weighted else 0, _ptr(weights), _ptr(state),
+                                            _ptr(grad_output), float(lr), float(eps),
+                                            _ptr(workspace),
+                                            int(workspace.numel() * workspace.element_size()),
+                                            _stream(stream)), "tbe_backward_apply_adagrad")
     return weights
 
 

@@ -58,6 +58,10 @@ def test_null_plan_calls():
     assert L.tbe_set_stage_events(None, None, 0) == tbe.TBE_EINVAL
     assert L.tbe_backward_prepare(None, 1, None, 0, None, None, None, 0, None) == tbe.TBE_EINVAL
     assert L.tbe_backward_apply(None, 1, 0, 0, None, None, 0.1, None, 0, None) == tbe.TBE_EINVAL
+    assert L.tbe_backward_adagrad(None, 1, None, None, None, 0, None, None, None, 0.1, 1e-8,
+                                  None, 0, None) == tbe.TBE_EINVAL
+    assert L.tbe_backward_apply_adagrad(None, 1, 0, 0, None, None, None, 0.1, 1e-8, None, 0,
+                                        None) == tbe.TBE_EINVAL
     L.tbe_plan_destroy(None)
 
 
