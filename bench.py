@@ -60,6 +60,8 @@ WORKLOAD_DESC = {
     "hist": "small-table TBE: T=1 x 64 rows, D=128 fp16, B=16384, 256 ids per bag",
     "stress": "run-length stress TBE: T=4 x 1,000,000 rows, D=128 fp32, B=8192, 50 Zipf(1.2) "
               "ids per bag, weighted",
+    "band": "band-planted TBE: the run-length stress shape with every touched row read "
+            "32..255 times (uniform), weighted",
     "toy": "toy TBE: T=3, rows {100,50,20}, D {8,16,4}, B=4",
 }
 BWD_STAGES = ["keys", "radix_sort", "rle", "segment_sgd", "long_combine"]
@@ -433,7 +435,7 @@ def hist_mfma_flops(wl):
 
 def report_configs(steps, warmup, hip):
     import torch
-    for name in ("uniform", "mixed", "hist", "stress"):
+    for name in ("uniform", "mixed", "hist", "stress", "band"):
         wl = Workload(name, nbatches=3 if name != "mixed" else 2)
         r = run_steps(wl, steps, warmup, hip)
         r2 = run_steps(wl, steps, warmup, hip, overlap=True)

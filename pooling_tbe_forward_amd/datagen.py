@@ -63,6 +63,11 @@ CONFIGS = {
     "stress": dict(seed=104, T=4, B=8192, rows=[1_000_000] * 4, dims=[128] * 4,
                    wdtype="f32", wdist=("normal", 0.01), lengths=("const", 50),
                    ids=("zipf", 1.2), weighted="all", lr=0.1),
+    # The stress shape with every touched row read a number of times uniform
+    # in 32..255 (the band where the pages' threshold result sits).
+    "band": dict(seed=105, T=4, B=8192, rows=[1_000_000] * 4, dims=[128] * 4,
+                 wdtype="f32", wdist=("normal", 0.01), lengths=("const", 50),
+                 ids=("band", 32, 255), weighted="all", lr=0.1),
 }
 
 
@@ -247,6 +252,20 @@ def _zipf_bounded(rng, a: float, R: int, n: int) -> np.ndarray:
     return out
 
 
+def _band_ids(rng, lo: int, hi: int, R: int, n: int) -> np.ndarray:
+    """n ids in which every id used is read a number of times drawn uniformly
+    from lo..hi (the last one is cut to fill exactly n), in random order."""
+    counts = []
+    total = 0
+    while total < n:
+        c = int(rng.integers(lo, hi + 1))
+        c = min(c, n - total)
+        counts.append(c)
+        total += c
+    rows = rng.choice(R, size=len(counts), replace=False).astype(np.int64)
+    return rng.permutation(np.repeat(rows, counts))
+
+
 def _rng(seed: int, batch: int, *key):
     """Stream for one purpose; batch 0 keeps the base streams, other batches
     draw fresh lengths / ids / weights / gradients over the same tables."""
@@ -312,6 +331,8 @@ def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
             it = rng3.integers(0, R, size=n_t, dtype=np.int64)
         elif isinstance(cfg["ids"], tuple) and cfg["ids"][0] == "zipf":
             it = _zipf_bounded(rng3, float(cfg["ids"][1]), R, n_t)
+        elif isinstance(cfg["ids"], tuple) and cfg["ids"][0] == "band":
+            it = _band_ids(rng3, int(cfg["ids"][1]), int(cfg["ids"][2]), R, n_t)
         else:
             raise ValueError(cfg["ids"])
         if cfg.get("force_toy") and t == 0 and n_t >= 2:

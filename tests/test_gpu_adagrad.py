@@ -127,7 +127,8 @@ def test_toy_adagrad_vs_oracle(seed, weighted, tau):
 
 
 @pytest.mark.parametrize("name,B,tau", [("uniform", 256, 256), ("stress", 256, 16),
-                                        ("mixed", 64, 256), ("hist", 64, 256)])
+                                        ("mixed", 64, 256), ("hist", 64, 256),
+                                        ("band", 512, 64)])
 def test_reduced_adagrad_vs_oracle(name, B, tau):
     prob = dg.make_problem(name, seed=700 + B, B=B)
     state0 = _state0(prob, 7, scale=0.5)
@@ -140,7 +141,7 @@ def test_reduced_adagrad_vs_oracle(name, B, tau):
     _untouched(prob, w_dev, s_dev, state0, o["unique_keys"])
 
 
-@pytest.mark.parametrize("name", ["stress", "uniform", "mixed"])
+@pytest.mark.parametrize("name", ["stress", "uniform", "mixed", "band"])
 def test_full_size_adagrad_sampled(name):
     prob = dg.make_problem(name)
     state0 = _state0(prob, 9)

@@ -88,7 +88,7 @@ def test_sort_rle_vs_oracle(name, B, seed, tau):
     _compare_sort(g, o, prob.N)
 
 
-@pytest.mark.parametrize("name", ["uniform", "stress", "mixed"])
+@pytest.mark.parametrize("name", ["uniform", "stress", "mixed", "band"])
 def test_sort_rle_full_size(name):
     prob = dg.make_problem(name)
     g = gpu_sort(prob, tau=256)
@@ -213,7 +213,8 @@ def _untouched_check(prob, w_dev, o, n=2000, seed=1):
 
 @pytest.mark.parametrize("name,B,tau", [("uniform", 256, 256), ("stress", 256, 256),
                                         ("stress", 256, 16), ("mixed", 64, 256),
-                                        ("hist", 64, 256)])
+                                        ("hist", 64, 256), ("band", 512, 64),
+                                        ("band", 512, 256)])
 def test_reduced_backward_vs_oracle(name, B, tau):
     prob = dg.make_problem(name, seed=600 + B, B=B)
     w_dev = dg.packed_weights_torch(prob, "cuda")
@@ -225,7 +226,7 @@ def test_reduced_backward_vs_oracle(name, B, tau):
     _untouched_check(prob, w_dev, o)
 
 
-@pytest.mark.parametrize("name", ["stress", "uniform", "mixed"])
+@pytest.mark.parametrize("name", ["stress", "uniform", "mixed", "band"])
 def test_full_size_backward_sampled(name):
     prob = dg.make_problem(name)
     w_dev = dg.packed_weights_torch(prob, "cuda")
