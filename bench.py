@@ -62,6 +62,8 @@ WORKLOAD_DESC = {
               "ids per bag, weighted",
     "band": "band-planted TBE: the run-length stress shape with every touched row read "
             "32..255 times (uniform), weighted",
+    "prod": "production-scale TBE: T=32 x 100,000 rows, D=128 fp16, B=131,072, Poisson(20) "
+            "bags (83.9M lookups, 3.0M distinct rows), Zipf(1.05) ids, unweighted",
     "toy": "toy TBE: T=3, rows {100,50,20}, D {8,16,4}, B=4",
 }
 BWD_STAGES = ["keys", "radix_sort", "rle", "segment_sgd", "long_combine"]
@@ -435,8 +437,8 @@ def hist_mfma_flops(wl):
 
 def report_configs(steps, warmup, hip):
     import torch
-    for name in ("uniform", "mixed", "hist", "stress", "band"):
-        wl = Workload(name, nbatches=3 if name != "mixed" else 2)
+    for name in ("uniform", "mixed", "hist", "stress", "band", "prod"):
+        wl = Workload(name, nbatches={"mixed": 2, "prod": 1}.get(name, 3))
         r = run_steps(wl, steps, warmup, hip)
         r2 = run_steps(wl, steps, warmup, hip, overlap=True)
         r3 = run_graph_steps(wl, capture_steps(wl), steps, warmup)

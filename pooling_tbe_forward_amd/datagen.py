@@ -68,6 +68,12 @@ CONFIGS = {
     "band": dict(seed=105, T=4, B=8192, rows=[1_000_000] * 4, dims=[128] * 4,
                  wdtype="f32", wdist=("normal", 0.01), lengths=("const", 50),
                  ids=("band", 32, 255), weighted="all", lr=0.1),
+    # Production-scale batch shaped like the statistics the pages quote (about
+    # 4.2M bags, B = 128K, ~20 ids per bag, ~3M distinct rows, one row read
+    # ~1e5 times): 32 features of 100K rows, D=128 fp16, Zipf(1.05) ids.
+    "prod": dict(seed=106, T=32, B=131072, rows=[100_000] * 32, dims=[128] * 32,
+                 wdtype="f16", wdist=("normal", 0.01), lengths=("poisson", 20.0),
+                 ids=("zipf_cdf", 1.05), weighted="none", lr=0.1),
 }
 
 
@@ -252,6 +258,15 @@ def _zipf_bounded(rng, a: float, R: int, n: int) -> np.ndarray:
     return out
 
 
+def _zipf_cdf(rng, a: float, R: int, n: int) -> np.ndarray:
+    """n draws of the Zipf(a) law bounded to ranks 1..R, by inverting its
+    cumulative distribution (p_k proportional to k^-a), minus one: the same
+    law as _zipf_bounded, drawn without rejection (for very large n)."""
+    cdf = np.cumsum(np.arange(1, R + 1, dtype=np.float64) ** -a)
+    u = rng.random(n) * cdf[-1]
+    return np.minimum(np.searchsorted(cdf, u, side="right"), R - 1).astype(np.int64)
+
+
 def _band_ids(rng, lo: int, hi: int, R: int, n: int) -> np.ndarray:
     """n ids in which every id used is read a number of times drawn uniformly
     from lo..hi (the last one is cut to fill exactly n), in random order."""
@@ -331,6 +346,8 @@ def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
             it = rng3.integers(0, R, size=n_t, dtype=np.int64)
         elif isinstance(cfg["ids"], tuple) and cfg["ids"][0] == "zipf":
             it = _zipf_bounded(rng3, float(cfg["ids"][1]), R, n_t)
+        elif isinstance(cfg["ids"], tuple) and cfg["ids"][0] == "zipf_cdf":
+            it = _zipf_cdf(rng3, float(cfg["ids"][1]), R, n_t)
         elif isinstance(cfg["ids"], tuple) and cfg["ids"][0] == "band":
             it = _band_ids(rng3, int(cfg["ids"][1]), int(cfg["ids"][2]), R, n_t)
         else:
