@@ -25,6 +25,7 @@ _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, F16 = 0, 1
+POOLING = {"sum": 0, "mean": 1}
 
 
 def build(force: bool = False) -> str:
@@ -52,16 +53,16 @@ def lib():
         P = ctypes.c_void_p
         L.oracle_layout.argtypes = [ctypes.c_int32, P, P, P, P, P]
         L.oracle_forward.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
-                                     P, P, P, P, P, P, ctypes.c_int64, P]
+                                     P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_int32]
         L.oracle_sort_rle.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_int64,
                                       P, P, P, P, P, P, P, P, P, P]
         L.oracle_backward_sgd.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
                                           P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_int64,
-                                          P, P, ctypes.c_int32]
+                                          P, P, ctypes.c_int32, ctypes.c_int32]
         L.oracle_backward_adagrad.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P,
                                               ctypes.c_int32, P, P, P, P, P, P, ctypes.c_float,
                                               ctypes.c_float, P, ctypes.c_int64, P, P, P, P,
-                                              ctypes.c_int32]
+                                              ctypes.c_int32, ctypes.c_int32]
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
         L.oracle_double_to_half.argtypes = [ctypes.c_double]
@@ -130,8 +131,9 @@ def dense_tables(packed, rows, dims):
 
 
 def forward(T, B, rows, dims, wdtype, tables, indices, offsets, psw=None,
-            weighted=None, bag_list=None):
-    """Pooled forward in float64.  Returns [B, sum D], or [len(bag_list), Dmax]."""
+            weighted=None, bag_list=None, pooling="sum"):
+    """Pooled forward in float64 (pooling "sum" or "mean").  Returns
+    [B, sum D], or [len(bag_list), Dmax]."""
     rows = _i64(rows)
     dims = np.ascontiguousarray(dims, dtype=np.int32)
     indices = _i64(indices)
@@ -147,7 +149,8 @@ def forward(T, B, rows, dims, wdtype, tables, indices, offsets, psw=None,
         nb = bl.size
         out = np.zeros((nb, int(dims.max())), np.float64)
     _check(lib().oracle_forward(T, B, _p(rows), _p(dims), wdtype, ctypes.cast(tarr, ctypes.c_void_p),
-                                _p(indices), _p(offsets), _p(psw), _p(wm), _p(bl), nb, _p(out)))
+                                _p(indices), _p(offsets), _p(psw), _p(wm), _p(bl), nb, _p(out),
+                                POOLING[pooling]))
     del keep
     return out
 
@@ -176,7 +179,7 @@ def sort_rle(T, B, rows, indices, offsets, tau):
 
 
 def backward_sgd(T, B, rows, dims, wdtype, tables, indices, offsets, psw, weighted,
-                 grad_output, lr, keys, write_back=False):
+                 grad_output, lr, keys, write_back=False, pooling="sum"):
     """Finished row gradients and exact SGD rows (float64) for ``keys``.
 
     Returns (grad_rows [nkeys, Dmax], new_rows [nkeys, Dmax]).  With
@@ -196,13 +199,13 @@ def backward_sgd(T, B, rows, dims, wdtype, tables, indices, offsets, psw, weight
     _check(lib().oracle_backward_sgd(T, B, _p(rows), _p(dims), wdtype,
                                      ctypes.cast(tarr, ctypes.c_void_p), _p(indices), _p(offsets),
                                      _p(psw), _p(wm), _p(g), float(lr), _p(keys), keys.size,
-                                     _p(gr), _p(nr), 1 if write_back else 0))
+                                     _p(gr), _p(nr), 1 if write_back else 0, POOLING[pooling]))
     del keep
     return gr, nr
 
 
 def backward_adagrad(T, B, rows, dims, wdtype, tables, indices, offsets, psw, weighted,
-                      grad_output, lr, eps, keys, state_in, write_back=False):
+                      grad_output, lr, eps, keys, state_in, write_back=False, pooling="sum"):
     """Finished row gradients, exact row-wise Adagrad rows (float64) and the
     rows' new fp32 state for ``keys``; ``state_in`` is the state of each
     key's row before the step.
@@ -230,7 +233,8 @@ def backward_adagrad(T, B, rows, dims, wdtype, tables, indices, offsets, psw, we
                                          ctypes.cast(tarr, ctypes.c_void_p), _p(indices),
                                          _p(offsets), _p(psw), _p(wm), _p(g), float(lr),
                                          float(eps), _p(keys), keys.size, _p(s_in), _p(s_out),
-                                         _p(gr), _p(nr), 1 if write_back else 0))
+                                         _p(gr), _p(nr), 1 if write_back else 0,
+                                         POOLING[pooling]))
     del keep
     return gr, nr, s_out
 

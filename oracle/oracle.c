@@ -129,12 +129,13 @@ static int check_inputs(int32_t T, int32_t B, const int64_t* rows,
 }
 
 /* ---------------------------------------------------------------------- */
-/* Forward: pooled sum of each bag, written at the table's column offset. */
+/* Forward: pooled sum of each bag (pooling 1: the sum divided by the bag's
+ * length; an empty bag stays zero), written at the table's column offset. */
 int oracle_forward(int32_t T, int32_t B, const int64_t* rows, const int32_t* dims,
                    int32_t wdtype, const oracle_table* tables,
                    const int64_t* indices, const int64_t* offsets,
                    const float* psw, const uint8_t* weighted,
-                   const int64_t* bag_list, int64_t nbags, double* out)
+                   const int64_t* bag_list, int64_t nbags, double* out, int32_t pooling)
 {
     int rc = check_inputs(T, B, rows, indices, offsets);
     if (rc) return rc;
@@ -164,6 +165,10 @@ int oracle_forward(int32_t T, int32_t B, const int64_t* rows, const int32_t* dim
             for (int32_t d = 0; d < D; ++d)
                 dst[d] += w * load_elem(tables[t].data, pos * D + d, wdtype);
         }
+        int64_t len = offsets[bag + 1] - offsets[bag];
+        if (pooling == ORACLE_POOL_MEAN && len > 0)
+            for (int32_t d = 0; d < D; ++d)
+                dst[d] /= (double)len;
     }
     free(Doff);
     return 0;
@@ -250,14 +255,16 @@ int oracle_sort_rle(int32_t T, int32_t B, const int64_t* rows,
 /* ---------------------------------------------------------------------- */
 /* Backward + exact SGD for the requested rows: G = sum over lookups j of the
  * row of w_j * grad_output[b(j), D_offsets[t] : +D_t], accumulated in lookup
- * order; new = W[r] - lr * G. */
+ * order (pooling 1: w_j divided by the length of j's bag, the derivative of
+ * the mean); new = W[r] - lr * G. */
 int oracle_backward_sgd(int32_t T, int32_t B, const int64_t* rows, const int32_t* dims,
                         int32_t wdtype, oracle_table* tables,
                         const int64_t* indices, const int64_t* offsets,
                         const float* psw, const uint8_t* weighted,
                         const float* grad_output, float lr,
                         const int64_t* keys, int64_t nkeys,
-                        double* grad_rows, double* new_rows, int32_t write_back)
+                        double* grad_rows, double* new_rows, int32_t write_back,
+                        int32_t pooling)
 {
     int rc = check_inputs(T, B, rows, indices, offsets);
     if (rc) return rc;
@@ -290,6 +297,8 @@ int oracle_backward_sgd(int32_t T, int32_t B, const int64_t* rows, const int32_t
                 if (lo >= nkeys || keys[lo] != key)
                     continue;
                 double w = (psw && (!weighted || weighted[t])) ? (double)psw[j] : 1.0;
+                if (pooling == ORACLE_POOL_MEAN)
+                    w /= (double)(offsets[bag + 1] - offsets[bag]);
                 const float* g = grad_output + b * sumD + Doff[t];
                 double* acc = G + lo * Dmax;
                 for (int32_t d = 0; d < D; ++d)
@@ -338,7 +347,8 @@ int oracle_backward_adagrad(int32_t T, int32_t B, const int64_t* rows, const int
                             const float* grad_output, float lr, float eps,
                             const int64_t* keys, int64_t nkeys,
                             const float* state_in, float* state_out,
-                            double* grad_rows, double* new_rows, int32_t write_back)
+                            double* grad_rows, double* new_rows, int32_t write_back,
+                            int32_t pooling)
 {
     if (nkeys > 0 && (!state_in || !state_out))
         return 1;
@@ -349,7 +359,7 @@ int oracle_backward_adagrad(int32_t T, int32_t B, const int64_t* rows, const int
      * (lr = 0 there: nothing is written back, only G is wanted) */
     double* G = (double*)calloc((size_t)(nkeys ? nkeys : 1) * (Dmax ? Dmax : 1), sizeof(double));
     int rc = oracle_backward_sgd(T, B, rows, dims, wdtype, tables, indices, offsets, psw,
-                                 weighted, grad_output, 0.0f, keys, nkeys, G, NULL, 0);
+                                 weighted, grad_output, 0.0f, keys, nkeys, G, NULL, 0, pooling);
     if (rc) { free(G); return rc; }
     int64_t* hcs = (int64_t*)malloc(sizeof(int64_t) * (T + 1));
     oracle_layout(T, rows, dims, NULL, NULL, hcs);

@@ -14,14 +14,17 @@
  *    is indices[offsets[t*B+b] : offsets[t*B+b+1]]; its pooled vector is the
  *    (optionally per-sample-weighted) sum of the rows it names, written to
  *    output row b at table t's column offset; an empty bag pools to zero and
- *    a repeated id counts twice;
+ *    a repeated id counts twice; mean pooling (the same section gives the sum
+ *    as the usual pooling, so the mean is the other common mode) divides a
+ *    bag's sum by its length;
  *  - integer stage, section "Why the backward is the hard half": the key of a
  *    lookup is hash_size_cumsum[t] + row, keys are sorted (ties kept in lookup
  *    order), run-length encoded; section "Three tiers, routed by run length":
  *    runs are split into short (< tau) and long (>= tau) lists;
  *  - backward, section "Why the backward is the hard half": a read row's
  *    gradient is the sum of the output gradients of every bag that read it
- *    (times the per-sample weight), and exact SGD applies w <- w - lr * g once
+ *    (times the per-sample weight; with mean pooling, also divided by the
+ *    bag's length), and exact SGD applies w <- w - lr * g once
  *    the sum is finished; exact row-wise Adagrad (same section) keeps one
  *    fp32 state value per row, raises it by the row's mean squared gradient
  *    and steps the row by lr / (sqrt(state) + eps) times the gradient.
@@ -41,6 +44,9 @@ extern "C" {
 #endif
 
 enum { ORACLE_F32 = 0, ORACLE_F16 = 1 };
+/* Pooling of a bag: the (weighted) sum of its rows, or that sum divided by
+ * the bag's length (an empty bag pools to zero either way). */
+enum { ORACLE_POOL_SUM = 0, ORACLE_POOL_MEAN = 1 };
 
 /* Rows of one table held on the host.  ids == NULL: dense, row r is at
  * data + r*D.  Otherwise ids[0..n) is strictly ascending and row ids[i] is at
@@ -61,7 +67,7 @@ int oracle_forward(int32_t T, int32_t B, const int64_t* rows, const int32_t* dim
                    int32_t wdtype, const oracle_table* tables,
                    const int64_t* indices, const int64_t* offsets,
                    const float* psw, const uint8_t* weighted,
-                   const int64_t* bag_list, int64_t nbags, double* out);
+                   const int64_t* bag_list, int64_t nbags, double* out, int32_t pooling);
 
 /* Arrays are caller-allocated with N = offsets[T*B] entries each. */
 int oracle_sort_rle(int32_t T, int32_t B, const int64_t* rows,
@@ -81,7 +87,8 @@ int oracle_backward_sgd(int32_t T, int32_t B, const int64_t* rows, const int32_t
                         const float* psw, const uint8_t* weighted,
                         const float* grad_output, float lr,
                         const int64_t* keys, int64_t nkeys,
-                        double* grad_rows, double* new_rows, int32_t write_back);
+                        double* grad_rows, double* new_rows, int32_t write_back,
+                        int32_t pooling);
 
 /* Backward + exact row-wise Adagrad for keys[0..nkeys) (strictly ascending).
  * state_in[k] is the fp32 state of key k's row before the step, state_out[k]
@@ -96,7 +103,8 @@ int oracle_backward_adagrad(int32_t T, int32_t B, const int64_t* rows, const int
                             const float* grad_output, float lr, float eps,
                             const int64_t* keys, int64_t nkeys,
                             const float* state_in, float* state_out,
-                            double* grad_rows, double* new_rows, int32_t write_back);
+                            double* grad_rows, double* new_rows, int32_t write_back,
+                            int32_t pooling);
 
 /* IEEE binary16 helpers (exposed so the tests can pin them). */
 double   oracle_half_to_double(uint16_t h);
