@@ -21,7 +21,8 @@ uniform ids).  Prints ONE JSON line on stdout.
   duration is measured live inside the timed region.
 * The JSON line also carries "adagrad": the same steps with exact row-wise
   Adagrad in the backward (tbe_backward_adagrad, one fp32 state per row): the
-  eager step time, the backward's stage times and its segment kernel's rate.
+  eager step time, the backward's stage times and its segment kernel's rate;
+  and "mean_pooling": the SGD steps on a mean-pooled plan.
 * --report also prints one JSON line per configuration (uniform, mixed, hist,
   stress) with forward / backward stage times on stderr.
 * --calibrate-copy runs a 1 GiB device copy (for scaling rocprofv3 byte
@@ -305,6 +306,23 @@ def adagrad_summary(wl, steps, warmup, hip):
                 segment_pct_peak=round(100 * seg_gbps / PEAK_HBM_GBPS, 2))
 
 
+def mean_pooling_summary(wl, steps, warmup, hip):
+    """The same SGD steps on a mean-pooled plan (tbe_plan_set_pooling): plain
+    eager step time and the stage times of a run with stage events."""
+    from pooling_tbe_forward_amd import tbe
+    tbe.tbe_plan_set_pooling(wl.plan, "mean")
+    try:
+        r = run_steps(wl, steps, warmup, hip)
+        rp = run_plain_steps(wl, steps, warmup)
+    finally:
+        tbe.tbe_plan_set_pooling(wl.plan, "sum")
+    return dict(step_ms_eager=1e3 * rp["wall_s"] / steps,
+                lookups_per_s=float(np.sum(rp["lookups"])) / rp["wall_s"],
+                fwd_ms=float(np.mean(r["fwd_ms"])), bwd_ms=float(np.mean(r["bwd_ms"])),
+                bwd_stage_us={k: round(1e3 * float(v), 2)
+                              for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))})
+
+
 def capture_steps(wl):
     """One HIP graph per batch, each holding that batch's whole step (forward,
     then backward-SGD: the library's kernels only, no host work)."""
@@ -564,6 +582,7 @@ def main():
     r_graph = run_graph_steps(wl, capture_steps(wl), args.steps, args.warmup)
     r_eager = run_plain_steps(wl, args.steps, args.warmup)
     ada = adagrad_summary(wl, args.steps, args.warmup, hip)
+    mean = mean_pooling_summary(wl, args.steps, args.warmup, hip)
     r = dict(serial=r_serial, overlap=r_over, graph=r_graph, eager=r_eager)[args.schedule]
     step_ms = 1e3 * r["wall_s"] / args.steps
     lookups = float(np.sum(r["lookups"]))
@@ -593,7 +612,7 @@ def main():
                ms_per_step_eager=1e3 * r_eager["wall_s"] / args.steps,
                fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
                bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
-               roofline=roof, adagrad=ada)
+               roofline=roof, adagrad=ada, mean_pooling=mean)
     del wl
     torch.cuda.empty_cache()
     if args.report:

@@ -56,8 +56,9 @@ typedef enum {
 
 typedef enum { TBE_F32 = 0, TBE_F16 = 1 } tbe_fp;   /* weight storage type */
 typedef enum { TBE_I32 = 0, TBE_I64 = 1 } tbe_int;  /* applies to indices AND offsets */
+typedef enum { TBE_POOL_SUM = 0, TBE_POOL_MEAN = 1 } tbe_pooling;
 
-typedef struct tbe_plan tbe_plan;  /* opaque; immutable after create except tuning */
+typedef struct tbe_plan tbe_plan;  /* opaque; immutable after create except tuning and pooling */
 
 /* Launch knobs.  Defaults come from measurements on MI355X; tbe_set_tuning
  * exists for sweeps and for tests that force a path. */
@@ -238,6 +239,18 @@ tbe_status tbe_bounds_check(const tbe_plan* plan, int32_t B, const void* indices
 /* Read / replace the plan's launch knobs (values are validated). */
 tbe_status tbe_get_tuning(const tbe_plan* plan, tbe_tuning* tuning);
 tbe_status tbe_set_tuning(tbe_plan* plan, const tbe_tuning* tuning);
+
+/*
+ * Pooling of a bag (section "A lookup table that is most of the model" gives
+ * the sum as the usual pooling).  TBE_POOL_SUM (the default): the
+ * (per-sample-weighted) sum of the bag's rows.  TBE_POOL_MEAN: that sum
+ * divided by the bag's length; an empty bag still pools to zero.  The
+ * backward of a mean-pooled plan divides each lookup's contribution by the
+ * length of its bag.  Applies to every later call on the plan; mean-pooled
+ * plans do not take the histogram path.  Errors: TBE_EINVAL (NULL plan,
+ * unknown mode).
+ */
+tbe_status tbe_plan_set_pooling(tbe_plan* plan, int32_t pooling);
 
 /*
  * Optional per-stage timing, for profilers and benchmarks.  events: host array

@@ -84,6 +84,7 @@ struct SegArgs {
     uint32_t max_long;
     float lr;
     float eps;                 // row-wise Adagrad only
+    int32_t all_weighted;      // mean pooling: every table's payload weight applies
     float* state;              // row-wise Adagrad: fp32 state per row, by key
     uint32_t short_blocks;     // blocks [0, short_blocks) take short runs
 };
@@ -282,7 +283,7 @@ __device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ w
             pos0[u] = info[u].y;
             wrow[u] = weights + d.w_off + static_cast<int64_t>(info[u].x - d.hash_off) * d.D + col;
             gcol[u] = act ? c.grad + d.out_off + col : nullptr;
-            tw[u] = WEIGHTED && (d.flags & TD_WEIGHTED);
+            tw[u] = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
             // unconditional (an idle slot reads the first row of the weights)
             w_old[u] = ldg(reinterpret_cast<const Pack<WT, VEC>*>(act ? wrow[u] : weights));
             Dr[u] = d.D;
@@ -400,7 +401,7 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
         }
         const uint4 li = ldg(c.long_info + lo);
         const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
-        const bool tw = WEIGHTED && (d.flags & TD_WEIGHTED);
+        const bool tw = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
         const uint32_t i0 = li.y + (q - li.w) * c.chunk;
         const uint32_t i1 = min(li.y + li.z, i0 + c.chunk);
         ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
@@ -643,6 +644,7 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.lr = a.lr;
     c.eps = a.eps;
     c.state = a.state;
+    c.all_weighted = p->pooling == TBE_POOL_MEAN ? 1 : 0;
     c.short_blocks = 0;
     if (a.state) return dispatch_segment<kAdagrad>(a, c, vec);
     return dispatch_segment<kSgd>(a, c, vec);

@@ -232,6 +232,7 @@ enum PayloadMode : int {
     kPayloadPos = 0,      // lookup position j (the sort_rle entry point)
     kPayloadSample = 1,   // sample id b of the lookup's bag
     kPayloadSampleW = 2,  // (b, per-sample weight bits) pair
+    kPayloadMean = 3,     // (b, weight / bag length) pair: mean pooling
 };
 
 // One block per run of whole bags (about kPrepKeys lookups), one lookup per
@@ -249,6 +250,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     __shared__ uint32_t hist[4][kRadix];
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
     __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
+    __shared__ uint32_t hwt[MODE == kPayloadMean ? kPrepMaxBags + 1 : 1];   // tables' weighted flag
     const int tid = threadIdx.x;
     for (int i = tid; i < 4 * kRadix; i += kPrepThreads) (&hist[0][0])[i] = 0u;
     const uint32_t g0 = blockIdx.x * bags_per_block;
@@ -258,7 +260,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const int64_t P0 = nb ? static_cast<int64_t>(offsets[g0]) : 0;
     for (uint32_t i = tid; i <= nb && nb > 0; i += kPrepThreads)
         boff[i] = static_cast<uint32_t>(static_cast<int64_t>(offsets[g0 + i]) - P0);
-    for (uint32_t i = tid; i < t_count; i += kPrepThreads) hoff[i] = tables[t_first + i].hash_off;
+    for (uint32_t i = tid; i < t_count; i += kPrepThreads) {
+        hoff[i] = tables[t_first + i].hash_off;
+        if (MODE == kPayloadMean) hwt[i] = (tables[t_first + i].flags & TD_WEIGHTED) ? 1u : 0u;
+    }
     __syncthreads();
     const uint32_t len = nb ? boff[nb] : 0u;
     uint32_t top = 1;
@@ -272,7 +277,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         for (int u = 0; u < UN; ++u) {
             const uint32_t rp = base + u * kPrepThreads + tid;
             id[u] = rp < len ? indices[P0 + rp] : IT(0);
-            wv[u] = (MODE == kPayloadSampleW && rp < len) ? psw[P0 + rp] : 0.f;
+            wv[u] = ((MODE == kPayloadSampleW || (MODE == kPayloadMean && psw)) && rp < len)
+                        ? psw[P0 + rp] : 1.f;
             g[u] = 0;
         }
         // g[u]: the last bag whose start is <= rp (that bag is not empty);
@@ -299,6 +305,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
             key[u] = hoff[t - t_first] + static_cast<uint32_t>(id[u]);
             pay[u] = gg - t * B;
             if (MODE == kPayloadPos) pay[u] = static_cast<uint32_t>(P0 + base + u * kPrepThreads + tid);
+            if (MODE == kPayloadMean) {   // d(mean)/d(row) = weight / bag length
+                const float w = (psw && hwt[t - t_first]) ? wv[u] : 1.f;
+                wv[u] = w / static_cast<float>(boff[g[u] + 1] - boff[g[u]]);
+            }
         }
         // digit counts: one LDS add per lookup and pass (the order of the
         // adds does not matter)
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
             if (rp < len) {
                 const int64_t p = P0 + rp;
                 keys[p] = key[u];
-                if (MODE == kPayloadSampleW)
+                if (MODE == kPayloadSampleW || MODE == kPayloadMean)
                     static_cast<uint2*>(vals)[p] = make_uint2(pay[u], __float_as_uint(wv[u]));
                 else
                     static_cast<uint32_t*>(vals)[p] = pay[u];
@@ -843,8 +853,10 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
             s += L.digit_bits[i];
         }
     }
-    const int mode = api_outputs ? kPayloadPos : (a.psw ? kPayloadSampleW : kPayloadSample);
-    a.payload_pairs = mode == kPayloadSampleW;
+    const int mode = api_outputs ? kPayloadPos
+                   : p->pooling == TBE_POOL_MEAN ? kPayloadMean
+                   : (a.psw ? kPayloadSampleW : kPayloadSample);
+    a.payload_pairs = mode == kPayloadSampleW || mode == kPayloadMean;
     const bool i64 = p->idtype == TBE_I64;
     if (mode == kPayloadPos)
         i64 ? launch_prep<int64_t, kPayloadPos>(a, pb, total_bags)
@@ -852,15 +864,18 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
     else if (mode == kPayloadSample)
         i64 ? launch_prep<int64_t, kPayloadSample>(a, pb, total_bags)
             : launch_prep<int32_t, kPayloadSample>(a, pb, total_bags);
-    else
+    else if (mode == kPayloadSampleW)
         i64 ? launch_prep<int64_t, kPayloadSampleW>(a, pb, total_bags)
             : launch_prep<int32_t, kPayloadSampleW>(a, pb, total_bags);
+    else
+        i64 ? launch_prep<int64_t, kPayloadMean>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadMean>(a, pb, total_bags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     stage_mark(p, 1, a.stream);
     static_assert(kSortRounds == 8, "one tile shape is instantiated");
-    e = mode == kPayloadSampleW ? sort_passes<kSortRounds, uint2>(a)
-                                : sort_passes<kSortRounds, uint32_t>(a);
+    e = a.payload_pairs ? sort_passes<kSortRounds, uint2>(a)
+                        : sort_passes<kSortRounds, uint32_t>(a);
     if (e != hipSuccess) return e;
     stage_mark(p, 2, a.stream);
 

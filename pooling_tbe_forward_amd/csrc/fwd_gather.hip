@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_fwd_gather(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, int32_t sumD,
     const WT* weights, const IT* __restrict__ indices,
     const IT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
-    uint32_t bags_per_wave, int32_t hist_active)
+    uint32_t bags_per_wave, int32_t hist_active, int32_t mean)
 {
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) +
@@ -170,8 +170,10 @@ __global__ __launch_bounds__(256) void k_fwd_gather(
             }
             if (grp == 0 && active) {
                 Pack<float, VEC> o;
+                // mean pooling: one rounding of sum / length (an empty bag stays 0)
+                const float len = mean && e > s ? static_cast<float>(e - s) : 1.f;
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) o.v[k] = acc[k];
+                for (int k = 0; k < VEC; ++k) o.v[k] = mean ? acc[k] / len : acc[k];
                 *reinterpret_cast<Pack<float, VEC>*>(orow + c) = o;
             }
         }
@@ -194,13 +196,16 @@ hipError_t launch_vec(const FwdArgs& a)
     const auto* ix = static_cast<const IT*>(a.indices);
     const auto* of = static_cast<const IT*>(a.offsets);
     const int ha = a.hist_active ? 1 : 0;
+    const int mean = a.mean ? 1 : 0;
     const uint32_t Bu = static_cast<uint32_t>(a.B);
     if (a.psw)
         hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, true>), grid, block, 0, a.stream,
-                           p->d_tables, Bu, total, p->sum_D, w, ix, of, a.psw, a.out, bpw, ha);
+                           p->d_tables, Bu, total, p->sum_D, w, ix, of, a.psw, a.out, bpw, ha,
+                           mean);
     else
         hipLaunchKernelGGL((k_fwd_gather<WT, IT, VEC, U, false>), grid, block, 0, a.stream,
-                           p->d_tables, Bu, total, p->sum_D, w, ix, of, a.psw, a.out, bpw, ha);
+                           p->d_tables, Bu, total, p->sum_D, w, ix, of, a.psw, a.out, bpw, ha,
+                           mean);
     return hipGetLastError();
 }
 

@@ -40,7 +40,9 @@ tbe_status check_call(const tbe_plan* p, int32_t B, int64_t num_indices, const v
 
 bool use_hist(const tbe_plan* p, int32_t B, int64_t N)
 {
-    if (p->tuning.hist_mode == 1) return false;
+    // the histogram kernel pools sums only (a speed path: the gather kernel
+    // gives the same results)
+    if (p->tuning.hist_mode == 1 || p->pooling == TBE_POOL_MEAN) return false;
     bool any = false;
     for (int t = 0; t < p->T; ++t) any |= (p->h_tables[t].flags & TD_HIST_OK) != 0;
     if (!any) return false;
@@ -170,6 +172,13 @@ tbe_status tbe_get_tuning(const tbe_plan* p, tbe_tuning* t)
     return TBE_OK;
 }
 
+tbe_status tbe_plan_set_pooling(tbe_plan* p, int32_t pooling)
+{
+    if (!p || (pooling != TBE_POOL_SUM && pooling != TBE_POOL_MEAN)) return TBE_EINVAL;
+    p->pooling = pooling;
+    return TBE_OK;
+}
+
 tbe_status tbe_set_tuning(tbe_plan* p, const tbe_tuning* t)
 {
     if (!p || !t) return TBE_EINVAL;
@@ -196,7 +205,7 @@ tbe_status tbe_forward(const tbe_plan* p, int32_t B, const void* weights, const 
                        reinterpret_cast<uintptr_t>(output) % (vec * 4)))
         vec >>= 1;
     FwdArgs a{p, B, weights, indices, offsets, psw, output, vec, use_hist(p, B, num_indices),
-              static_cast<hipStream_t>(stream)};
+              p->pooling == TBE_POOL_MEAN, static_cast<hipStream_t>(stream)};
     stage_mark(p, 0, a.stream);
     tbe_status st2 = TBE_OK;
     // the gather kernel is launched only if some table is not pooled by the
@@ -295,7 +304,8 @@ static tbe_status apply_half(const tbe_plan* p, int32_t B, int64_t num_indices, 
     if (st != TBE_OK) return st;
     if (num_indices == 0) return TBE_OK;
     a.final_buf = a.L.npasses & 1;   // each radix pass swaps the ping-pong buffers
-    a.payload_pairs = weighted != 0;
+    // (sample, weight) payload: per-sample weights, or mean pooling's 1 / length
+    a.payload_pairs = weighted != 0 || p->pooling == TBE_POOL_MEAN;
     st = run_segment_sgd(a) == hipSuccess ? TBE_OK : TBE_EHIP;
     const_cast<tbe_plan*>(p)->n_stage_ev = 0;
     return st;

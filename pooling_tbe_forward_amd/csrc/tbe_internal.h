@@ -51,6 +51,7 @@ struct tbe_plan {
     tbe::TableDesc* d_tables = nullptr;   // device [T]
     uint32_t* d_hash_off = nullptr;       // device [T+1]
     tbe_tuning tuning{};
+    int32_t pooling = 0;                  // TBE_POOL_SUM or TBE_POOL_MEAN
     int device = 0;
     // one-shot stage events of the next call (tbe_set_stage_events)
     hipEvent_t stage_ev[8] = {};
@@ -70,6 +71,7 @@ struct FwdArgs {
     float* out;
     int vec;            // elements per lane load (power of two)
     bool hist_active;   // eligible tables go through the histogram kernel
+    bool mean;          // mean pooling: each bag's sum divided by its length
     hipStream_t stream;
 };
 hipError_t launch_fwd_gather(const FwdArgs& a);

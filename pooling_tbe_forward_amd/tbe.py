@@ -83,6 +83,8 @@ def lib():
         L.tbe_get_tuning.restype = I32
         L.tbe_set_tuning.argtypes = [P, ctypes.POINTER(tbe_tuning)]
         L.tbe_set_tuning.restype = I32
+        L.tbe_plan_set_pooling.argtypes = [P, I32]
+        L.tbe_plan_set_pooling.restype = I32
         L.tbe_status_string.argtypes = [I32]
         L.tbe_status_string.restype = ctypes.c_char_p
         L.tbe_version.argtypes = []
@@ -180,6 +182,14 @@ def tbe_get_tuning(plan: Plan) -> tbe_tuning:
     t = tbe_tuning()
     _check(lib().tbe_get_tuning(plan.handle, ctypes.byref(t)), "tbe_get_tuning")
     return t
+
+
+POOLING = {"sum": 0, "mean": 1}
+
+
+def tbe_plan_set_pooling(plan: Plan, pooling: str):
+    """"sum" (default) or "mean": a bag's sum divided by its length."""
+    _check(lib().tbe_plan_set_pooling(plan.handle, POOLING[pooling]), "tbe_plan_set_pooling")
 
 
 def tbe_set_tuning(plan: Plan, **kw):

@@ -53,6 +53,7 @@ def test_null_plan_calls():
                               None) == tbe.TBE_EINVAL
     assert L.tbe_bounds_check(None, 1, None, 0, None, None, None) == tbe.TBE_EINVAL
     assert L.tbe_set_tuning(None, None) == tbe.TBE_EINVAL
+    assert L.tbe_plan_set_pooling(None, 1) == tbe.TBE_EINVAL
     assert L.tbe_plan_layout(None, None, None, None) == tbe.TBE_EINVAL
     assert L.tbe_workspace_init(None, 1 << 20, None) == tbe.TBE_EINVAL
     assert L.tbe_set_stage_events(None, None, 0) == tbe.TBE_EINVAL

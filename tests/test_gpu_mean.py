@@ -1,0 +1,138 @@
+"""GPU parity of mean pooling (tbe_plan_set_pooling(plan, "mean")) through the
+C ABI against the oracle: forward (empty bags stay zero), backward-SGD and
+row-wise Adagrad (each lookup's contribution divided by its bag's length),
+prepare/apply, and the error code of an unknown mode."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pooling_tbe_forward_amd import datagen as dg
+from pooling_tbe_forward_amd import tbe
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan(prob):
+    plan = H.make_plan(prob)
+    tbe.tbe_plan_set_pooling(plan, "mean")
+    return plan
+
+
+@pytest.mark.parametrize("name,B", [("toy", None), ("uniform", 256), ("mixed", 64),
+                                    ("hist", 64), ("stress", 128)])
+def test_mean_forward_vs_oracle(name, B):
+    prob = dg.make_problem(name, seed=900, **({} if B is None else dict(B=B)))
+    w = dg.packed_weights_torch(prob, "cuda")
+    plan = _plan(prob)
+    d = H.device_inputs(prob)
+    out = torch.full((prob.B, prob.sum_D), float("nan"), dtype=torch.float32, device="cuda")
+    tbe.tbe_forward(plan, prob.B, w, d["indices"], d["offsets"], d["psw"], out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rng = np.random.default_rng(0)
+    bags = np.unique(np.concatenate([rng.choice(prob.T * prob.B, size=min(600, prob.T * prob.B),
+                                                replace=False),
+                                     np.flatnonzero(prob.lengths.ravel() == 0)[:20]]))
+    tt, bb = bags // prob.B, bags % prob.B
+    rowsets = [np.unique(prob.indices[prob.offsets[t * prob.B]:prob.offsets[(t + 1) * prob.B]])
+               for t in range(prob.T)]
+    ref = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob),
+                         H.sparse_tables(prob, rowsets), prob.indices, prob.offsets, prob.psw,
+                         prob.weighted, bag_list=bags, pooling="mean")
+    cols = np.concatenate([[0], np.cumsum(prob.dims)])
+    g = np.zeros_like(ref)
+    for k in range(bags.size):
+        D = int(prob.dims[tt[k]])
+        g[k, :D] = got[bb[k], cols[tt[k]]:cols[tt[k]] + D]
+        g[k, D:] = ref[k, D:]
+    rep = H.allclose_report(g, ref, 1e-5, 1e-6)
+    assert rep["ok"], rep
+    if name == "toy":
+        assert np.all(got[2, cols[1]:cols[2]] == 0)     # the forced empty bag (t=1, b=2)
+
+
+def _oracle_rows(prob, keys, pooling, state_in=None, eps=None):
+    tt, rr = H.key_to_table_row(prob, keys)
+    tabs = H.sparse_tables(prob, [np.unique(rr[tt == t]) for t in range(prob.T)])
+    if state_in is None:
+        return oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob), tabs,
+                                   prob.indices, prob.offsets, prob.psw, prob.weighted, prob.grad,
+                                   prob.lr, keys, pooling=pooling)[1], None
+    _, nr, st = oracle.backward_adagrad(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob),
+                                        tabs, prob.indices, prob.offsets, prob.psw,
+                                        prob.weighted, prob.grad, prob.lr, eps, keys,
+                                        state_in[keys], pooling=pooling)
+    return nr, st
+
+
+def _rows_on_device(prob, w_dev, keys, like):
+    tt, rr = H.key_to_table_row(prob, keys)
+    got = np.array(like)
+    for t in range(prob.T):
+        sel = np.flatnonzero(tt == t)
+        if sel.size:
+            got[sel, :int(prob.dims[t])] = H.rows_from_device(w_dev, prob, t, rr[sel])
+    return got
+
+
+@pytest.mark.parametrize("name,B,tau", [("toy", None, 2), ("uniform", 256, 128),
+                                        ("stress", 256, 16), ("mixed", 64, 128)])
+@pytest.mark.parametrize("opt", ["sgd", "adagrad"])
+def test_mean_backward_vs_oracle(name, B, tau, opt):
+    prob = dg.make_problem(name, seed=910, **({} if B is None else dict(B=B)))
+    plan = _plan(prob)
+    tbe.tbe_set_tuning(plan, tau=tau, chunk=8)
+    d = H.device_inputs(prob)
+    w = dg.packed_weights_torch(prob, "cuda")
+    ws = tbe.alloc_workspace(plan, prob.B, prob.N)
+    state0 = np.random.default_rng(1).random(int(np.sum(prob.rows)), dtype=np.float32)
+    s_dev = torch.from_numpy(state0.copy()).cuda()
+    if opt == "sgd":
+        tbe.tbe_backward_sgd(plan, prob.B, w, d["indices"], d["offsets"], d["psw"], d["grad"],
+                             prob.lr, ws)
+    else:
+        tbe.tbe_backward_adagrad(plan, prob.B, w, s_dev, d["indices"], d["offsets"], d["psw"],
+                                 d["grad"], prob.lr, ws)
+    torch.cuda.synchronize()
+    o = H.oracle_sort(prob, tau)
+    keys = o["unique_keys"]
+    if keys.size > 20000:
+        keys = np.unique(np.random.default_rng(2).choice(keys, 20000, replace=False))
+    nr, st = _oracle_rows(prob, keys, "mean", state0 if opt == "adagrad" else None,
+                          tbe.ADAGRAD_EPS)
+    got = _rows_on_device(prob, w, keys, nr)
+    rep = H.allclose_report(got, nr, *H.TOL[prob.wdtype])
+    assert rep["ok"], rep
+    if opt == "adagrad":
+        rep = H.allclose_report(s_dev.cpu().numpy()[keys], st, *H.TOL[prob.wdtype])
+        assert rep["ok"], rep
+    # mean and sum differ wherever a bag has more than one lookup
+    if name == "uniform":
+        nr_sum, _ = _oracle_rows(prob, keys[:50], "sum")
+        assert not np.allclose(nr_sum, nr[:50])
+
+
+def test_mean_prepare_apply_matches_whole():
+    prob = dg.make_problem("stress", seed=920, B=256)
+    plan = _plan(prob)
+    d = H.device_inputs(prob)
+    w1 = dg.packed_weights_torch(prob, "cuda")
+    ws = tbe.alloc_workspace(plan, prob.B, prob.N)
+    tbe.tbe_backward_sgd(plan, prob.B, w1, d["indices"], d["offsets"], d["psw"], d["grad"],
+                         prob.lr, ws)
+    w2 = dg.packed_weights_torch(prob, "cuda")
+    tbe.tbe_backward_prepare(plan, prob.B, d["indices"], d["offsets"], d["psw"], ws)
+    tbe.tbe_backward_apply(plan, prob.B, prob.N, d["psw"] is not None, w2, d["grad"], prob.lr, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+
+
+def test_pooling_mode_errors():
+    prob = dg.make_problem("toy", seed=1)
+    plan = H.make_plan(prob)
+    assert tbe.lib().tbe_plan_set_pooling(plan.handle, 2) == tbe.TBE_EINVAL
+    assert tbe.lib().tbe_plan_set_pooling(plan.handle, -1) == tbe.TBE_EINVAL
+    tbe.tbe_plan_set_pooling(plan, "mean")
+    tbe.tbe_plan_set_pooling(plan, "sum")
