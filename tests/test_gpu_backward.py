@@ -139,6 +139,22 @@ def test_exact_arithmetic_bit_exact(wdtype, seed, tau, chunk):
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
 
 
+@pytest.mark.parametrize("dims,wdtype", [((4,), "f32"), ((1,), "f32"), ((2, 4), "f32"),
+                                         ((4,), "f16"), ((1, 2), "f16")])
+@pytest.mark.parametrize("tau", [128, 2 ** 31 - 1])
+def test_narrow_rows_many_short_runs(dims, wdtype, tau):
+    """Rows that fit one lane's load (D <= its vector width) with hundreds of
+    short runs: a wave batch must not hold more run records than lanes (a
+    one-lane worker would make it 128 and leave half of them unprocessed)."""
+    prob, packed = dg.exact_problem(11, T=len(dims), B=400, dims=dims, wdtype=wdtype,
+                                    weighted=True, max_len=12, max_rows=3000)
+    assert len(H.oracle_sort(prob, tau)["short_runs"]) > 256
+    w = gpu_backward(prob, H.device_weights_from_host(packed), tau=tau, chunk=16)
+    ref = packed.copy()
+    H.oracle_backward(prob, ref)
+    assert np.array_equal(w.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+
+
 @pytest.mark.parametrize("seed", [1, 2, 3])
 @pytest.mark.parametrize("weighted", ["none", "all"])
 def test_toy_backward_vs_oracle(seed, weighted):
