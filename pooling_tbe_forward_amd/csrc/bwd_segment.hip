@@ -474,81 +474,93 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
 }
 
 // Long runs, step 2 (next launch, so every partial is visible without a
-// device-wide cache flush): one worker per long run adds its chunks'
-// partials in chunk order -- 8 loads in flight -- and applies the update.
+// device-wide cache flush): one block per long run.  The block's 256 lanes
+// form 256 / L chunk slots of L lanes (one row slab); slot s adds the run's
+// chunks s, s + slots, s + 2 * slots, ... (4 loads in flight), then the slots
+// are folded in a fixed order -- lane swaps inside a wave, then the four waves
+// through LDS -- so the sum does not depend on scheduling, and wave 0 applies
+// the update.  The longest run's combine is this launch's critical path; a
+// block per run shortens it by the slot count (stress workload: 31 -> 11 us).
 // Row-wise Adagrad: one slab per row, and lanes past the row's D keep zeros
 // so the whole worker takes part in the sum of squares.
 template <typename WT, typename ACC, int VEC, int OPT>
 __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict__ weights,
                                                       const ACC* __restrict__ partials)
 {
-    const int lane = threadIdx.x & 63;
-    const int g_log2 = 6 - c.lpr_log2;
-    const int grp = lane >> c.lpr_log2;
-    const int sub = lane & ((1 << c.lpr_log2) - 1);
+    __shared__ Pack<ACC, VEC> red[4][64];   // each wave's folded slab sum
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lpr = c.lpr_log2;
+    const int L = 1 << lpr;
+    const int sub = lane & (L - 1);
+    const uint32_t slot = static_cast<uint32_t>(tid >> lpr);
+    const uint32_t nslots = 256u >> lpr;
     const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
-    const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
-    for (uint32_t k0 = wave << g_log2; k0 < nlong; k0 += nwaves << g_log2) {
-        const uint32_t k = k0 + grp;
-        if (k >= nlong) continue;
+    for (uint32_t k = blockIdx.x; k < nlong; k += gridDim.x) {
         const uint4 li = ldg(c.long_info + k);
         const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
         WT* __restrict__ wrow = weights + d.w_off + static_cast<int64_t>(li.x - d.hash_off) * d.D;
         const uint32_t nq = (li.z + c.chunk - 1) / c.chunk;
         const uint32_t qend = min(li.w + nq, c.max_chunks);
-        if (OPT == kAdagrad) {
-            const int col = sub * VEC;
+        const int slab = VEC << lpr;
+        const int nslab = OPT == kAdagrad ? 1 : (d.D + slab - 1) / slab;
+        for (int sl = 0; sl < nslab; ++sl) {
+            const int col = sl * slab + sub * VEC;
             const bool act = col < d.D;
             const int cc = act ? col : 0;
-            const Pack<WT, VEC> w_old = ldg_stream(reinterpret_cast<const Pack<WT, VEC>*>(wrow + cc));
-            const float s_old = ldg(c.state + li.x);
+            Pack<WT, VEC> w_old;
+            float s_old = 0.f;
+            if (wave == 0) {   // the updating wave's row slab and state, early
+                w_old = ldg_stream(reinterpret_cast<const Pack<WT, VEC>*>(wrow + cc));
+                if (OPT == kAdagrad) s_old = ldg(c.state + li.x);
+            }
             ACC acc[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) acc[j] = ACC(0);
-            for (uint32_t qq = li.w; qq < qend; qq += 8) {
-                Pack<ACC, VEC> part[8];
+            for (uint32_t q0 = li.w + slot; q0 < qend; q0 += 4 * nslots) {
+                Pack<ACC, VEC> part[4];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const uint32_t qm = qq + m < qend ? qq + m : qend - 1;
+                for (int m = 0; m < 4; ++m) {   // unconditional: past the end re-reads the last
+                    const uint32_t qm = q0 + m * nslots;
+                    const uint32_t qc = qm < qend ? qm : qend - 1;
                     part[m] = ldg(reinterpret_cast<const Pack<ACC, VEC>*>(
-                        partials + static_cast<int64_t>(qm) * c.max_D + cc));
+                        partials + static_cast<int64_t>(qc) * c.max_D + cc));
                 }
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    if (act && qq + m < qend)
+                for (int m = 0; m < 4; ++m)
+                    if (act && q0 + m * nslots < qend)
 #pragma unroll
                         for (int j = 0; j < VEC; ++j) acc[j] += part[m].v[j];
             }
-            float s_new;
-            const Pack<WT, VEC> o = adagrad_row<WT, ACC, VEC>(w_old, acc, s_old, d.D,
-                                                              1 << c.lpr_log2, c.lr, c.eps, s_new);
-            if (act) stg_stream(reinterpret_cast<Pack<WT, VEC>*>(wrow + col), o);
-            if (sub == 0) c.state[li.x] = s_new;
-            continue;
-        }
-        for (int c0 = 0; c0 < d.D; c0 += (VEC << c.lpr_log2)) {
-            const int col = c0 + sub * VEC;
-            if (col >= d.D) continue;
-            const Pack<WT, VEC> w_old = ldg_stream(reinterpret_cast<const Pack<WT, VEC>*>(wrow + col));
-            ACC acc[VEC];
+            // fold the slots of a wave (lanes that differ only in the slot bits)
+            for (int m = 32; m >= L; m >>= 1)
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[j] = ACC(0);
-            for (uint32_t qq = li.w; qq < qend; qq += 8) {
-                Pack<ACC, VEC> part[8];
+                for (int j = 0; j < VEC; ++j) acc[j] += __shfl_xor(acc[j], m);
+            if (lane < L) {
+                Pack<ACC, VEC> o;
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {   // unconditional: past the end re-reads the last
-                    const uint32_t qm = qq + m < qend ? qq + m : qend - 1;
-                    part[m] = ldg(reinterpret_cast<const Pack<ACC, VEC>*>(
-                        partials + static_cast<int64_t>(qm) * c.max_D + col));
-                }
-#pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    if (qq + m < qend)
-#pragma unroll
-                        for (int j = 0; j < VEC; ++j) acc[j] += part[m].v[j];
+                for (int j = 0; j < VEC; ++j) o.v[j] = acc[j];
+                red[wave][lane] = o;
             }
-            sgd_store<WT, ACC, VEC>(wrow + col, w_old, acc, c.lr);
+            __syncthreads();
+            if (wave == 0) {
+                const int ln = lane & (L - 1);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    acc[j] = ((red[0][ln].v[j] + red[1][ln].v[j]) + red[2][ln].v[j]) +
+                             red[3][ln].v[j];
+                if (OPT == kAdagrad) {   // every lane of the wave takes part in the swaps
+                    float s_new;
+                    const Pack<WT, VEC> o = adagrad_row<WT, ACC, VEC>(w_old, acc, s_old, d.D, L,
+                                                                      c.lr, c.eps, s_new);
+                    if (lane < L && act) stg_stream(reinterpret_cast<Pack<WT, VEC>*>(wrow + col), o);
+                    if (lane == 0) c.state[li.x] = s_new;
+                } else if (lane < L && act) {
+                    sgd_store<WT, ACC, VEC>(wrow + col, w_old, acc, c.lr);
+                }
+            }
+            __syncthreads();   // red is reused by the next slab or run
         }
     }
 }
@@ -607,7 +619,9 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     const int G = 1 << (6 - c.lpr_log2);
     c.short_blocks = blocks_for(L.N, int64_t(4) * G * 2, 2048);  // G*S runs per wave batch
     const uint32_t b_chunk = blocks_for(L.max_chunks, int64_t(4) * G, 1024);
-    const uint32_t b_long = blocks_for(L.max_long, int64_t(4) * G, 256);
+    // a block per long run (at most 4096: measured best of 1024..8192 on the
+    // stress, band and mixed workloads)
+    const uint32_t b_long = blocks_for(L.max_long, 1, 4096);
     const dim3 grid(c.short_blocks + b_chunk);
     // short-run batches: S = 2 runs per worker, U = 4 gradient rows in flight
     // (measured best of S in {1,2,4,8} x U in {4,8} on the uniform, stress and

@@ -78,6 +78,41 @@ def test_exact_arithmetic_bit_exact(wdtype, seed, hist_mode):
     assert np.array_equal(out.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("bpw", [2, 3, 8, 64])
+@pytest.mark.parametrize("case", ["f32-weighted", "f16-hist", "f32-mean"])
+def test_bags_per_wave_bit_exact(bpw, case):
+    """Several consecutive bags per wavefront (the next bag's ids fetched
+    during the current bag): empty bags, waves that cross table boundaries,
+    tables of one and of several column slabs, weighted next to unweighted
+    tables, and bags skipped for the histogram kernel.  Exact arithmetic, so
+    the output equals the oracle bit for bit."""
+    if case == "f16-hist":   # tables 0 and 2 on the histogram path, 1 gathered
+        prob, packed = dg.exact_problem(63, T=3, B=50, dims=(64, 512, 16), wdtype="f16",
+                                        weighted=False, max_len=90, max_rows=40)
+        tun = dict(hist_mode=2)
+    else:
+        prob, packed = dg.exact_problem(61 if case == "f32-weighted" else 62, T=4, B=50,
+                                        dims=(8, 64, 520, 32), wdtype="f32", weighted=True,
+                                        max_len=90, max_rows=40)
+        prob.weighted[1] = False
+        tun = {}
+    plan = H.make_plan(prob)
+    pooling = "mean" if case == "f32-mean" else "sum"
+    if pooling == "mean":
+        tbe.tbe_plan_set_pooling(plan, "mean")
+    out = _run_forward(prob, H.device_weights_from_host(packed), plan=plan,
+                       fwd_bags_per_wave=bpw, **tun)
+    tabs = oracle.dense_tables(packed, prob.rows, prob.dims)
+    ref = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob), tabs,
+                         prob.indices, prob.offsets, prob.psw, prob.weighted, pooling=pooling)
+    assert (prob.lengths == 0).any()
+    if pooling == "mean":   # one division per bag: within an ulp of the fp64 quotient
+        rep = H.allclose_report(out, ref, 1e-6, 0.0)
+        assert rep["ok"], rep
+    else:
+        assert np.array_equal(out.astype(np.float64), ref)
+
+
 def _sampled_forward_check(prob, w_dev, out, nbags=1500, seed=0):
     rng = np.random.default_rng(seed)
     TB = prob.T * prob.B
