@@ -127,7 +127,7 @@ struct SegArgs {
     float eps;                 // row-wise Adagrad only
     int32_t all_weighted;      // mean pooling: every table's payload weight applies
     float* state;              // row-wise Adagrad: fp32 state per row, by key
-    uint32_t short_blocks;     // blocks [0, short_blocks) take short runs
+    uint32_t chunk_blocks;     // the grid's last chunk_blocks blocks take long-run chunks
 };
 
 enum Opt : int { kSgd = 0, kAdagrad = 1 };
@@ -422,23 +422,17 @@ __device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ we
     }
 }
 
-// Long runs, step 1: one worker per chunk of `chunk` lookups writes the
-// chunk's partial sum (fp64 for fp32 tables) to the workspace.  A chunk is
-// one run, so the worker keeps 8 gradient rows in flight (measured faster
-// than 4 on the Zipf workloads; the kernel's register count does not change).
+// One wavefront per chunk (rows of L = 64 lanes): the wave keeps 8 gradient
+// rows in flight over the whole chunk and writes its partial; the four waves
+// of a block take four chunks.
 template <typename ACC, int VEC, bool WEIGHTED>
-__device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ partials,
-                                            uint32_t wave, uint32_t nwaves)
+__device__ __forceinline__ void long_chunks_wave(const SegArgs& c, ACC* __restrict__ partials,
+                                                 uint32_t wave, uint32_t nwaves)
 {
     const int lane = threadIdx.x & 63;
-    const int g_log2 = 6 - c.lpr_log2;
-    const int grp = lane >> c.lpr_log2;
-    const int sub = lane & ((1 << c.lpr_log2) - 1);
     const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
     const uint32_t nchunks = min(ldg(c.counts + 3), c.max_chunks);
-    for (uint32_t q0 = wave << g_log2; q0 < nchunks; q0 += nwaves << g_log2) {
-        const uint32_t q = q0 + grp;
-        if (q >= nchunks) continue;
+    for (uint32_t q = wave; q < nchunks; q += nwaves) {
         uint32_t lo = 0, hi = nlong;  // long run owning chunk q: last with first chunk <= q
         while (hi - lo > 1) {
             const uint32_t mid = (lo + hi) >> 1;
@@ -450,8 +444,8 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
         const uint32_t i0 = li.y + (q - li.w) * c.chunk;
         const uint32_t i1 = min(li.y + li.z, i0 + c.chunk);
         ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
-        for (int c0 = 0; c0 < c.max_D; c0 += (VEC << c.lpr_log2)) {
-            const int col = c0 + sub * VEC;
+        for (int c0 = 0; c0 < d.D; c0 += 64 * VEC) {
+            const int col = c0 + lane * VEC;
             const uint32_t p0[1] = {i0};
             const uint32_t ln[1] = {i1 - i0};
             const float* const gc[1] = {col < d.D ? c.grad + d.out_off + col : nullptr};
@@ -461,14 +455,91 @@ __device__ __forceinline__ void long_chunks(const SegArgs& c, ACC* __restrict__ 
             for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
             const uint32_t nof[1] = {0};
             const float now[1] = {1.f};
-            flat_sum<ACC, VEC, 1, 8, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, sub,
-                                                      1 << c.lpr_log2, grp << c.lpr_log2, acc);
+            flat_sum<ACC, VEC, 1, 8, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, lane, 64, 0,
+                                                      acc);
             if (col < d.D) {
                 Pack<ACC, VEC> o;
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) o.v[k] = acc[0][k];
                 *reinterpret_cast<Pack<ACC, VEC>*>(prow + col) = o;
             }
+        }
+    }
+}
+
+// Long runs, step 1: one block per chunk of `chunk` lookups writes the
+// chunk's partial sum (fp64 for fp32 tables) to the workspace.  The block's
+// 256 / L slots of L lanes take consecutive sub-ranges of the chunk, each
+// with 8 gradient rows in flight; the slots are folded in a fixed order (lane
+// swaps inside a wave, then the four waves through LDS), so the partial does
+// not depend on scheduling and a chunk's dependent chain is one slot's share
+// of it rather than the whole chunk (stress workload: segment kernel 101 ->
+// 89 us, band 94 -> 77 us).  Rows as wide as a wavefront (L = 64) take
+// long_chunks_wave instead: there the block form measured slower (mixed
+// workload 526 -> 552 us).
+template <typename ACC, int VEC, bool WEIGHTED>
+__device__ __forceinline__ void long_chunks_block(const SegArgs& c, ACC* __restrict__ partials,
+                                                  Pack<ACC, VEC> (*red)[64], uint32_t blk,
+                                                  uint32_t nblk)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lpr = c.lpr_log2;
+    const int L = 1 << lpr;
+    const int sub = lane & (L - 1);
+    const int gbase = (lane >> lpr) << lpr;
+    const uint32_t slot = static_cast<uint32_t>(tid >> lpr);
+    const uint32_t nslots = 256u >> lpr;
+    const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
+    const uint32_t nchunks = min(ldg(c.counts + 3), c.max_chunks);
+    for (uint32_t q = blk; q < nchunks; q += nblk) {
+        uint32_t lo = 0, hi = nlong;  // long run owning chunk q: last with first chunk <= q
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (ldg(c.long_info + mid).w <= q) lo = mid; else hi = mid;
+        }
+        const uint4 li = ldg(c.long_info + lo);
+        const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
+        const bool tw = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
+        const uint32_t i0 = li.y + (q - li.w) * c.chunk;
+        const uint32_t len = min(li.y + li.z, i0 + c.chunk) - i0;
+        const uint32_t per = (len + nslots - 1) / nslots;   // this slot's share
+        const uint32_t s0 = min(len, slot * per);
+        const uint32_t s1 = min(len, s0 + per);
+        ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
+        for (int c0 = 0; c0 < d.D; c0 += (VEC << lpr)) {
+            const int col = c0 + sub * VEC;
+            const uint32_t p0[1] = {i0 + s0};
+            const uint32_t ln[1] = {s1 - s0};
+            const float* const gc[1] = {col < d.D ? c.grad + d.out_off + col : nullptr};
+            const bool twa[1] = {tw};
+            ACC acc[1][VEC];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
+            const uint32_t nof[1] = {0};
+            const float now[1] = {1.f};
+            flat_sum<ACC, VEC, 1, 8, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, sub, L,
+                                                      gbase, acc);
+            for (int m = 32; m >= L; m >>= 1)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc[0][k] += __shfl_xor(acc[0][k], m);
+            if (lane < L) {
+                Pack<ACC, VEC> o;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) o.v[k] = acc[0][k];
+                red[wave][lane] = o;
+            }
+            __syncthreads();
+            if (wave == 0 && lane < L && col < d.D) {
+                Pack<ACC, VEC> o;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k)
+                    o.v[k] = ((red[0][lane].v[k] + red[1][lane].v[k]) + red[2][lane].v[k]) +
+                             red[3][lane].v[k];
+                *reinterpret_cast<Pack<ACC, VEC>*>(prow + col) = o;
+            }
+            __syncthreads();   // red is reused by the next slab or chunk
         }
     }
 }
@@ -567,16 +638,25 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
 
 constexpr int kLdsTables = 256;   // table descriptors staged in LDS
 
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, int OPT>
+// BLOCKCHUNK: long-run chunks take a block each (rows narrower than a
+// wavefront) rather than a wavefront each; an instantiation of its own, since
+// the block form's code measured slower in the other kernels (mixed workload
+// 527 -> 558 us) even where it never runs.
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, int OPT,
+          bool BLOCKCHUNK>
 __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ weights,
                                                  ACC* __restrict__ partials)
 {
     static_assert((S << (6 - kMinLprLog2)) <= 64, "a batch is loaded one record per lane");
     __shared__ TableDesc sdesc[kLdsTables];
+    __shared__ Pack<ACC, VEC> red[BLOCKCHUNK ? 4 : 1][64];
     const uint32_t wib = threadIdx.x >> 6;
-    if (blockIdx.x < c.short_blocks) {
+    // blocks [0, gridDim.x - chunk_blocks) take short runs (dispatched first:
+    // measured faster than chunks first), the rest long-run chunks
+    const uint32_t short_blocks = gridDim.x - c.chunk_blocks;
+    if (blockIdx.x < short_blocks) {
         const uint32_t wave = blockIdx.x * 4 + wib;
-        const uint32_t nwaves = c.short_blocks * 4;
+        const uint32_t nwaves = short_blocks * 4;
         if (c.T <= kLdsTables) {
             for (int i = threadIdx.x; i < c.T; i += 256) sdesc[i] = ldg(c.tables + i);
             __syncthreads();
@@ -585,9 +665,12 @@ __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ wei
             short_runs<WT, ACC, VEC, S, U, WEIGHTED, false, OPT>(c, weights, sdesc, wave, nwaves);
         }
     }
+    else if constexpr (BLOCKCHUNK)
+        long_chunks_block<ACC, VEC, WEIGHTED>(c, partials, red, blockIdx.x - short_blocks,
+                                              c.chunk_blocks);
     else
-        long_chunks<ACC, VEC, WEIGHTED>(c, partials, (blockIdx.x - c.short_blocks) * 4 + wib,
-                                        (gridDim.x - c.short_blocks) * 4);
+        long_chunks_wave<ACC, VEC, WEIGHTED>(c, partials, (blockIdx.x - short_blocks) * 4 + wib,
+                                             c.chunk_blocks * 4);
 }
 
 uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
@@ -598,15 +681,24 @@ uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
     return static_cast<uint32_t>(b);
 }
 
+template <typename WT, typename ACC, int VEC, int S, int U, int OPT, bool BLOCKCHUNK>
+void launch_seg_c(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
+{
+    if (a.payload_pairs)
+        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true, OPT, BLOCKCHUNK>), grid,
+                           dim3(256), 0, a.stream, c, w, partials);
+    else
+        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, false, OPT, BLOCKCHUNK>), grid,
+                           dim3(256), 0, a.stream, c, w, partials);
+}
+
 template <typename WT, typename ACC, int VEC, int S, int U, int OPT>
 void launch_seg(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
 {
-    if (a.payload_pairs)
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true, OPT>), grid, dim3(256), 0,
-                           a.stream, c, w, partials);
+    if (c.lpr_log2 < 6)   // rows narrower than a wavefront: a block per chunk
+        launch_seg_c<WT, ACC, VEC, S, U, OPT, true>(a, grid, c, w, partials);
     else
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, false, OPT>), grid, dim3(256), 0,
-                           a.stream, c, w, partials);
+        launch_seg_c<WT, ACC, VEC, S, U, OPT, false>(a, grid, c, w, partials);
 }
 
 template <typename WT, typename ACC, int VEC, int OPT>
@@ -617,12 +709,14 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     ACC* partials = reinterpret_cast<ACC*>(ws + L.off_partials);
     WT* w = static_cast<WT*>(a.weights);
     const int G = 1 << (6 - c.lpr_log2);
-    c.short_blocks = blocks_for(L.N, int64_t(4) * G * 2, 2048);  // G*S runs per wave batch
-    const uint32_t b_chunk = blocks_for(L.max_chunks, int64_t(4) * G, 1024);
+    const uint32_t short_blocks = blocks_for(L.N, int64_t(4) * G * 2, 2048);  // G*S runs per wave batch
+    // a block per chunk (rows narrower than a wave), else a wave per chunk
+    c.chunk_blocks = c.lpr_log2 == 6 ? blocks_for(L.max_chunks, 4, 1024)
+                                     : blocks_for(L.max_chunks, 1, 4096);
     // a block per long run (at most 4096: measured best of 1024..8192 on the
     // stress, band and mixed workloads)
     const uint32_t b_long = blocks_for(L.max_long, 1, 4096);
-    const dim3 grid(c.short_blocks + b_chunk);
+    const dim3 grid(short_blocks + c.chunk_blocks);
     // short-run batches: S = 2 runs per worker, U = 4 gradient rows in flight
     // (measured best of S in {1,2,4,8} x U in {4,8} on the uniform, stress and
     // mixed workloads)
@@ -705,7 +799,7 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.eps = a.eps;
     c.state = a.state;
     c.all_weighted = p->pooling == TBE_POOL_MEAN ? 1 : 0;
-    c.short_blocks = 0;
+    c.chunk_blocks = 0;
     if (a.state) return dispatch_segment<kAdagrad>(a, c, vec);
     return dispatch_segment<kSgd>(a, c, vec);
 }
