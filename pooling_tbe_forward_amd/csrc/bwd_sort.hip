@@ -310,14 +310,25 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
                 wv[u] = w / static_cast<float>(boff[g[u] + 1] - boff[g[u]]);
             }
         }
-        // digit counts: one LDS add per lookup and pass (the order of the
-        // adds does not matter)
+        // digit counts (the order of the adds does not matter).  The lanes
+        // whose digit equals the wave's first active lane's are merged into
+        // one add: a bag's ids come from one table, so the upper digits are
+        // often one value across the wave, and same-address LDS adds would
+        // otherwise serialize; the other lanes add one each.
+        const int lane = tid & 63;
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const bool ok = base + u * kPrepThreads + tid < len;
             if (ok)
-                for (int q = 0; q < pb.npasses; ++q)
-                    atomicAdd(&hist[q][(key[u] >> pb.shift[q]) & pb.mask[q]], 1u);
+                for (int q = 0; q < pb.npasses; ++q) {
+                    const uint32_t d = (key[u] >> pb.shift[q]) & pb.mask[q];
+                    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+                    const uint64_t same = __ballot(d == d0);
+                    if (d != d0)
+                        atomicAdd(&hist[q][d], 1u);
+                    else if (lane == __builtin_ctzll(same))
+                        atomicAdd(&hist[q][d0], static_cast<uint32_t>(__popcll(same)));
+                }
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
