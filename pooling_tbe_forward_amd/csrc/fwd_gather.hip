@@ -218,8 +218,13 @@ hipError_t launch_vec(const FwdArgs& a)
     const uint32_t waves = (total + bpw - 1) / bpw;
     const uint32_t blocks = (waves + 3) / 4;
     if (blocks == 0) return hipSuccess;
-    // rows in flight per lane: 4 with 16-byte loads, 8 with narrower ones
-    constexpr int U = (VEC * sizeof(WT) >= 16) ? 4 : 8;
+    // rows per lane per round (2U in flight with the double buffer): 2 with
+    // 16-byte loads, 8 with narrower ones.  The kernel is bound by how many
+    // waves keep gathers in flight: U = 2 holds 8 waves per SIMD where U = 4
+    // held 5 (fp16 weighted) or 6 (fp32), and measured faster on every
+    // workload with hot rows (mixed forward 280 -> 235 us, stress 58 -> 52,
+    // band 57 -> 50; uniform unchanged; U = 1 was slower on stress).
+    constexpr int U = (VEC * sizeof(WT) >= 16) ? 2 : 8;
     const dim3 grid(blocks), block(256);
     const auto* w = static_cast<const WT*>(a.weights);
     const auto* ix = static_cast<const IT*>(a.indices);
