@@ -14,16 +14,18 @@
 // gfx950 design:
 //  * a gradient row of D fp32 elements is covered by L lanes (VEC elements,
 //    up to 16-byte loads); a 64-lane wavefront holds G = 64/L workers;
-//  * short runs: each worker owns U runs at once (U slots).  It issues the U
-//    weight-row loads up front, then walks the runs' contributions in lock
-//    step, so U sample-id loads and U gradient-row loads are in flight per
-//    step; a run of one lookup costs one dependent step, not U;
-//  * long runs: the same launch carries chunk workers (one chunk of `chunk`
-//    lookups each) that write partial sums; the next launch adds each run's
-//    partials in chunk order and applies the update, so the result does not
-//    depend on scheduling.  (Combining in the same launch, last arrival wins,
-//    needs a device-scope release per chunk, which on gfx950 writes back and
+//  * short runs: each worker owns S runs at once.  It issues their weight-row
+//    loads up front, then walks their contributions as one flat sequence:
+//    L sample ids at once, U gradient rows in flight across run boundaries,
+//    so a run of one lookup costs one dependent step, not one each;
+//  * long runs: the same launch carries chunk workers (a block per chunk of
+//    `chunk` lookups, or a wavefront for rows of 64 lanes) that write partial
+//    sums; the next launch (a block per long run) adds each run's partials in
+//    a fixed order and applies the update, so the result does not depend on
+//    scheduling.  (Combining in the same launch, last arrival wins, needs a
+//    device-scope release per chunk, which on gfx950 writes back and
 //    invalidates the whole L2 -- far dearer than one more launch);
+//  * weight rows are read and written with streaming (non-temporal) hints;
 //  * accumulation is fp64 for fp32 tables (long Zipf runs would otherwise
 //    drift past 1e-5 relative) and fp32 for fp16 tables; w - lr*g is rounded
 //    once to the storage type;
