@@ -43,7 +43,7 @@ constexpr int kRadix = 256;
 constexpr int kSortThreads = 1024;   // 16 waves per radix tile
 constexpr int kRleThreads = 1024;
 constexpr int kRleItems = 8;         // sorted positions per thread (two 16-byte loads)
-constexpr int kRleTile = kRleThreads * kRleItems;
+constexpr int kRleItemsSmall = 4;    // ... for small batches (see kSmallN)
 constexpr int kRleMaxT = 2048;       // hash offsets staged in LDS up to this many tables
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagInc = 2u << 30;
@@ -56,6 +56,14 @@ constexpr int kPrepThreads = 512;    // measured: 512 or 256 threads per block b
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kSortRounds = 8;       // keys per thread in a radix tile
+constexpr int kSortRoundsSmall = 4;  // ... for small batches (see kSmallN)
+// Batches of at most kSmallN lookups use tiles of half the depth in the radix
+// passes and the run-length encode: with a few tens of tiles every tile has a
+// CU of its own, and shorter tiles finish sooner.  Beyond it the longer
+// look-back chain over twice the tiles costs more.  Measured: uniform
+// workload (328K lookups) radix 45 -> 43 us and encode 17 -> 14 us; stress
+// (1.6M) and mixed (4.9M) slower with the short tiles.
+constexpr int64_t kSmallN = int64_t(1) << 19;
 }  // namespace
 
 BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
@@ -72,10 +80,11 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
         L.digit_bits[i] = per < left ? per : left;
         left -= L.digit_bits[i];
     }
-    L.sort_tile = kSortThreads * kSortRounds;
+    const bool small = N <= kSmallN;
+    L.sort_tile = kSortThreads * (small ? kSortRoundsSmall : kSortRounds);
     L.sort_blocks = static_cast<int32_t>((N + L.sort_tile - 1) / L.sort_tile);
-    L.rle_tile = kRleTile;
-    L.rle_blocks = static_cast<int32_t>((N + kRleTile - 1) / kRleTile);
+    L.rle_tile = kRleThreads * (small ? kRleItemsSmall : kRleItems);
+    L.rle_blocks = static_cast<int32_t>((N + L.rle_tile - 1) / L.rle_tile);
     const int64_t total_bags = int64_t(p->T) * B;
     int64_t pb = (N + kPrepKeys - 1) / kPrepKeys;   // ~kPrepKeys keys per k_prep block
     if (pb > 1024) pb = 1024;
@@ -604,11 +613,19 @@ __device__ __forceinline__ uint32_t lookback_wave(uint32_t* st, uint32_t tile, u
     return excl;
 }
 
-// In-place exclusive scan of a [kRleItems][kRleThreads / 64] table of counts
+// In-place exclusive scan of a [Q][kRleThreads / 64] table of counts
 // (round-major), by one wavefront; returns the table total on every lane.
+template <int Q>
 __device__ __forceinline__ uint32_t scan_table(uint32_t* tab, int lane)
 {
-    static_assert(kRleItems * (kRleThreads / 64) == 128, "two entries per lane");
+    static_assert(Q * (kRleThreads / 64) == 64 || Q * (kRleThreads / 64) == 128,
+                  "one or two entries per lane");
+    if constexpr (Q * (kRleThreads / 64) == 64) {
+        const uint32_t x1 = tab[lane];
+        const uint32_t inc1 = wave_incl_scan(x1, lane);
+        tab[lane] = inc1 - x1;
+        return __shfl(inc1, 63);
+    }
     const uint32_t x = tab[2 * lane], y = tab[2 * lane + 1];
     const uint32_t inc = wave_incl_scan(x + y, lane);
     const uint32_t ex = inc - x - y;
@@ -656,9 +673,10 @@ __device__ __forceinline__ uint32_t run_end_wave(const uint32_t* __restrict__ ke
     return static_cast<uint32_t>(hi);
 }
 
-// Run-length encode of the sorted keys.  A tile is kRleItems rounds of
+// Run-length encode of the sorted keys.  A tile is Q rounds (kRleItems, or
+// kRleItemsSmall for small batches) of
 // kRleThreads consecutive positions (round q, thread i: position
-// tile*kRleTile + q*kRleThreads + i), so every store of a round is coalesced.
+// tile*Q*kRleThreads + q*kRleThreads + i), so every store of a round is coalesced.
 // Run indices come from per-(round, wave) ballot counts scanned in position
 // order; run lengths from the next head's position (kept in LDS), except for
 // the tile's last run, which one wavefront follows past the tile's end.
@@ -666,7 +684,7 @@ __device__ __forceinline__ uint32_t run_end_wave(const uint32_t* __restrict__ ke
 // id, 2 = payload is (sample id, per-sample weight).  With a payload, each
 // short run's first (sample, weight) is stored next to its record, so a run of
 // one lookup needs no payload load in the segment kernel.
-template <bool API, int FIRST>
+template <bool API, int FIRST, int Q>
 __global__ __launch_bounds__(kRleThreads) void k_rle(
     const uint32_t* __restrict__ keys, const void* __restrict__ payload,
     uint2* __restrict__ short_first, uint32_t N, uint32_t tau, uint32_t chunk, uint32_t ntiles,
@@ -679,8 +697,8 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     uint32_t* __restrict__ long_ids)
 {
     constexpr int NW = kRleThreads / 64;
-    constexpr int Q = kRleItems;
-    __shared__ uint32_t hp[kRleTile + 1];        // head positions in run order
+    constexpr int kTile = kRleThreads * Q;
+    __shared__ uint32_t hp[kTile + 1];           // head positions in run order
     __shared__ uint32_t s_hash[kRleMaxT + 1];
     __shared__ uint32_t cnt[3][Q * NW];          // heads, long runs, chunks per (round, wave)
     __shared__ uint32_t s_tot[3];
@@ -703,8 +721,8 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
         if (tid == 0) atomicOr(err, 2u);
         return;
     }
-    const uint32_t t0 = tile * kRleTile;
-    const uint32_t tend = (N - t0) < uint32_t(kRleTile) ? N : t0 + kRleTile;
+    const uint32_t t0 = tile * kTile;
+    const uint32_t tend = (N - t0) < uint32_t(kTile) ? N : t0 + kTile;
 
     // every load is issued unconditionally (positions past the end are
     // clamped to N-1 and ignored), so all 2-3 x Q of them are in flight at once
@@ -743,7 +761,7 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     }
     __syncthreads();
     if (wave == 0) {
-        const uint32_t tot = scan_table(cnt[0], lane);
+        const uint32_t tot = scan_table<Q>(cnt[0], lane);
         if (lane == 0) {
             s_tot[0] = tot;
             hp[tot] = s_end;
@@ -780,7 +798,7 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     }
     __syncthreads();
     if (wave == 1 || wave == 2) {
-        const uint32_t tot = scan_table(cnt[wave], lane);
+        const uint32_t tot = scan_table<Q>(cnt[wave], lane);
         if (lane == 0) s_tot[wave] = tot;
     }
     __syncthreads();
@@ -946,9 +964,12 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     stage_mark(p, 1, a.stream);
-    static_assert(kSortRounds == 8, "one tile shape is instantiated");
-    e = a.payload_pairs ? sort_passes<kSortRounds, uint2>(a)
-                        : sort_passes<kSortRounds, uint32_t>(a);
+    if (L.sort_tile == kSortThreads * kSortRoundsSmall)
+        e = a.payload_pairs ? sort_passes<kSortRoundsSmall, uint2>(a)
+                            : sort_passes<kSortRoundsSmall, uint32_t>(a);
+    else
+        e = a.payload_pairs ? sort_passes<kSortRounds, uint2>(a)
+                            : sort_passes<kSortRounds, uint32_t>(a);
     if (e != hipSuccess) return e;
     stage_mark(p, 2, a.stream);
 
@@ -956,8 +977,11 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
     const uint32_t tau = static_cast<uint32_t>(p->tuning.tau);
     const uint32_t chunk = static_cast<uint32_t>(p->tuning.chunk);
     const uint32_t nt = static_cast<uint32_t>(L.rle_blocks);
-    auto kern = api_outputs ? k_rle<true, 0>
-                            : (a.payload_pairs ? k_rle<false, 2> : k_rle<false, 1>);
+    const bool sq = L.rle_tile == kRleThreads * kRleItemsSmall;
+    auto kern = api_outputs ? (sq ? k_rle<true, 0, kRleItemsSmall> : k_rle<true, 0, kRleItems>)
+              : a.payload_pairs
+                  ? (sq ? k_rle<false, 2, kRleItemsSmall> : k_rle<false, 2, kRleItems>)
+                  : (sq ? k_rle<false, 1, kRleItemsSmall> : k_rle<false, 1, kRleItems>);
     hipLaunchKernelGGL(kern, dim3(nt), dim3(kRleThreads), 0, a.stream, skeys,
                        static_cast<const void*>(ws + L.off_vals[a.final_buf]),
                        reinterpret_cast<uint2*>(ws + L.off_short_first), N, tau, chunk, nt,
