@@ -22,7 +22,8 @@ uniform ids).  Prints ONE JSON line on stdout.
 * The JSON line also carries "adagrad": the same steps with exact row-wise
   Adagrad in the backward (tbe_backward_adagrad, one fp32 state per row): the
   eager step time, the backward's stage times and its segment kernel's rate;
-  and "mean_pooling": the SGD steps on a mean-pooled plan.
+  "mean_pooling": the SGD steps on a mean-pooled plan; and "int64_indices":
+  the SGD steps with int64 indices and offsets.
 * --report also prints one JSON line per configuration (uniform, mixed, hist,
   stress) with forward / backward stage times on stderr.
 * --calibrate-copy runs a 1 GiB device copy (for scaling rocprofv3 byte
@@ -323,6 +324,24 @@ def mean_pooling_summary(wl, steps, warmup, hip):
                               for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))})
 
 
+def int64_summary(config, nbatches, steps, warmup, hip):
+    """The same workload with int64 indices and offsets (a plan of index type
+    TBE_I64, its own copy of the tables): plain eager step time and the stage
+    times of a run with stage events."""
+    import torch
+    wl = Workload(config, nbatches=nbatches, index_dtype="i64")
+    r = run_steps(wl, steps, warmup, hip)
+    rp = run_plain_steps(wl, steps, warmup)
+    res = dict(step_ms_eager=1e3 * rp["wall_s"] / steps,
+               lookups_per_s=float(np.sum(rp["lookups"])) / rp["wall_s"],
+               fwd_ms=float(np.mean(r["fwd_ms"])), bwd_ms=float(np.mean(r["bwd_ms"])),
+               bwd_stage_us={k: round(1e3 * float(v), 2)
+                             for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))})
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def capture_steps(wl):
     """One HIP graph per batch, each holding that batch's whole step (forward,
     then backward-SGD: the library's kernels only, no host work)."""
@@ -615,6 +634,7 @@ def main():
                roofline=roof, adagrad=ada, mean_pooling=mean)
     del wl
     torch.cuda.empty_cache()
+    out["int64_indices"] = int64_summary(args.config, args.batches, args.steps, args.warmup, hip)
     if args.report:
         report_configs(max(10, args.steps // 2), 3, hip)
     if not args.no_cpu:
