@@ -2,12 +2,19 @@
 """Benchmark of the TBE hot path on one MI355X.
 
 One step = forward pooled sum + backward with exact SGD over one batch of the
-uniform workload (8 tables x 1M rows x D=128 fp32, B=2048, Poisson(20) bags,
-uniform ids).  Prints ONE JSON line on stdout.
+mixed production-like workload (40 features, rows log-uniform in 1e4..1e7,
+D in {64, 128, 256} fp16, B = 4096, geometric(30) bags capped at 500,
+Zipf(1.1) ids, per-sample weights on 20 features; 4.93M lookups per batch),
+the largest configuration this operator is measured on.  Prints ONE JSON line
+on stdout; the uniform workload (8 x 1M-row D=128 fp32 tables, B = 2048,
+Poisson(20) bags) is measured the same way and nested in it.
 
 * Inputs are resident in HBM before the timed region.  Consecutive steps cycle
-  through several distinct batches over the same tables, so no step re-reads
-  the rows of the step before it from cache.
+  through several distinct batches over the same tables ("warm": what a
+  training loop sees; the Zipf-hot rows of one batch are hot in the next).
+  A "cold" run puts an untimed 1 GiB device copy (larger than the 256 MB
+  on-package cache) before each forward and before each backward, so every
+  pass starts with nothing of the previous one in any cache.
 * The step's schedule (--schedule): by default each step (forward, then
   backward-SGD) is launched eagerly on one stream ("eager"); "graph" captures
   each batch's step once in a HIP graph and replays it; "serial" is the eager
@@ -20,12 +27,14 @@ uniform ids).  Prints ONE JSON line on stdout.
   its own stage boundaries (tbe_set_stage_events), so the dominant kernel's
   duration is measured live inside the timed region.
 * The JSON line also carries "adagrad": the same steps with exact row-wise
-  Adagrad in the backward (tbe_backward_adagrad, one fp32 state per row): the
-  eager step time, the backward's stage times and its segment kernel's rate;
-  "mean_pooling": the SGD steps on a mean-pooled plan; and "int64_indices":
-  the SGD steps with int64 indices and offsets.
+  Adagrad in the backward (tbe_backward_adagrad, one fp32 state per row);
+  "mean_pooling": the SGD steps on a mean-pooled plan; "int64_indices": the
+  SGD steps with int64 indices and offsets; and "cpu_baseline": the CPU oracle
+  on a bounded sample of the same workload, on one host thread and on all of
+  the process's host threads (OpenMP).
 * --report also prints one JSON line per configuration (uniform, mixed, hist,
-  stress) with forward / backward stage times on stderr.
+  stress, band, prod) with forward / backward stage times on stderr;
+  --tau / --chunk set the long-run threshold and chunk for a sweep.
 * --calibrate-copy runs a 1 GiB device copy (for scaling rocprofv3 byte
   counters); --summarize-pmc turns rocprofv3 --pmc CSVs into the traffic
   summary under profiles/ that the roofline's "traffic" field reads.
@@ -51,14 +60,20 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_F16_TFLOPS = 2500.0   # dense fp16 matrix peak of an MI355X
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_segment_uniform.json")
 SEGMENT_SRC = os.path.join(ROOT, "pooling_tbe_forward_amd", "csrc", "bwd_segment.hip")
+FLUSH_BYTES = 1 << 30           # the cold runs' cache flush: larger than the 256 MB MALL
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_k_segment_{workload}.json")
+
 
 WORKLOAD_DESC = {
     "uniform": "uniform TBE: T=8 tables x 1,000,000 rows, D=128 fp32, B=2048, "
                "Poisson(20) bags, uniform ids, unweighted, forward + backward exact SGD",
-    "mixed": "mixed TBE: T=40 features, rows log-uniform 1e4..1e7, D in {64,128,256} fp16, "
-             "B=4096, geometric(30) bags capped at 500, Zipf(1.1) ids, 20 weighted features",
+    "mixed": "mixed production-like TBE: T=40 features, rows log-uniform 1e4..1e7, "
+             "D in {64,128,256} fp16, B=4096, geometric(30) bags capped at 500, Zipf(1.1) ids, "
+             "per-sample weights on 20 features, forward + backward exact SGD",
     "hist": "small-table TBE: T=1 x 64 rows, D=128 fp16, B=16384, 256 ids per bag",
     "stress": "run-length stress TBE: T=4 x 1,000,000 rows, D=128 fp32, B=8192, 50 Zipf(1.2) "
               "ids per bag, weighted",
@@ -80,6 +95,13 @@ SCHEDULE_DESC = {
 }
 
 
+def radix_passes(sum_rows):
+    """Radix passes the library's sort makes over keys of ceil(log2 sum_rows)
+    bits (digits of at most 8 bits)."""
+    bits = max(1, int(np.ceil(np.log2(max(2, int(sum_rows))))))
+    return (bits + 7) // 8
+
+
 def algorithmic_bytes(prob):
     """Bytes the method must move (int32 indices), per launch / per pass."""
     s_i = 4
@@ -96,8 +118,7 @@ def algorithmic_bytes(prob):
     lookup_row_bytes = int((prob.dims[tl].astype(np.int64) * s_w).sum())
     out_bytes = prob.B * prob.sum_D * 4
     jag = N * s_i + (TB + 1) * s_i + n_w * 4
-    bits = max(1, int(np.ceil(np.log2(max(2, int(prob.rows.sum()))))))
-    passes = (bits + 7) // 8
+    passes = radix_passes(prob.rows.sum())
     payload = 8 if prob.psw is not None else 4
     sort_bytes = passes * N * (4 + payload) * 2
     run_bytes = uk.size * 16
@@ -147,20 +168,25 @@ class Hip:
 
 
 class Workload:
-    """Device-resident inputs for several batches over one set of tables."""
+    """Device-resident inputs for several batches over one set of tables.
 
-    def __init__(self, name, nbatches, index_dtype="i32"):
+    probs: the batches' host problems (made here when None); tuning: launch
+    knobs for the plan (e.g. tau, chunk)."""
+
+    def __init__(self, name, nbatches, index_dtype="i32", probs=None, tuning=None):
         import torch
         from pooling_tbe_forward_amd import datagen as dg
         from pooling_tbe_forward_amd import tbe
         self.name = name
-        self.probs = [dg.make_problem(name, batch=k) for k in range(nbatches)]
+        self.probs = probs or [dg.make_problem(name, batch=k) for k in range(nbatches)]
         p0 = self.probs[0]
         self.weights = dg.packed_weights_torch(p0, "cuda")
         self.plan = tbe.tbe_plan_create(p0.rows, p0.dims,
                                         tbe.TBE_F32 if p0.wdtype == "f32" else tbe.TBE_F16,
                                         tbe.TBE_I32 if index_dtype == "i32" else tbe.TBE_I64,
                                         weighted=p0.weighted)
+        if tuning:
+            tbe.tbe_set_tuning(self.plan, **tuning)
         it = torch.int32 if index_dtype == "i32" else torch.int64
         self.inputs = []
         for p in self.probs:
@@ -178,7 +204,20 @@ class Workload:
         self.side = torch.cuda.Stream()          # default priority
         self.ev_start = torch.cuda.Event()
         self.ev_ready = torch.cuda.Event()
+        self._flush = None
         torch.cuda.synchronize()
+
+    def flush(self):
+        """An untimed 1 GiB device copy on the current stream: whatever the
+        previous pass left in the L2s and the 256 MB MALL is evicted."""
+        import torch
+        if self._flush is None:
+            a = torch.ones(FLUSH_BYTES // 8, dtype=torch.float32, device="cuda")
+            self._flush = (a, torch.empty_like(a))
+        self._flush[1].copy_(self._flush[0])
+
+    def close(self):
+        self._flush = None
 
     def fwd(self, k, events=None):
         from pooling_tbe_forward_amd import tbe
@@ -231,18 +270,29 @@ class Workload:
                                d["grad"], p.lr, self.ws, stream=main)
 
 
-def run_steps(wl, steps, warmup, hip, overlap=False, adagrad=False):
+def run_steps(wl, steps, warmup, hip, overlap=False, adagrad=False, cold=False):
     """Warm up, then time `steps` steps (synchronize on both sides); per-stage
     HIP events recorded by the library on the streams it runs on.
 
     overlap=False: forward, then the whole backward, on one stream.
     overlap=True: the backward's integer stage (key pass, radix sort, RLE) on a
-    second stream concurrently with the forward, then segment reduce + SGD."""
+    second stream concurrently with the forward, then segment reduce + SGD.
+    cold=True: an untimed cache flush before each forward and each backward
+    (outside the stage events; the wall time then includes the flushes)."""
     import torch
     nb = len(wl.probs)
     bwd = wl.bwd_adagrad if adagrad else wl.bwd
-    one = (lambda k, fe=None, be=None: wl.step_overlapped(k, hip, fe, be)) if overlap else \
-        (lambda k, fe=None, be=None: (wl.fwd(k, fe), bwd(k, be)))
+    fl = wl.flush if cold else (lambda: None)
+
+    def one(k, fe=None, be=None):
+        if overlap:
+            wl.step_overlapped(k, hip, fe, be)
+            return
+        fl()
+        wl.fwd(k, fe)
+        fl()
+        bwd(k, be)
+
     for s in range(warmup):
         one(s % nb)
     torch.cuda.synchronize()
@@ -290,6 +340,10 @@ def run_plain_steps(wl, steps, warmup, adagrad=False):
     return dict(wall_s=wall, lookups=np.array([wl.bytes[k]["N"] for k in ks], dtype=np.float64))
 
 
+def stage_us(r):
+    return {k: round(1e3 * float(v), 2) for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))}
+
+
 def adagrad_summary(wl, steps, warmup, hip):
     """The same steps with row-wise Adagrad in the backward: plain eager step
     time, and the backward's stage times and segment-kernel rate from a run
@@ -300,9 +354,7 @@ def adagrad_summary(wl, steps, warmup, hip):
     seg_gbps = float(np.mean(r["seg_bytes"])) / (seg_us * 1e-6) / 1e9
     return dict(step_ms_eager=1e3 * rp["wall_s"] / steps,
                 lookups_per_s=float(np.sum(rp["lookups"])) / rp["wall_s"],
-                bwd_ms=float(np.mean(r["bwd_ms"])),
-                bwd_stage_us={k: round(1e3 * float(v), 2)
-                              for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))},
+                bwd_ms=float(np.mean(r["bwd_ms"])), bwd_stage_us=stage_us(r),
                 segment_gbps_min=round(seg_gbps, 1),
                 segment_pct_peak=round(100 * seg_gbps / PEAK_HBM_GBPS, 2))
 
@@ -320,23 +372,21 @@ def mean_pooling_summary(wl, steps, warmup, hip):
     return dict(step_ms_eager=1e3 * rp["wall_s"] / steps,
                 lookups_per_s=float(np.sum(rp["lookups"])) / rp["wall_s"],
                 fwd_ms=float(np.mean(r["fwd_ms"])), bwd_ms=float(np.mean(r["bwd_ms"])),
-                bwd_stage_us={k: round(1e3 * float(v), 2)
-                              for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))})
+                bwd_stage_us=stage_us(r))
 
 
-def int64_summary(config, nbatches, steps, warmup, hip):
-    """The same workload with int64 indices and offsets (a plan of index type
+def int64_summary(config, probs, steps, warmup, hip):
+    """The same batches with int64 indices and offsets (a plan of index type
     TBE_I64, its own copy of the tables): plain eager step time and the stage
     times of a run with stage events."""
     import torch
-    wl = Workload(config, nbatches=nbatches, index_dtype="i64")
+    wl = Workload(config, len(probs), index_dtype="i64", probs=probs)
     r = run_steps(wl, steps, warmup, hip)
     rp = run_plain_steps(wl, steps, warmup)
     res = dict(step_ms_eager=1e3 * rp["wall_s"] / steps,
                lookups_per_s=float(np.sum(rp["lookups"])) / rp["wall_s"],
                fwd_ms=float(np.mean(r["fwd_ms"])), bwd_ms=float(np.mean(r["bwd_ms"])),
-               bwd_stage_us={k: round(1e3 * float(v), 2)
-                             for k, v in zip(BWD_STAGES, r["stage_ms"].mean(axis=0))})
+               bwd_stage_us=stage_us(r))
     del wl
     torch.cuda.empty_cache()
     return res
@@ -376,65 +426,95 @@ def run_graph_steps(wl, graphs, steps, warmup):
     return dict(wall_s=wall, lookups=np.array([wl.bytes[k]["N"] for k in ks], dtype=np.float64))
 
 
-def cpu_baseline(budget_s=20.0):
-    """The CPU oracle, as it stands, on the uniform workload's batch 0:
-    forward of every bag, the integer stage, and backward-SGD of every touched
-    row (rows are regenerated on the host for the touched ids only; that set-up
-    is not timed).  Repeated while within the time budget."""
-    import oracle
-    from pooling_tbe_forward_amd import datagen as dg
-    prob = dg.make_problem("uniform")
-    rowsets = []
-    for t in range(prob.T):
-        s, e = prob.offsets[t * prob.B], prob.offsets[(t + 1) * prob.B]
-        rowsets.append(np.unique(prob.indices[s:e]))
-    tabs = [(ids, np.ascontiguousarray(dg.weight_rows(prob, t, ids).reshape(-1)))
-            for t, ids in enumerate(rowsets)]
-    code = oracle.F32
-    reps, total = 0, 0.0
-    stage = dict(forward=0.0, sort_rle=0.0, backward=0.0)
-    while total < budget_s and reps < 50:
-        t0 = time.perf_counter()
-        oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
-                       prob.offsets, prob.psw, prob.weighted)
-        t1 = time.perf_counter()
-        r = oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, 64)
-        t2 = time.perf_counter()
-        oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
-                            prob.offsets, prob.psw, prob.weighted, prob.grad, prob.lr,
-                            r["unique_keys"])
-        t3 = time.perf_counter()
-        stage["forward"] += t1 - t0
-        stage["sort_rle"] += t2 - t1
-        stage["backward"] += t3 - t2
-        total += t3 - t0
-        reps += 1
+def host_cpu():
     cpu = platform.processor() or platform.machine()
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return dict(value=prob.N * reps / total, unit="lookups/s", cores=1, kind="oracle",
-                sample=f"full uniform step (forward all {prob.T * prob.B} bags, sort+RLE of "
-                       f"{prob.N} lookups, backward-SGD of every touched row), batch 0, "
-                       f"{reps} repetition(s), single thread, fp64 accumulation",
-                ms_per_step=1e3 * total / reps,
-                stage_ms={k: 1e3 * v / reps for k, v in stage.items()},
-                host_cpu=cpu, host_threads=os.cpu_count())
+    return cpu
+
+
+def host_threads():
+    """Threads this process may use: its CPU affinity, at most 16 (the host
+    share of one GPU on the machines this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(config="mixed", budget_s=20.0, samples=256):
+    """The CPU oracle, as it stands, on a bounded sample of the workload:
+    samples 0..samples-1 of every feature of batch 0 (forward of those bags,
+    the integer stage over their lookups, backward-SGD of every row they
+    touch; the touched rows are regenerated on the host, untimed).  Timed on
+    one host thread and again with the oracle's OpenMP loops on every thread
+    the process may use, each leg repeated within about half the budget."""
+    import oracle
+    from pooling_tbe_forward_amd import datagen as dg
+    full = dg.make_problem(config)
+    prob = dg.sample_prefix(full, samples)
+    tl = prob.table_of_lookup()
+    rowsets = [np.unique(prob.indices[tl == t]) for t in range(prob.T)]
+    tabs = [(ids, np.ascontiguousarray(dg.weight_rows(prob, t, ids).reshape(-1)))
+            for t, ids in enumerate(rowsets)]
+    code = oracle.F32 if prob.wdtype == "f32" else oracle.F16
+
+    def leg(threads, budget):
+        oracle.set_threads(threads)
+        reps, total = 0, 0.0
+        stage = dict(forward=0.0, sort_rle=0.0, backward=0.0)
+        while total < budget and reps < 50:
+            t0 = time.perf_counter()
+            oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
+                           prob.offsets, prob.psw, prob.weighted)
+            t1 = time.perf_counter()
+            r = oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, 128)
+            t2 = time.perf_counter()
+            oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
+                                prob.offsets, prob.psw, prob.weighted, prob.grad, prob.lr,
+                                r["unique_keys"])
+            t3 = time.perf_counter()
+            stage["forward"] += t1 - t0
+            stage["sort_rle"] += t2 - t1
+            stage["backward"] += t3 - t2
+            total += t3 - t0
+            reps += 1
+        return dict(value=prob.N * reps / total, cores=threads, reps=reps,
+                    ms_per_step=1e3 * total / reps,
+                    stage_ms={k: round(1e3 * v / reps, 3) for k, v in stage.items()})
+
+    nthr = host_threads()
+    try:
+        one = leg(1, budget_s / 2)
+        many = leg(nthr, budget_s / 2) if nthr > 1 else one
+    finally:
+        oracle.set_threads(1)
+    return dict(value=many["value"], unit="lookups/s", cores=many["cores"], kind="oracle",
+                sample=f"{config} batch 0, samples 0..{prob.B - 1} of all {prob.T} features "
+                       f"({prob.T * prob.B} bags, {prob.N} lookups, {sum(r.size for r in rowsets)} "
+                       f"distinct rows): forward of every bag, sort+RLE of every lookup, "
+                       f"backward-SGD of every touched row; fp64 accumulation; value = the "
+                       f"OpenMP leg",
+                ms_per_step=many["ms_per_step"], stage_ms=many["stage_ms"], reps=many["reps"],
+                single_thread=one, host_cpu=host_cpu(), host_threads=nthr,
+                nproc=os.cpu_count())
 
 
 def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per k_segment launch from the committed PMC summary, or None
-    when the kernel source changed since the counters were taken."""
+def measured_traffic(workload):
+    """HBM bytes per k_segment launch from the committed PMC summary of this
+    workload, or None when the kernel source changed since the counters were
+    taken (or there is no summary)."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if t.get("source_sha256_16") != source_hash(SEGMENT_SRC):
@@ -445,13 +525,60 @@ def measured_traffic():
 def summarize(r):
     f = float(np.mean(r["fwd_ms"]))
     b = float(np.mean(r["bwd_ms"]))
-    st = r["stage_ms"].mean(axis=0)
     lk = float(np.mean(r["lookups"]))
-    return dict(fwd_ms=f, bwd_ms=b, fwd_lookups_per_s=lk / (f * 1e-3),
-                bwd_lookups_per_s=lk / (b * 1e-3),
-                fwd_hbm_gbps_min=float(np.mean(r["fwd_bytes"])) / (f * 1e-3) / 1e9,
-                bwd_hbm_gbps_min=float(np.mean(r["bwd_bytes"])) / (b * 1e-3) / 1e9,
-                bwd_stage_us={k: round(1e3 * float(v), 2) for k, v in zip(BWD_STAGES, st)})
+    out = dict(fwd_ms=f, bwd_ms=b, fwd_lookups_per_s=lk / (f * 1e-3),
+               bwd_lookups_per_s=lk / (b * 1e-3),
+               fwd_hbm_gbps_min=float(np.mean(r["fwd_bytes"])) / (f * 1e-3) / 1e9,
+               bwd_hbm_gbps_min=float(np.mean(r["bwd_bytes"])) / (b * 1e-3) / 1e9,
+               bwd_stage_us=stage_us(r))
+    out["fwd_pct_peak"] = 100 * out["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS
+    out["bwd_pct_peak"] = 100 * out["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS
+    return out
+
+
+def segment_roofline(r, workload):
+    """Roofline entry of the dominant kernel, k_segment: its algorithmic bytes
+    per launch over its average launch time from the library's stage events."""
+    seg_us = float(np.mean(r["stage_ms"][:, 3])) * 1e3
+    seg_bytes = float(np.mean(r["seg_bytes"]))
+    seg_gbps = seg_bytes / (seg_us * 1e-6) / 1e9
+    return dict(bound="hbm", kernel="k_segment (backward segment-reduce + SGD)",
+                achieved=round(seg_gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                frac=round(seg_gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(workload),
+                avg_launch_us=round(seg_us, 2), bytes_per_launch=int(seg_bytes))
+
+
+def measure(wl, steps, warmup, hip, schedule, extras=True):
+    """Every schedule of one workload, plus the cold run; returns the fields
+    of its JSON object."""
+    r_serial = run_steps(wl, steps, warmup, hip)
+    r_over = run_steps(wl, steps, warmup, hip, overlap=True)
+    r_graph = run_graph_steps(wl, capture_steps(wl), steps, warmup)
+    r_eager = run_plain_steps(wl, steps, warmup)
+    r_cold = run_steps(wl, max(5, steps // 2), 2, hip, cold=True)
+    wl.close()
+    r = dict(serial=r_serial, overlap=r_over, graph=r_graph, eager=r_eager)[schedule]
+    p0 = wl.probs[0]
+    cold = summarize(r_cold)
+    out = dict(step_ms=1e3 * r["wall_s"] / steps,
+               lookups_per_s=float(np.sum(r["lookups"])) / r["wall_s"],
+               lookups_per_step=int(np.mean(r["lookups"])), T=int(p0.T), B=int(p0.B),
+               ms_per_step_serial=1e3 * r_serial["wall_s"] / steps,
+               ms_per_step_overlap=1e3 * r_over["wall_s"] / steps,
+               ms_per_step_graph=1e3 * r_graph["wall_s"] / steps,
+               ms_per_step_eager=1e3 * r_eager["wall_s"] / steps,
+               **summarize(r_serial),
+               roofline=segment_roofline(r_serial, wl.name),
+               cold=dict(note="1 GiB device copy before each forward and each backward, outside "
+                              "the stage events", fwd_ms=cold["fwd_ms"], bwd_ms=cold["bwd_ms"],
+                         fwd_pct_peak=cold["fwd_pct_peak"], bwd_pct_peak=cold["bwd_pct_peak"],
+                         bwd_stage_us=cold["bwd_stage_us"],
+                         segment_roofline=segment_roofline(r_cold, wl.name)))
+    out["overlap_stage_us"] = stage_us(r_over)
+    if extras:
+        out["adagrad"] = adagrad_summary(wl, steps, warmup, hip)
+        out["mean_pooling"] = mean_pooling_summary(wl, steps, warmup, hip)
+    return out
 
 
 def hist_mfma_flops(wl):
@@ -472,26 +599,18 @@ def hist_mfma_flops(wl):
     return flops
 
 
-def report_configs(steps, warmup, hip):
+def report_configs(names, steps, warmup, hip, tuning=None):
+    """One JSON line per configuration on stderr (stage times, per-pass % of
+    peak, every schedule)."""
     import torch
-    for name in ("uniform", "mixed", "hist", "stress", "band", "prod"):
-        wl = Workload(name, nbatches={"mixed": 2, "prod": 1}.get(name, 3))
-        r = run_steps(wl, steps, warmup, hip)
-        r2 = run_steps(wl, steps, warmup, hip, overlap=True)
-        r3 = run_graph_steps(wl, capture_steps(wl), steps, warmup)
-        r4 = run_plain_steps(wl, steps, warmup)
-        a = adagrad_summary(wl, steps, warmup, hip)
-        line = dict(config=name, N=wl.bytes[0]["N"], unique_rows=wl.bytes[0]["unique_rows"],
-                    step_ms_eager=1e3 * r4["wall_s"] / steps,
-                    adagrad=a,
-                    step_ms_graph=1e3 * r3["wall_s"] / steps,
-                    step_ms_serial=1e3 * r["wall_s"] / steps,
-                    step_ms_overlap=1e3 * r2["wall_s"] / steps,
+    for name in names:
+        wl = Workload(name, nbatches={"prod": 1}.get(name, 3), tuning=tuning)
+        line = dict(config=name, tuning=tuning or {}, N=wl.bytes[0]["N"],
+                    unique_rows=wl.bytes[0]["unique_rows"],
                     fwd_bytes_min=wl.bytes[0]["fwd_min"],
                     fwd_bytes_lookup=wl.bytes[0]["fwd_lookup"],
-                    bwd_bytes_min=wl.bytes[0]["bwd_min"], **summarize(r))
-        line["fwd_pct_peak"] = 100 * line["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS
-        line["bwd_pct_peak"] = 100 * line["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS
+                    bwd_bytes_min=wl.bytes[0]["bwd_min"],
+                    **measure(wl, steps, warmup, hip, "eager", extras=tuning is None))
         hist_flops = hist_mfma_flops(wl)
         if hist_flops:   # counts x table on the matrix unit (fp16 in, fp32 accumulate)
             tf = hist_flops / (line["fwd_ms"] * 1e-3) / 1e12
@@ -527,21 +646,22 @@ def _kernel_avg(rows, pattern, counter):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out, command):
-    """Per-launch HBM bytes of k_segment from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by the ratio of a 1 GiB copy's known bytes to what
-    the same counter reported for it."""
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out, command, workload):
+    """Per-launch HBM bytes of the library's kernels from FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled by the ratio of a 1 GiB copy's
+    known bytes to what the same counter reported for it."""
     copy_pat = r"copyBuffer|direct_copy"
     cf, _ = _kernel_avg(_pmc_rows(copy_fetch_dir), copy_pat, "FETCH_SIZE")
     cw, _ = _kernel_avg(_pmc_rows(copy_write_dir), copy_pat, "WRITE_SIZE")
     gib_kib = float(1 << 20)
     f_scale = gib_kib / cf if cf else None
     w_scale = gib_kib / cw if cw else None
-    res = dict(kernel="k_segment", workload="uniform", command=command,
+    res = dict(kernel="k_segment", workload=workload, command=command,
                copy_fetch_kib=cf, copy_write_kib=cw, fetch_scale=f_scale, write_scale=w_scale,
                source_sha256_16=source_hash(SEGMENT_SRC), kernels={})
     fetch_rows, write_rows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     for name, pat in [("k_segment", r"k_segment"), ("k_fwd_gather", r"k_fwd_gather"),
+                      ("k_fwd_hist", r"k_fwd_hist"),
                       ("k_onesweep", r"k_onesweep"), ("k_rle", r"k_rle"),
                       ("k_prep", r"k_prep"), ("k_long_combine", r"k_long_combine")]:
         fv, nf = _kernel_avg(fetch_rows, pat, "FETCH_SIZE")
@@ -563,18 +683,26 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batches", type=int, default=4)
     ap.add_argument("--schedule", default="eager", choices=sorted(SCHEDULE_DESC))
-    ap.add_argument("--config", default="uniform", choices=sorted(WORKLOAD_DESC))
+    ap.add_argument("--config", default="mixed", choices=sorted(WORKLOAD_DESC))
+    ap.add_argument("--secondary", default="uniform",
+                    help="workload measured the same way and nested in the line ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--report", action="store_true",
                     help="also print per-configuration measurements on stderr")
+    ap.add_argument("--report-configs", default="uniform,mixed,hist,stress,band,prod")
+    ap.add_argument("--tau", type=int, default=0, help="long-run threshold for --report")
+    ap.add_argument("--chunk", type=int, default=0, help="long-run chunk for --report")
+    ap.add_argument("--quick", action="store_true",
+                    help="the headline workload's eager steps only (for profilers)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"))
-    ap.add_argument("--pmc-out", default=TRAFFIC_FILE)
+    ap.add_argument("--pmc-workload", default="mixed")
     ap.add_argument("--pmc-command", default="")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.pmc_out, args.pmc_command)
+        summarize_pmc(*args.summarize_pmc, traffic_file(args.pmc_workload), args.pmc_command,
+                      args.pmc_workload)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this operator's hot path runs on a single "
@@ -592,53 +720,46 @@ def main():
         calibrate_copy()
         return
     hip = Hip()
+    tuning = {k: v for k, v in (("tau", args.tau), ("chunk", args.chunk)) if v}
 
-    wl = Workload(args.config, nbatches=args.batches)
-    # the reported step is --schedule's; the others are timed too, for the
-    # per-stage breakdown (stage events of the serial run) and as cross-checks
-    r_serial = run_steps(wl, args.steps, args.warmup, hip, overlap=False)
-    r_over = run_steps(wl, args.steps, args.warmup, hip, overlap=True)
-    r_graph = run_graph_steps(wl, capture_steps(wl), args.steps, args.warmup)
-    r_eager = run_plain_steps(wl, args.steps, args.warmup)
-    ada = adagrad_summary(wl, args.steps, args.warmup, hip)
-    mean = mean_pooling_summary(wl, args.steps, args.warmup, hip)
-    r = dict(serial=r_serial, overlap=r_over, graph=r_graph, eager=r_eager)[args.schedule]
-    step_ms = 1e3 * r["wall_s"] / args.steps
-    lookups = float(np.sum(r["lookups"]))
-    value = lookups / r["wall_s"]
-    sm = summarize(r_serial)
-    p0 = wl.probs[0]
-    # the dominant kernel's duration: stage events of the eagerly launched steps
-    seg_us = float(np.mean(r_serial["stage_ms"][:, 3])) * 1e3
-    seg_bytes = float(np.mean(r_serial["seg_bytes"]))
-    seg_gbps = seg_bytes / (seg_us * 1e-6) / 1e9
-    roof = dict(bound="hbm", kernel="k_segment (backward segment-reduce + SGD)",
-                achieved=round(seg_gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                frac=round(seg_gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(),
-                avg_launch_us=round(seg_us, 2), bytes_per_launch=int(seg_bytes))
+    if args.report:
+        report_configs([c for c in args.report_configs.split(",") if c], max(10, args.steps // 2),
+                       3, hip, tuning or None)
+        return
+
+    wl = Workload(args.config, nbatches=args.batches, tuning=tuning or None)
+    if args.quick:
+        r = run_plain_steps(wl, args.steps, args.warmup)
+        print(json.dumps(dict(config=args.config, steps=args.steps,
+                              ms_per_step=1e3 * r["wall_s"] / args.steps)), flush=True)
+        return
+    m = measure(wl, args.steps, args.warmup, hip, args.schedule)
+    probs = wl.probs
+    p0 = probs[0]
     out = dict(metric="TBE fwd/bwd lookups/s and achieved HBM GB/s (% of peak) on 1 MI355X",
-               value=value, unit="lookups/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-               ms_per_step=step_ms, higher_is_better=True, scaling="weak", vs_baseline=None,
-               dtype="f32", data="synthetic",
-               config=dict(workload=WORKLOAD_DESC[args.config], T=int(p0.T), B=int(p0.B),
-                           lookups_per_step=int(np.mean(r["lookups"])),
+               value=m.pop("lookups_per_s"), unit="lookups/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=m.pop("step_ms"), higher_is_better=True,
+               scaling="weak", vs_baseline=None,
+               dtype="f16 weights, f32 accumulate" if p0.wdtype == "f16" else "f32",
+               data="synthetic",
+               config=dict(workload=WORKLOAD_DESC[args.config], T=m.pop("T"), B=m.pop("B"),
+                           lookups_per_step=m.pop("lookups_per_step"),
                            batches_cycled=args.batches, index_dtype="int32",
-                           parallelism="single GPU"),
-               schedule=SCHEDULE_DESC[args.schedule],
-               ms_per_step_serial=1e3 * r_serial["wall_s"] / args.steps,
-               ms_per_step_overlap=1e3 * r_over["wall_s"] / args.steps,
-               ms_per_step_graph=1e3 * r_graph["wall_s"] / args.steps,
-               ms_per_step_eager=1e3 * r_eager["wall_s"] / args.steps,
-               fwd_pct_peak=100 * sm["fwd_hbm_gbps_min"] / PEAK_HBM_GBPS,
-               bwd_pct_peak=100 * sm["bwd_hbm_gbps_min"] / PEAK_HBM_GBPS, **sm,
-               roofline=roof, adagrad=ada, mean_pooling=mean)
+                           weight_dtype=p0.wdtype, parallelism="single GPU"),
+               schedule=SCHEDULE_DESC[args.schedule], **m)
     del wl
     torch.cuda.empty_cache()
-    out["int64_indices"] = int64_summary(args.config, args.batches, args.steps, args.warmup, hip)
-    if args.report:
-        report_configs(max(10, args.steps // 2), 3, hip)
+    out["int64_indices"] = int64_summary(args.config, probs, args.steps, args.warmup, hip)
+    del probs
+    if args.secondary:
+        wl2 = Workload(args.secondary, nbatches=args.batches)
+        m2 = measure(wl2, args.steps, args.warmup, hip, args.schedule, extras=False)
+        m2["workload"] = WORKLOAD_DESC[args.secondary]
+        out[args.secondary] = m2
+        del wl2
+        torch.cuda.empty_cache()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

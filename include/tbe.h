@@ -72,11 +72,22 @@ typedef struct {
     int32_t reserved[10];
 } tbe_tuning;
 
+/* Bits of a backward workspace's error word (tbe_workspace_status; also
+ * counts[4] of tbe_sort_view).  The word is sticky: a bit stays set until
+ * tbe_workspace_init.  Any bit set means that the calls made on the workspace
+ * since then may have left invalid results (weights, state, sort outputs). */
+#define TBE_WS_ERR_LOOKBACK 1u  /* a look-back wait of the sort or run-length encode
+                                   gave up (a predecessor never published) */
+#define TBE_WS_ERR_CONTROL 2u   /* a call found the control block uninitialised */
+#define TBE_WS_ERR_PAYLOAD 4u   /* tbe_backward_apply(_adagrad) was told `weighted`
+                                   unlike what tbe_backward_prepare stored; that
+                                   apply did nothing */
+
 /* Device pointers into a backward workspace (valid until the workspace is
  * reused).  Every count lives in device memory: counts[0] = number of runs,
  * counts[1] = short runs, counts[2] = long runs, counts[3] = long-run chunks,
- * counts[4] = error word (nonzero: the call's results are invalid; it stays
- * set until tbe_workspace_init). */
+ * counts[4] = error word (TBE_WS_ERR_* bits), counts[5] = payload mode of the
+ * last integer stage (library-internal). */
 typedef struct {
     uint32_t* sorted_keys;   /* [N]   keys ascending; ties keep lookup order        */
     uint32_t* sorted_pos;    /* [N]   lookup position j of each sorted entry        */
@@ -85,7 +96,7 @@ typedef struct {
     uint32_t* run_len;       /* [N]   lookups in each run                           */
     uint32_t* short_runs;    /* [N]   run ids with len < tau, ascending             */
     uint32_t* long_runs;     /* [N]   run ids with len >= tau, ascending            */
-    uint32_t* counts;        /* [5]                                                 */
+    uint32_t* counts;        /* [6]                                                 */
 } tbe_sort_view;
 
 /*
@@ -174,8 +185,11 @@ tbe_status tbe_backward_sgd(const tbe_plan* plan, int32_t B, void* weights,
  * tbe_backward_apply: segment reduce + exact SGD from a workspace that
  * tbe_backward_prepare filled for the same plan, B and num_indices, with the
  * plan's tuning unchanged in between.  weighted: nonzero iff prepare was
- * given per-sample weights.  The caller orders apply after prepare (same
- * stream, or an event); errors as for tbe_backward_sgd.
+ * given per-sample weights.  The workspace records which payload prepare
+ * stored; if `weighted` disagrees with it (or no prepare ran since
+ * tbe_workspace_init), apply updates nothing and sets TBE_WS_ERR_PAYLOAD in
+ * the workspace's error word (tbe_workspace_status).  The caller orders apply
+ * after prepare (same stream, or an event); errors as for tbe_backward_sgd.
  */
 tbe_status tbe_backward_prepare(const tbe_plan* plan, int32_t B, const void* indices,
                                 int64_t num_indices, const void* offsets,
@@ -218,23 +232,51 @@ tbe_status tbe_backward_apply_adagrad(const tbe_plan* plan, int32_t B, int64_t n
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The backward's integer stage alone: linearize, stable radix sort,
- * run-length encode, classify against tuning.tau.  Fills *view (host struct)
- * with device pointers into the workspace.
+ * The backward's integer stage alone (section "Why the backward is the hard
+ * half": the backward inverts the batch -- every lookup gets the key
+ * hash_size_cumsum[t] + row, the keys are sorted so each row's contributors
+ * sit next to each other, and a run-length encode makes each row one unit of
+ * work; the article's Triton backward gets this from one native op that
+ * linearizes, radix-sorts and run-length encodes.  The split of runs by length
+ * is section "Three tiers, routed by run length").  The sort is stable (ties
+ * in lookup order) and its payload is the lookup position j, so sorted_pos is
+ * the stable permutation.  Arguments as for tbe_backward_sgd; fills *view
+ * (host struct) with device pointers into the workspace, valid until the
+ * workspace is used again.  Runs with length >= tuning.tau are listed as long.
+ * Errors: TBE_EINVAL (NULL view, or as for tbe_backward_sgd), TBE_ERANGE,
+ * TBE_EHIP.  Device-side failures set the error word (counts[4]).
  */
 tbe_status tbe_sort_rle(const tbe_plan* plan, int32_t B, const void* indices,
                         int64_t num_indices, const void* offsets, void* workspace,
                         size_t workspace_bytes, tbe_sort_view* view, void* stream);
 
 /*
- * Device-side input check: *error_count (device int64, overwritten) receives
- * the number of violations: offsets[0] != 0, decreasing offsets,
- * offsets[T*B] != num_indices, ids outside [0, rows[t]).  The caller syncs
- * the stream to read it.
+ * Device-side input check (section "Why the backward is the hard half" names
+ * bounds checking of the indices as a separate native op run outside the
+ * fused path; the preconditions are those of the input format in section "A
+ * lookup table that is most of the model").  *error_count (device int64,
+ * caller-owned, overwritten) receives the number of violations:
+ * offsets[0] != 0, a decreasing offset step, offsets[T*B] != num_indices, and
+ * each id outside [0, rows[t]).  Nothing is clamped or skipped, and every
+ * read stays in bounds even on bad input.  The caller syncs the stream to read
+ * the count.  Errors: TBE_EINVAL (NULL plan or error_count, negative sizes,
+ * NULL indices/offsets where needed), TBE_ERANGE, TBE_EHIP.
  */
 tbe_status tbe_bounds_check(const tbe_plan* plan, int32_t B, const void* indices,
                             int64_t num_indices, const void* offsets,
                             int64_t* error_count, void* stream);
+
+/*
+ * Error word of a backward workspace (TBE_WS_ERR_* bits; 0 = every call on
+ * the workspace since tbe_workspace_init ran normally), copied to
+ * *error_word, a caller-owned 4-byte-aligned device uint32, on `stream`, after
+ * the work already enqueued there; the caller syncs to read it.  The word
+ * itself sits at byte offset 48 of the workspace.  Nothing is cleared.
+ * Errors: TBE_EINVAL (NULL or misaligned pointers, a workspace smaller than
+ * its control block), TBE_EHIP.
+ */
+tbe_status tbe_workspace_status(const void* workspace, size_t workspace_bytes,
+                                uint32_t* error_word, void* stream);
 
 /* Read / replace the plan's launch knobs (values are validated). */
 tbe_status tbe_get_tuning(const tbe_plan* plan, tbe_tuning* tuning);

@@ -34,7 +34,7 @@ def build(force: bool = False) -> str:
             and os.path.getmtime(_SO) >= max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))):
         return _SO
     tmp = _SO + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-fPIC", "-shared",
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-fPIC", "-shared", "-fopenmp",
                            _SRC, "-o", tmp, "-lm"])
     os.replace(tmp, _SO)
     return _SO
@@ -63,6 +63,8 @@ def lib():
                                               ctypes.c_int32, P, P, P, P, P, P, ctypes.c_float,
                                               ctypes.c_float, P, ctypes.c_int64, P, P, P, P,
                                               ctypes.c_int32, ctypes.c_int32]
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = ctypes.c_int
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
         L.oracle_double_to_half.argtypes = [ctypes.c_double]
@@ -237,6 +239,12 @@ def backward_adagrad(T, B, rows, dims, wdtype, tables, indices, offsets, psw, we
                                          POOLING[pooling]))
     del keep
     return gr, nr, s_out
+
+
+def set_threads(n: int) -> int:
+    """Host threads for forward and backward (1 = single-threaded, the
+    default); results are the same bits for any count."""
+    return int(lib().oracle_set_threads(int(n)))
 
 
 def half_to_double(bits):

@@ -8,6 +8,22 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 1;
+
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    g_threads = n < 1 ? 1 : n;
+#else
+    (void)n;
+    g_threads = 1;
+#endif
+    return g_threads;
+}
 
 /* ---------------------------------------------------------------------- */
 /* IEEE 754 binary16 (1 sign bit, 5 exponent bits with bias 15, 10 fraction
@@ -152,6 +168,12 @@ int oracle_forward(int32_t T, int32_t B, const int64_t* rows, const int32_t* dim
     for (int64_t k = 0; k < count; ++k) {
         int64_t bag = bag_list ? bag_list[k] : k;
         if (bag < 0 || bag >= (int64_t)T * B) { free(Doff); return 1; }
+    }
+    int err = 0;
+    /* bags are independent: each output element is written by one thread */
+#pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t k = 0; k < count; ++k) {
+        int64_t bag = bag_list ? bag_list[k] : k;
         int32_t t = (int32_t)(bag / B);
         int64_t b = bag % B;
         int32_t D = dims[t];
@@ -160,7 +182,11 @@ int oracle_forward(int32_t T, int32_t B, const int64_t* rows, const int32_t* dim
             dst[d] = 0.0;                              /* an empty bag pools to zero */
         for (int64_t j = offsets[bag]; j < offsets[bag + 1]; ++j) {
             int64_t pos = held_row(&tables[t], indices[j]);
-            if (pos < 0) { free(Doff); return 3; }
+            if (pos < 0) {
+#pragma omp atomic write
+                err = 3;
+                break;
+            }
             double w = (psw && (!weighted || weighted[t])) ? (double)psw[j] : 1.0;
             for (int32_t d = 0; d < D; ++d)
                 dst[d] += w * load_elem(tables[t].data, pos * D + d, wdtype);
@@ -171,7 +197,7 @@ int oracle_forward(int32_t T, int32_t B, const int64_t* rows, const int32_t* dim
                 dst[d] /= (double)len;
     }
     free(Doff);
-    return 0;
+    return err;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -283,40 +309,63 @@ int oracle_backward_sgd(int32_t T, int32_t B, const int64_t* rows, const int32_t
     int64_t sumD = Doff[T];
     double* G = (double*)calloc((size_t)(nkeys ? nkeys : 1) * Dmax, sizeof(double));
 
-    for (int32_t t = 0; t < T; ++t) {
-        int32_t D = dims[t];
-        for (int64_t b = 0; b < B; ++b) {
-            int64_t bag = (int64_t)t * B + b;
-            for (int64_t j = offsets[bag]; j < offsets[bag + 1]; ++j) {
-                int64_t key = hcs[t] + indices[j];
-                int64_t lo = 0, hi = nkeys;          /* find key among requested */
-                while (lo < hi) {
-                    int64_t mid = lo + (hi - lo) / 2;
-                    if (keys[mid] < key) lo = mid + 1; else hi = mid;
+    /* Every bag adds each of its lookups' weighted output-gradient slices into
+     * the row the lookup read.  The requested keys are split into contiguous
+     * ranges; a range's rows are summed by one thread, which walks, in lookup
+     * order, the lookups of the tables the range touches (one range = the
+     * whole loop when single-threaded), so every row's sum is in lookup order
+     * whatever the thread count. */
+    int64_t nranges = g_threads > 1 ? (int64_t)g_threads * 8 : 1;
+    if (nranges > nkeys) nranges = nkeys > 0 ? nkeys : 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t q = 0; q < nranges; ++q) {
+        int64_t k0 = nkeys * q / nranges, k1 = nkeys * (q + 1) / nranges;
+        if (k0 >= k1)
+            continue;
+        for (int32_t t = 0; t < T; ++t) {
+            if (hcs[t + 1] <= keys[k0] || hcs[t] > keys[k1 - 1])
+                continue;                            /* no key of this range in table t */
+            int32_t D = dims[t];
+            for (int64_t b = 0; b < B; ++b) {
+                int64_t bag = (int64_t)t * B + b;
+                for (int64_t j = offsets[bag]; j < offsets[bag + 1]; ++j) {
+                    int64_t key = hcs[t] + indices[j];
+                    int64_t lo = k0, hi = k1;        /* find key among this range's */
+                    while (lo < hi) {
+                        int64_t mid = lo + (hi - lo) / 2;
+                        if (keys[mid] < key) lo = mid + 1; else hi = mid;
+                    }
+                    if (lo >= k1 || keys[lo] != key)
+                        continue;
+                    double w = (psw && (!weighted || weighted[t])) ? (double)psw[j] : 1.0;
+                    if (pooling == ORACLE_POOL_MEAN)
+                        w /= (double)(offsets[bag + 1] - offsets[bag]);
+                    const float* g = grad_output + b * sumD + Doff[t];
+                    double* acc = G + lo * Dmax;
+                    for (int32_t d = 0; d < D; ++d)
+                        acc[d] += w * (double)g[d];
                 }
-                if (lo >= nkeys || keys[lo] != key)
-                    continue;
-                double w = (psw && (!weighted || weighted[t])) ? (double)psw[j] : 1.0;
-                if (pooling == ORACLE_POOL_MEAN)
-                    w /= (double)(offsets[bag + 1] - offsets[bag]);
-                const float* g = grad_output + b * sumD + Doff[t];
-                double* acc = G + lo * Dmax;
-                for (int32_t d = 0; d < D; ++d)
-                    acc[d] += w * (double)g[d];
             }
         }
     }
 
     rc = 0;
-    for (int64_t k = 0; k < nkeys && rc == 0; ++k) {
+    for (int64_t k = 0; k < nkeys; ++k)
+        if (keys[k] < 0 || keys[k] >= hcs[T]) { rc = 1; break; }
+    /* each key's row is updated on its own (rows are distinct) */
+#pragma omp parallel for schedule(dynamic, 256) num_threads(g_threads) if (g_threads > 1 && rc == 0)
+    for (int64_t k = 0; k < (rc == 0 ? nkeys : 0); ++k) {
         /* table of the key: the last t with hash_size_cumsum[t] <= key */
         int32_t t = 0;
         while (t + 1 < T && hcs[t + 1] <= keys[k])
             ++t;
         int64_t r = keys[k] - hcs[t];
-        if (keys[k] < 0 || keys[k] >= hcs[T]) { rc = 1; break; }
         int64_t pos = held_row(&tables[t], r);
-        if (pos < 0) { rc = 3; break; }
+        if (pos < 0) {
+#pragma omp atomic write
+            rc = 3;
+            continue;
+        }
         int32_t D = dims[t];
         for (int32_t d = 0; d < D; ++d) {
             double g = G[k * Dmax + d];

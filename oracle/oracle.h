@@ -106,6 +106,14 @@ int oracle_backward_adagrad(int32_t T, int32_t B, const int64_t* rows, const int
                             double* grad_rows, double* new_rows, int32_t write_back,
                             int32_t pooling);
 
+/* Host threads used by oracle_forward (bags split among threads) and
+ * oracle_backward_sgd / oracle_backward_adagrad (the requested keys split into
+ * ranges; each range's rows summed by one thread).  Every output element is
+ * still accumulated by one thread in lookup order, so results are the same
+ * bits for any count.  n < 1 means 1; the default is 1.  Returns the count
+ * now in force (1 when the library was built without OpenMP). */
+int oracle_set_threads(int n);
+
 /* IEEE binary16 helpers (exposed so the tests can pin them). */
 double   oracle_half_to_double(uint16_t h);
 uint16_t oracle_double_to_half(double x);

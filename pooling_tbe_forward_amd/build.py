@@ -1,4 +1,6 @@
-"""Build libtbe.so (HIP, gfx950) in-tree with hipcc.
+"""Build libtbe.so (HIP, gfx950) in-tree with hipcc, and beside it
+libtbe_datagen.so, the device half of the seeded input generator (test and
+benchmark inputs only; it holds none of the operator's arithmetic).
 
 Usage: python -m pooling_tbe_forward_amd.build [--jobs N]
 """
@@ -16,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtbe.so")
+GEN_SRC = os.path.join(HERE, "gen", "weights_gen.hip")
+GEN_LIB = os.path.join(HERE, "libtbe_datagen.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -31,26 +35,33 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 
 def _compile(src: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libtbe.so (always rebuilds)."""
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out: str):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libtbe.so and
+    libtbe_datagen.so (always rebuilds)."""
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [GEN_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], GEN_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", GEN_LIB)
     return LIB
 
 

@@ -130,7 +130,21 @@ struct SegArgs {
     int32_t all_weighted;      // mean pooling: every table's payload weight applies
     float* state;              // row-wise Adagrad: fp32 state per row, by key
     uint32_t chunk_blocks;     // the grid's last chunk_blocks blocks take long-run chunks
+    const uint32_t* mode;      // payload the integer stage left in the workspace
+    uint32_t expect_mode;      // ... and the payload this call was told to expect
+    uint32_t* err;             // the workspace's error word
 };
+
+// The workspace must hold the payload this launch reads (sample ids, or
+// (sample, weight) pairs): a caller of the apply half that names the wrong one
+// would have sample ids read at the wrong stride.  On a mismatch the kernel
+// does no work and sets the error word's payload bit.
+__device__ __forceinline__ bool payload_mismatch(const SegArgs& c)
+{
+    if (ldg(c.mode) == c.expect_mode) return false;
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(c.err, kErrPayload);
+    return true;
+}
 
 enum Opt : int { kSgd = 0, kAdagrad = 1 };
 
@@ -561,6 +575,7 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
                                                       const ACC* __restrict__ partials)
 {
     __shared__ Pack<ACC, VEC> red[4][64];   // each wave's folded slab sum
+    if (payload_mismatch(c)) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -652,6 +667,7 @@ __global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ wei
     static_assert((S << (6 - kMinLprLog2)) <= 64, "a batch is loaded one record per lane");
     __shared__ TableDesc sdesc[kLdsTables];
     __shared__ Pack<ACC, VEC> red[BLOCKCHUNK ? 4 : 1][64];
+    if (payload_mismatch(c)) return;
     const uint32_t wib = threadIdx.x >> 6;
     // blocks [0, gridDim.x - chunk_blocks) take short runs (dispatched first:
     // measured faster than chunks first), the rest long-run chunks
@@ -802,6 +818,9 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.state = a.state;
     c.all_weighted = p->pooling == TBE_POOL_MEAN ? 1 : 0;
     c.chunk_blocks = 0;
+    c.mode = reinterpret_cast<const uint32_t*>(ws + L.off_ctl) + kCtlMode;
+    c.expect_mode = a.payload_pairs ? kModePairs : kModeSample;
+    c.err = reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlError;
     if (a.state) return dispatch_segment<kAdagrad>(a, c, vec);
     return dispatch_segment<kSgd>(a, c, vec);
 }

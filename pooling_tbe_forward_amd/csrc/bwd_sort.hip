@@ -201,7 +201,7 @@ __device__ __forceinline__ uint32_t lookback(uint32_t* st, uint32_t stride, uint
         tp -= consumed;
         if (consumed == 0) {
             if (++spins > kSpinLimit) {
-                atomicOr(err, 1u);
+                atomicOr(err, kErrLookback);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     }
     const uint32_t tile = s_tile;
     if (tile >= ntiles) {          // only with an uninitialised control block
-        if (tid == 0) atomicOr(err, 2u);
+        if (tid == 0) atomicOr(err, kErrControl);
         return;
     }
 
@@ -602,7 +602,7 @@ __device__ __forceinline__ uint32_t lookback_wave(uint32_t* st, uint32_t tile, u
         tp -= first_unpub;
         if (first_unpub == 0) {
             if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(err, 1u);
+                if (lane == 0) atomicOr(err, kErrLookback);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     uint32_t* __restrict__ rstatus, uint32_t* __restrict__ ticket, uint32_t* __restrict__ err,
     const uint32_t* __restrict__ hash_off, int32_t T, uint4* __restrict__ short_info,
     uint4* __restrict__ long_info, uint32_t* __restrict__ counts,
-    uint32_t max_long, uint32_t* __restrict__ prev_totals,
+    uint32_t* __restrict__ mode_word, uint32_t max_long, uint32_t* __restrict__ prev_totals,
     uint32_t* __restrict__ unique, uint32_t* __restrict__ run_start,
     uint32_t* __restrict__ run_len, uint32_t* __restrict__ short_ids,
     uint32_t* __restrict__ long_ids)
@@ -718,7 +718,7 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     __syncthreads();
     const uint32_t tile = s_tile;
     if (tile >= ntiles) {          // only with an uninitialised control block
-        if (tid == 0) atomicOr(err, 2u);
+        if (tid == 0) atomicOr(err, kErrControl);
         return;
     }
     const uint32_t t0 = tile * kTile;
@@ -816,6 +816,9 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
         const uint32_t R = texcl[0] + s_tot[0];
         counts[1] = R - (texcl[1] + s_tot[1]);
         if (API) run_start[R] = N;
+        // which payload the sorted entries carry, for the segment kernels'
+        // check of what their caller says
+        *mode_word = FIRST == 2 ? kModePairs : (FIRST == 1 ? kModeSample : kModeNone);
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -989,7 +992,7 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                        ctl + kCtlError, p->d_hash_off, p->T,
                        reinterpret_cast<uint4*>(ws + L.off_short_info),
                        reinterpret_cast<uint4*>(ws + L.off_long_info), ctl + kCtlCounts,
-                       static_cast<uint32_t>(L.max_long),
+                       ctl + kCtlMode, static_cast<uint32_t>(L.max_long),
                        ctl + kCtlTotals + (L.npasses - 1) * kRadix,
                        reinterpret_cast<uint32_t*>(ws + L.off_unique),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_start),
@@ -1003,10 +1006,24 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
 }  // namespace tbe
 
 namespace tbe {
+namespace {
+__global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst)
+{
+    *dst = *src;
+}
+}  // namespace
+
 hipError_t launch_workspace_init(void* ws, hipStream_t s)
 {
     hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(1024), 0, s, static_cast<uint32_t*>(ws),
                        kCtlWords);
+    return hipGetLastError();
+}
+
+hipError_t launch_workspace_status(const void* ws, uint32_t* out, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(1), 0, s,
+                       static_cast<const uint32_t*>(ws) + kCtlError, out);
     return hipGetLastError();
 }
 }  // namespace tbe

@@ -55,7 +55,7 @@ bool use_hist(const tbe_plan* p, int32_t B, int64_t N)
 
 extern "C" {
 
-int32_t tbe_version(void) { return 100; }
+int32_t tbe_version(void) { return 101; }
 
 const char* tbe_status_string(tbe_status s)
 {
@@ -410,6 +410,19 @@ tbe_status tbe_workspace_init(void* workspace, size_t workspace_bytes, void* str
         workspace_bytes < size_t(kCtlWords) * 4)
         return TBE_EINVAL;
     if (launch_workspace_init(workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TBE_EHIP;
+    return TBE_OK;
+}
+
+tbe_status tbe_workspace_status(const void* workspace, size_t workspace_bytes,
+                                uint32_t* error_word, void* stream)
+{
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+        workspace_bytes < size_t(kCtlWords) * 4 || !error_word ||
+        (reinterpret_cast<uintptr_t>(error_word) & 3))
+        return TBE_EINVAL;
+    if (launch_workspace_status(workspace, error_word, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
         return TBE_EHIP;
     return TBE_OK;
 }

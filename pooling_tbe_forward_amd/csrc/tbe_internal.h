@@ -81,11 +81,21 @@ hipError_t launch_fwd_hist(const FwdArgs& a);
 // Control block at offset 0 of every backward workspace.  It must be zero when
 // a call starts (tbe_workspace_init), and every call leaves it zero again:
 // tile tickets reset themselves, each pass's digit totals are cleared by the
-// next kernel.  Counts and the error word are outputs.
+// next kernel.  Counts, the payload mode and the error word are outputs.
 constexpr int kCtlTicket = 0;      // [4] tile tickets of the radix passes
 constexpr int kCtlRleTicket = 4;   // tile ticket of the run-length encode
-constexpr int kCtlError = 12;      // nonzero: a look-back wait gave up (sticky)
+constexpr int kCtlError = 12;      // error word, sticky until tbe_workspace_init (kErr* bits)
+constexpr int kCtlMode = 13;       // payload of the last integer stage (kMode*); an output
 constexpr int kCtlCounts = 8;      // [4] runs, short runs, long runs, long-run chunks
+
+// Bits of the error word (tbe_workspace_status).
+constexpr uint32_t kErrLookback = 1u;     // a look-back wait gave up: results invalid
+constexpr uint32_t kErrControl = 2u;      // the control block was not initialised
+constexpr uint32_t kErrPayload = 4u;      // apply found another payload than it was told
+// Payload the integer stage left in the workspace (kCtlMode).
+constexpr uint32_t kModeNone = 0u;        // none yet, or tbe_sort_rle's lookup positions
+constexpr uint32_t kModeSample = 1u;      // sample ids
+constexpr uint32_t kModePairs = 2u;       // (sample id, weight) pairs
 constexpr int kTotCopies = 8;      // digit totals are kept in this many copies
 constexpr int kCtlTotals = 16;     // [kTotCopies][4][256] digit totals of every radix pass
 constexpr int kCtlWords = 16 + kTotCopies * 4 * 256;
@@ -158,6 +168,8 @@ inline void stage_mark(const tbe_plan* p, int k, hipStream_t s)
 
 // Zero the control block (first kCtlWords words) of a fresh workspace.
 hipError_t launch_workspace_init(void* ws, hipStream_t s);
+// Copy the workspace's error word to a caller's device word.
+hipError_t launch_workspace_status(const void* ws, uint32_t* out, hipStream_t s);
 
 hipError_t launch_bounds_check(const tbe_plan* p, int32_t B, const void* indices,
                                int64_t N, const void* offsets, int64_t* err, hipStream_t s);

@@ -18,8 +18,9 @@ purpose 0 = table shapes, 2 = bag lengths, 3 = ids (per table), 4 = per-sample
 weights, 5 = output gradient.  Embedding weights (purpose 1) come from a
 counter-based generator, ``lowbias32`` (Chris Wellons' integer hash), keyed on
 (seed, table, element index), so that any row can be regenerated on the host
-without materialising a multi-GB table, and the whole table can be built on the
-GPU with identical bits.  A weight value is an Irwin-Hall sum of four 16-bit
+without materialising a multi-GB table, and a whole table is built on the GPU
+with identical bits by one kernel launch (``gen/weights_gen.hip``, built into
+``libtbe_datagen.so``; that library holds only this generator).  A weight value is an Irwin-Hall sum of four 16-bit
 uniforms, centred and scaled to the configured standard deviation (an
 approximately normal law), or a 24-bit uniform on [-1, 1).
 """
@@ -27,6 +28,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -128,18 +130,31 @@ class Problem:
 # Counter-based weight generator (host numpy and device torch, same bits).
 # --------------------------------------------------------------------------
 def _mul32(x, c):
-    """(x * c) mod 2**32 for 0 <= x < 2**32, safe in signed 64-bit lanes."""
-    lo = c & 0xFFFF
-    hi = c >> 16
-    return (x * lo + (((x * hi) & 0xFFFF) << 16)) & M32
+    """(x * c) mod 2**32 for a Python int 0 <= x < 2**32."""
+    return (x * c) & M32
 
 
 def _lowbias32(x):
-    x = x ^ (x >> 16)
+    """Chris Wellons' lowbias32 integer hash of a Python int in [0, 2**32)."""
+    x ^= x >> 16
     x = _mul32(x, 0x7FEB352D)
-    x = x ^ (x >> 15)
+    x ^= x >> 15
     x = _mul32(x, 0x846CA68B)
-    x = x ^ (x >> 16)
+    x ^= x >> 16
+    return x
+
+
+def _lowbias32_u64(x):
+    """lowbias32 of every element of a uint64 array of 32-bit values, in place
+    (uint64 products are exact modulo 2**64, so masking keeps the low word)."""
+    m = np.uint64(M32)
+    x ^= x >> np.uint64(16)
+    x *= np.uint64(0x7FEB352D)
+    x &= m
+    x ^= x >> np.uint64(15)
+    x *= np.uint64(0x846CA68B)
+    x &= m
+    x ^= x >> np.uint64(16)
     return x
 
 
@@ -153,63 +168,105 @@ def _ih_scale(sigma: float) -> float:
     return sigma / math.sqrt(4.0 * (65536.0 ** 2 - 1.0) / 12.0)
 
 
-def _values_from_hash(h0, h1, wdist, lib):
-    """Map two hash words per element to a float64 value (numpy or torch)."""
+def _dist_code(wdist):
+    """(kind, scale) of a weight law: kind 0 = approximately normal with
+    standard deviation wdist[1], kind 1 = uniform on [-1, 1)."""
     if wdist[0] == "normal":
-        s = (h0 & 0xFFFF) + (h0 >> 16) + (h1 & 0xFFFF) + (h1 >> 16) - 131070
-        return lib_float64(s, lib) * _ih_scale(float(wdist[1]))
+        return 0, _ih_scale(float(wdist[1]))
     if wdist[0] == "uniform":
-        lo, hi = float(wdist[1]), float(wdist[2])
-        assert (lo, hi) == (-1.0, 1.0), "only U(-1,1) is generated"
-        u24 = h0 >> 8
-        return lib_float64(2 * u24 - (1 << 24), lib) * (2.0 ** -24)
+        assert (float(wdist[1]), float(wdist[2])) == (-1.0, 1.0), "only U(-1,1) is generated"
+        return 1, 2.0 ** -24
     raise ValueError(wdist)
 
 
-def lib_float64(x, lib):
-    if lib is np:
-        return x.astype(np.float64)
-    return x.to(lib.float64)
+def _hash_elems_np(e, seed, t):
+    """Two 32-bit hash words (uint64 arrays) per element index e >= 0."""
+    e = np.asarray(e, dtype=np.int64).astype(np.uint64)
+    e_lo = e & np.uint64(M32)
+    e_hi = e >> np.uint64(32)
+    out = []
+    for lane in (0, 1):
+        h = e_lo ^ np.uint64(_stream_key(seed, t, lane))
+        h = _lowbias32_u64(h)
+        h ^= e_hi
+        out.append(_lowbias32_u64(h))
+    return out
 
 
-def _hash_elems(e, seed, t, lib):
-    """Two 32-bit hash words per element index e (int64 array/tensor)."""
-    k0 = _stream_key(seed, t, 0)
-    k1 = _stream_key(seed, t, 1)
-    e_lo = e & M32
-    e_hi = e >> 32
-    h0 = _lowbias32(_lowbias32(e_lo ^ k0) ^ e_hi)
-    h1 = _lowbias32(_lowbias32(e_lo ^ k1) ^ e_hi)
-    return h0, h1
+def _rows_block(seed, t, D, kind, scale, f16, r):
+    e = (r[:, None] * D + np.arange(D, dtype=np.int64)[None, :]).reshape(-1)
+    h0, h1 = _hash_elems_np(e, seed, t)
+    if kind == 0:
+        s = (h0 & np.uint64(0xFFFF)) + (h0 >> np.uint64(16)) + (h1 & np.uint64(0xFFFF)) + \
+            (h1 >> np.uint64(16))
+        v = (s.astype(np.int64) - 131070).astype(np.float64) * scale
+    else:
+        u24 = (h0 >> np.uint64(8)).astype(np.int64)
+        v = (2 * u24 - (1 << 24)).astype(np.float64) * scale
+    v = v.astype(np.float32)
+    return v.astype(np.float16) if f16 else v
 
 
 def weight_rows(prob: Problem, t: int, row_ids) -> np.ndarray:
-    """Rows ``row_ids`` of table t as a [len, D_t] array of the weight dtype."""
+    """Rows ``row_ids`` of table t as a [len, D_t] array of the weight dtype.
+
+    Element e = row * D_t + column gets the hash words h0, h1 of
+    _hash_elems_np; the value is computed in float64, rounded to float32 and,
+    for fp16 tables, rounded once more to float16.  Work goes in blocks of
+    about 64K elements, so the temporaries stay in cache."""
     D = int(prob.dims[t])
     r = np.asarray(row_ids, dtype=np.int64).reshape(-1)
-    e = (r[:, None] * D + np.arange(D, dtype=np.int64)[None, :]).reshape(-1)
-    h0, h1 = _hash_elems(e, prob.seed, t, np)
-    v = _values_from_hash(h0, h1, prob.wdist, np).astype(np.float32)
-    if prob.wdtype == "f16":
-        v = v.astype(np.float16)
-    return v.reshape(len(r), D)
+    kind, scale = _dist_code(prob.wdist)
+    f16 = prob.wdtype == "f16"
+    out = np.empty((r.size, D), dtype=np.float16 if f16 else np.float32)
+    step = max(1, 65536 // D)
+    for s in range(0, r.size, step):
+        e = min(s + step, r.size)
+        out[s:e] = _rows_block(prob.seed, t, D, kind, scale, f16, r[s:e]).reshape(-1, D)
+    return out
 
 
-def table_weights_torch(prob: Problem, t: int, out, chunk: int = 1 << 25):
-    """Fill the 1-D torch tensor ``out`` (rows_t*D_t elements) with table t."""
+_gen_lib = None
+GEN_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtbe_datagen.so")
+
+
+def _gen():
+    """libtbe_datagen.so: the device half of this generator (built with the
+    package; see gen/weights_gen.hip)."""
+    global _gen_lib
+    if _gen_lib is None:
+        import ctypes
+        if not os.path.exists(GEN_LIB_PATH):
+            raise RuntimeError(f"{GEN_LIB_PATH} is not built; run "
+                               "`python -m pooling_tbe_forward_amd.build`")
+        L = ctypes.CDLL(GEN_LIB_PATH)
+        L.tbe_datagen_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int32,
+                                       ctypes.c_double, ctypes.c_void_p]
+        L.tbe_datagen_fill.restype = ctypes.c_int
+        _gen_lib = L
+    return _gen_lib
+
+
+def table_weights_torch(prob: Problem, t: int, out):
+    """Fill the 1-D torch tensor ``out`` (rows_t*D_t elements) with table t:
+    one kernel launch on a GPU tensor, the host generator otherwise."""
     import torch
     n = int(prob.rows[t]) * int(prob.dims[t])
-    assert out.numel() == n
-    for s in range(0, n, chunk):
-        m = min(chunk, n - s)
-        e = torch.arange(s, s + m, dtype=torch.int64, device=out.device)
-        h0, h1 = _hash_elems(e, prob.seed, t, torch)
-        del e
-        v = _values_from_hash(h0, h1, prob.wdist, torch)
-        del h0, h1
-        v = v.to(torch.float32)
-        out[s:s + m].copy_(v.to(out.dtype))
-        del v
+    assert out.numel() == n and out.is_contiguous()
+    if not out.is_cuda:
+        out.copy_(torch.from_numpy(weight_rows(prob, t, np.arange(int(prob.rows[t]))).reshape(-1)))
+        return out
+    import ctypes
+    kind, scale = _dist_code(prob.wdist)
+    f16 = 1 if prob.wdtype == "f16" else 0
+    assert out.dtype == (torch.float16 if f16 else torch.float32)
+    rc = _gen().tbe_datagen_fill(ctypes.c_void_p(out.data_ptr()), n, f16,
+                                 _stream_key(prob.seed, t, 0), _stream_key(prob.seed, t, 1),
+                                 kind, scale,
+                                 ctypes.c_void_p(torch.cuda.current_stream(out.device).cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"tbe_datagen_fill failed (hip error {rc})")
     return out
 
 
@@ -383,6 +440,27 @@ def make_problem(name: str, seed: Optional[int] = None, B: Optional[int] = None,
                    wdist=cfg["wdist"], weighted=wmask,
                    lengths=lengths, offsets=offsets, indices=indices, psw=psw,
                    grad=grad, lr=float(cfg["lr"]))
+
+
+def sample_prefix(prob: Problem, Bs: int) -> Problem:
+    """The same batch restricted to samples 0..Bs-1 of every feature (a
+    bounded sample of a workload): bag (t, b) of the result is bag (t, b) of
+    ``prob`` for b < Bs, with its ids, per-sample weights and output-gradient
+    row.  Input bookkeeping only."""
+    Bs = min(int(Bs), prob.B)
+    lengths = prob.lengths[:, :Bs].copy()
+    parts_i, parts_w = [], []
+    for t in range(prob.T):
+        s, e = int(prob.offsets[t * prob.B]), int(prob.offsets[t * prob.B + Bs])
+        parts_i.append(prob.indices[s:e])
+        if prob.psw is not None:
+            parts_w.append(prob.psw[s:e])
+    offsets = np.concatenate([[0], np.cumsum(lengths.ravel())]).astype(np.int64)
+    return dataclasses.replace(
+        prob, B=Bs, lengths=lengths, offsets=offsets,
+        indices=np.concatenate(parts_i) if parts_i else np.zeros(0, np.int64),
+        psw=np.concatenate(parts_w) if prob.psw is not None else None,
+        grad=np.ascontiguousarray(prob.grad[:Bs]))
 
 
 def exact_problem(seed: int, T: int = 3, B: int = 37, max_rows: int = 40,

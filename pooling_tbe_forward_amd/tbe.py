@@ -77,6 +77,8 @@ def lib():
         L.tbe_set_stage_events.restype = I32
         L.tbe_workspace_init.argtypes = [P, SZ, P]
         L.tbe_workspace_init.restype = I32
+        L.tbe_workspace_status.argtypes = [P, SZ, P, P]
+        L.tbe_workspace_status.restype = I32
         L.tbe_bounds_check.argtypes = [P, I32, P, I64, P, P, P]
         L.tbe_bounds_check.restype = I32
         L.tbe_get_tuning.argtypes = [P, ctypes.POINTER(tbe_tuning)]
@@ -125,6 +127,33 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, dtype, numel=None, at_least=False):
+    """Raise unless tensor t has this dtype and size: the kernels read every
+    buffer at the widths and lengths the plan implies."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and (t.numel() < numel if at_least else t.numel() != numel):
+        raise ValueError(f"{name} must have {'at least ' if at_least else ''}{numel} "
+                         f"elements, got {t.numel()}")
+
+
+def _check_jagged(plan, B, indices, offsets, per_sample_weights=None):
+    it = plan.torch_idtype
+    _need(indices, "indices", it)
+    _need(offsets, "offsets", it, plan.T * int(B) + 1)
+    if per_sample_weights is not None:
+        _need(per_sample_weights, "per_sample_weights", torch.float32, indices.numel())
+
+
+def _check_dense(plan, B, weights=None, rowmajor=None, rowmajor_name="grad_output"):
+    if weights is not None or rowmajor is None:
+        _need(weights, "weights", plan.torch_wdtype, plan.weight_elems, at_least=True)
+    if rowmajor is not None:
+        _need(rowmajor, rowmajor_name, torch.float32, int(B) * plan.sum_D)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -141,6 +170,9 @@ class Plan:
         self.dims = list(dims)
         self.weight_dtype = weight_dtype
         self.index_dtype = index_dtype
+        self.sum_D = sum(self.dims)
+        self.sum_rows = sum(self.rows)
+        self.weight_elems = sum(r * d for r, d in zip(self.rows, self.dims))
 
     @property
     def torch_wdtype(self):
@@ -202,6 +234,8 @@ def tbe_set_tuning(plan: Plan, **kw):
 
 def tbe_forward(plan: Plan, B: int, weights, indices, offsets, per_sample_weights, output,
                 stream=None):
+    _check_jagged(plan, B, indices, offsets, per_sample_weights)
+    _check_dense(plan, B, weights, output, "output")
     _check(lib().tbe_forward(plan.handle, int(B), _ptr(weights), _ptr(indices),
                              int(indices.numel()), _ptr(offsets), _ptr(per_sample_weights),
                              _ptr(output), _stream(stream)), "tbe_forward")
@@ -240,6 +274,8 @@ def alloc_workspace(plan: Plan, B: int, num_indices: int, device="cuda"):
 
 def tbe_backward_sgd(plan: Plan, B: int, weights, indices, offsets, per_sample_weights,
                      grad_output, lr: float, workspace, stream=None):
+    _check_jagged(plan, B, indices, offsets, per_sample_weights)
+    _check_dense(plan, B, weights, grad_output)
     _check(lib().tbe_backward_sgd(plan.handle, int(B), _ptr(weights), _ptr(indices),
                                   int(indices.numel()), _ptr(offsets), _ptr(per_sample_weights),
                                   _ptr(grad_output), float(lr), _ptr(workspace),
@@ -250,6 +286,7 @@ def tbe_backward_sgd(plan: Plan, B: int, weights, indices, offsets, per_sample_w
 
 def tbe_backward_prepare(plan: Plan, B: int, indices, offsets, per_sample_weights, workspace,
                          stream=None):
+    _check_jagged(plan, B, indices, offsets, per_sample_weights)
     _check(lib().tbe_backward_prepare(plan.handle, int(B), _ptr(indices), int(indices.numel()),
                                       _ptr(offsets), _ptr(per_sample_weights), _ptr(workspace),
                                       int(workspace.numel() * workspace.element_size()),
@@ -259,6 +296,7 @@ def tbe_backward_prepare(plan: Plan, B: int, indices, offsets, per_sample_weight
 
 def tbe_backward_apply(plan: Plan, B: int, num_indices: int, weighted: bool, weights,
                        grad_output, lr: float, workspace, stream=None):
+    _check_dense(plan, B, weights, grad_output)
     _check(lib().tbe_backward_apply(plan.handle, int(B), int(num_indices), 1 if weighted else 0,
                                     _ptr(weights), _ptr(grad_output), float(lr), _ptr(workspace),
                                     int(workspace.numel() * workspace.element_size()),
@@ -274,6 +312,9 @@ def tbe_backward_adagrad(plan: Plan, B: int, weights, state, indices, offsets,
                          eps: float = ADAGRAD_EPS, stream=None):
     """Backward + exact row-wise Adagrad in place; ``state`` is the fp32 row
     state, one value per row of every table (indexed by the row's key)."""
+    _check_jagged(plan, B, indices, offsets, per_sample_weights)
+    _check_dense(plan, B, weights, grad_output)
+    _need(state, "state", torch.float32, plan.sum_rows)
     _check(lib().tbe_backward_adagrad(plan.handle, int(B), _ptr(weights), _ptr(state),
                                       _ptr(indices), int(indices.numel()), _ptr(offsets),
                                       _ptr(per_sample_weights), _ptr(grad_output), float(lr),
@@ -286,6 +327,8 @@ def tbe_backward_adagrad(plan: Plan, B: int, weights, state, indices, offsets,
 def tbe_backward_apply_adagrad(plan: Plan, B: int, num_indices: int, weighted: bool, weights,
                                state, grad_output, lr: float, workspace,
                                eps: float = ADAGRAD_EPS, stream=None):
+    _check_dense(plan, B, weights, grad_output)
+    _need(state, "state", torch.float32, plan.sum_rows)
     _check(lib().tbe_backward_apply_adagrad(plan.handle, int(B), int(num_indices),
                                             1 if weighted else 0, _ptr(weights), _ptr(state),
                                             _ptr(grad_output), float(lr), float(eps),
@@ -298,6 +341,7 @@ def tbe_backward_apply_adagrad(plan: Plan, B: int, num_indices: int, weighted: b
 def tbe_sort_rle(plan: Plan, B: int, indices, offsets, workspace, stream=None) -> dict:
     """Returns int32 tensors viewing the workspace (keys as unsigned 32-bit
     values stored in int32) plus the device counts tensor."""
+    _check_jagged(plan, B, indices, offsets)
     v = tbe_sort_view()
     N = int(indices.numel())
     _check(lib().tbe_sort_rle(plan.handle, int(B), _ptr(indices), N, _ptr(offsets),
@@ -313,10 +357,29 @@ def tbe_sort_rle(plan: Plan, B: int, indices, offsets, workspace, stream=None) -
     return dict(sorted_keys=view(v.sorted_keys, N), sorted_pos=view(v.sorted_pos, N),
                 unique_keys=view(v.unique_keys, N), run_start=view(v.run_start, N + 1),
                 run_len=view(v.run_len, N), short_runs=view(v.short_runs, N),
-                long_runs=view(v.long_runs, N), counts=view(v.counts, 5))
+                long_runs=view(v.long_runs, N), counts=view(v.counts, 6))
+
+
+def tbe_workspace_status(workspace, error_word=None, stream=None):
+    """Enqueue a copy of the workspace's error word (TBE_WS_ERR_* bits) into
+    ``error_word`` (a device int32 tensor of one element; allocated when not
+    given) and return that tensor; read it after the stream is synchronised."""
+    if error_word is None:
+        error_word = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    _need(error_word, "error_word", torch.int32, 1)
+    _check(lib().tbe_workspace_status(_ptr(workspace),
+                                      int(workspace.numel() * workspace.element_size()),
+                                      _ptr(error_word), _stream(stream)), "tbe_workspace_status")
+    return error_word
+
+
+TBE_WS_ERR_LOOKBACK, TBE_WS_ERR_CONTROL, TBE_WS_ERR_PAYLOAD = 1, 2, 4
 
 
 def tbe_bounds_check(plan: Plan, B: int, indices, offsets, error_count, stream=None):
+    _need(indices, "indices", plan.torch_idtype)
+    _need(offsets, "offsets", plan.torch_idtype, plan.T * int(B) + 1)
+    _need(error_count, "error_count", torch.int64, 1, at_least=True)
     _check(lib().tbe_bounds_check(plan.handle, int(B), _ptr(indices), int(indices.numel()),
                                   _ptr(offsets), _ptr(error_count), _stream(stream)),
            "tbe_bounds_check")

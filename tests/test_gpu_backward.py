@@ -353,7 +353,7 @@ def test_workspace_reused_across_calls_and_sizes():
         o = H.oracle_sort(prob, 8)
         rep = _sampled_backward_check(prob, None, w0, _key_sample(prob, o, n_short=500, seed=k))
         assert rep["ok"], (k, rep)
-        assert int(_u32(ws[48:52].view(torch.int32))[0]) == 0   # error word stays clear
+        assert int(tbe.tbe_workspace_status(ws).item()) == 0   # error word stays clear
 
 
 def test_stage_events_bracket_the_backward():
@@ -419,4 +419,33 @@ def test_prepare_apply_overlapped_matches_backward_sgd(name, B, tau):
     torch.cuda.synchronize()
     assert torch.equal(out, out_ref)
     assert torch.equal(w_new, w_ref)
-    assert int(_u32(ws2[48:52].view(torch.int32))[0]) == 0
+    assert int(tbe.tbe_workspace_status(ws2).item()) == 0
+
+
+def test_apply_refuses_a_payload_it_was_not_given():
+    """tbe_backward_apply told `weighted` unlike what tbe_backward_prepare
+    stored (or with no prepare at all) updates nothing and sets the payload
+    bit of the workspace's error word; a matching call then works."""
+    prob = dg.make_problem("stress", seed=12, B=64)
+    plan = H.make_plan(prob)
+    d = H.device_inputs(prob)
+    w0 = dg.packed_weights_torch(prob, "cuda")
+    ws = _workspace(plan, prob)
+    w = w0.clone()
+    tbe.tbe_backward_apply(plan, prob.B, prob.N, True, w, d["grad"], prob.lr, ws)  # no prepare
+    torch.cuda.synchronize()
+    assert int(tbe.tbe_workspace_status(ws).item()) == tbe.TBE_WS_ERR_PAYLOAD
+    assert torch.equal(w, w0)
+    ws = _workspace(plan, prob)
+    tbe.tbe_backward_prepare(plan, prob.B, d["indices"], d["offsets"], d["psw"], ws)
+    tbe.tbe_backward_apply(plan, prob.B, prob.N, False, w, d["grad"], prob.lr, ws)  # wrong
+    torch.cuda.synchronize()
+    assert int(tbe.tbe_workspace_status(ws).item()) == tbe.TBE_WS_ERR_PAYLOAD
+    assert torch.equal(w, w0)
+    ws = _workspace(plan, prob)
+    tbe.tbe_backward_prepare(plan, prob.B, d["indices"], d["offsets"], d["psw"], ws)
+    tbe.tbe_backward_apply(plan, prob.B, prob.N, True, w, d["grad"], prob.lr, ws)
+    torch.cuda.synchronize()
+    assert int(tbe.tbe_workspace_status(ws).item()) == 0
+    w_ref = gpu_backward(prob, w0.clone())
+    assert torch.equal(w, w_ref)

@@ -46,5 +46,5 @@ def test_captured_step_replays_match_eager(name, B):
         torch.cuda.synchronize()
         assert torch.equal(out_graph, out_eager), rep
         assert torch.equal(w_graph, w_eager), rep
-        err = int(ws_graph[48:52].view(torch.int32).cpu().numpy().view(np.uint32)[0])
+        err = int(tbe.tbe_workspace_status(ws_graph).item())
         assert err == 0, rep

@@ -298,3 +298,38 @@ def test_property_integer_stage(seed, T, B, tau):
         assert np.all(np.diff(seg) > 0)              # lookup order kept inside a run
         assert np.all(r["sorted_keys"][s:s + L] == r["unique_keys"][k])
     assert r["num_short"] + r["num_long"] == r["num_runs"]
+
+
+@pytest.mark.parametrize("name,B", [("mixed", 48), ("stress", 96), ("toy", None)])
+def test_threads_do_not_change_bits(name, B):
+    """The OpenMP leg of the oracle (bags, then key ranges, split among host
+    threads) gives the same bits as one thread: every output element is still
+    summed by one thread in lookup order.  A thread count above the number of
+    keys, and a sparse row store with a row missing, are covered too."""
+    prob = dg.make_problem(name, seed=77, B=B) if B else dg.make_problem(name, seed=77)
+    tl = prob.table_of_lookup()
+    rowsets = [np.unique(prob.indices[tl == t]) for t in range(prob.T)]
+    tabs = H.sparse_tables(prob, rowsets)
+    keys = H.oracle_sort(prob, 1 << 40)["unique_keys"]
+    code = H.wcode(prob)
+    res = []
+    try:
+        for n in (1, 3, 8, 4096):
+            assert oracle.set_threads(n) == n
+            f = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
+                               prob.offsets, prob.psw, prob.weighted)
+            gr, nr = oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, code, tabs,
+                                         prob.indices, prob.offsets, prob.psw, prob.weighted,
+                                         prob.grad, prob.lr, keys)
+            res.append((f, gr, nr))
+            bad = [(ids[1:], d[int(prob.dims[t]):]) if ids.size else (ids, d)
+                   for t, (ids, d) in enumerate(tabs)]
+            with pytest.raises(oracle.OracleError):
+                oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, bad, prob.indices,
+                               prob.offsets, prob.psw, prob.weighted)
+    finally:
+        oracle.set_threads(1)
+    for f, gr, nr in res[1:]:
+        assert np.array_equal(f.view(np.uint64), res[0][0].view(np.uint64))
+        assert np.array_equal(gr.view(np.uint64), res[0][1].view(np.uint64))
+        assert np.array_equal(nr.view(np.uint64), res[0][2].view(np.uint64))
