@@ -46,8 +46,13 @@ __global__ __launch_bounds__(256) void k_gen_weights(OT* __restrict__ out, int64
             const int32_t u = static_cast<int32_t>(h0 >> 8);
             v = static_cast<double>(2 * u - (1 << 24)) * 0x1p-24;
         }
-        const float f = static_cast<float>(v);   // round to nearest even
-        out[e] = static_cast<OT>(f);             // fp16: one more rounding, nearest even
+        float f = static_cast<float>(v);   // round to nearest even
+        // The fp32 value must exist: without this the compiler folds the two
+        // conversions into one direct double -> fp16 rounding, which differs
+        // from rounding twice by one fp16 ulp near ties (measured: about 1 in
+        // 30,000 elements of the fp16 tables).
+        asm volatile("" : "+v"(f));
+        out[e] = static_cast<OT>(f);       // fp16: one more rounding, nearest even
     }
 }
 

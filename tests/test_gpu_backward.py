@@ -317,10 +317,14 @@ def test_error_codes():
     plan = H.make_plan(prob)
     d = H.device_inputs(prob)
     ws = torch.zeros(16, dtype=torch.uint8, device="cuda")  # far too small
+    w = torch.zeros(plan.weight_elems, device="cuda")
     with pytest.raises(tbe.TBEError) as e:
-        tbe.tbe_backward_sgd(plan, prob.B, torch.zeros(10, device="cuda"), d["indices"],
-                             d["offsets"], None, d["grad"], 0.1, ws)
+        tbe.tbe_backward_sgd(plan, prob.B, w, d["indices"], d["offsets"], None, d["grad"], 0.1,
+                             ws)
     assert e.value.status == tbe.TBE_EINVAL
+    with pytest.raises(ValueError):     # the binding refuses a short weights buffer first
+        tbe.tbe_backward_sgd(plan, prob.B, w[:10], d["indices"], d["offsets"], None, d["grad"],
+                             0.1, tbe.alloc_workspace(plan, prob.B, prob.N))
     with pytest.raises(tbe.TBEError):
         tbe.tbe_set_tuning(plan, tau=0)
     with pytest.raises(tbe.TBEError):
