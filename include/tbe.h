@@ -170,6 +170,34 @@ tbe_status tbe_backward_sgd(const tbe_plan* plan, int32_t B, void* weights,
                             float lr, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tbe_backward_sgd without a caller workspace, for callers that cannot
+ * allocate device memory or pass a workspace (code under stream capture,
+ * serving loops, harnesses that forbid allocation).  The same kernels and the
+ * same result as tbe_backward_sgd; the workspace is a 64 MiB array inside the
+ * library, one copy per GPU, held until the process ends.  Nothing is
+ * allocated per call.
+ *   error_word: device uint32 (4-byte aligned) or NULL; when given, it
+ *               receives the call's workspace error word (TBE_WS_ERR_* bits,
+ *               0 = valid) on `stream` after the update.
+ * Each call clears the array's control block first, so a call never sees an
+ * earlier call's state.  Every call on one GPU shares the array: calls that
+ * may overlap on one GPU (different streams, or several host threads) race
+ * and must be serialised by the caller.
+ * Errors: as for tbe_backward_sgd, and TBE_ERANGE when the call needs more
+ * workspace than the array holds (tbe_backward_workspace_bytes(plan, B,
+ * num_indices) > tbe_backward_noalloc_max_bytes(); about 830K lookups for
+ * fp32 tables of D = 128 -- a batch of 328K such lookups needs 25 MB).
+ */
+tbe_status tbe_backward_sgd_noalloc(const tbe_plan* plan, int32_t B, void* weights,
+                                    const void* indices, int64_t num_indices,
+                                    const void* offsets, const float* per_sample_weights,
+                                    const float* grad_output, float lr, uint32_t* error_word,
+                                    void* stream);
+
+/* Size in bytes of tbe_backward_sgd_noalloc's per-GPU workspace array. */
+size_t tbe_backward_noalloc_max_bytes(void);
+
+/*
  * The backward in two halves, for callers that overlap its integer stage with
  * other work.  The integer stage reads only indices, offsets and per-sample
  * weights, so it can run on a second stream while the forward of the same

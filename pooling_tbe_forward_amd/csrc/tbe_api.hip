@@ -1,10 +1,17 @@
 // C ABI of libtbe: argument validation, plan construction, kernel dispatch.
 // Every entry point is declared and documented in include/tbe.h.
+#include <mutex>
 #include <new>
 
 #include "tbe_internal.h"
 
 using namespace tbe;
+
+// Scratch of tbe_backward_sgd_noalloc: the backward's workspace for callers
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// until the process ends; all calls on one GPU share it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -350,6 +357,68 @@ tbe_status tbe_backward_apply_adagrad(const tbe_plan* p, int32_t B, int64_t num_
     return apply_half(p, B, num_indices, weighted, weights, state, grad_output, lr, eps, true,
                       workspace, workspace_bytes, stream);
 }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch copy, looked up once per device with
+// that device current (the host-side name `scratch` is not a device address).
+tbe_status scratch_on_current_device(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TBE_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TBE_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TBE_OK;
+}
+}  // namespace
+
+tbe_status tbe_backward_sgd_noalloc(const tbe_plan* p, int32_t B, void* weights,
+                                    const void* indices, int64_t num_indices, const void* offsets,
+                                    const float* psw, const float* grad_output, float lr,
+                                    uint32_t* error_word, void* stream)
+{
+    tbe_status st = check_call(p, B, num_indices, indices, offsets);
+    if (st != TBE_OK) return st;
+    if (!weights || !grad_output || (reinterpret_cast<uintptr_t>(error_word) & 3))
+        return TBE_EINVAL;
+    if (bwd_layout(p, B, num_indices).total > kScratchBytes) return TBE_ERANGE;
+    if (B == 0 || num_indices == 0) {
+        // nothing to update; the caller's error word still gets a value
+        if (error_word) {
+            void* ws = nullptr;
+            st = scratch_on_current_device(&ws);
+            if (st != TBE_OK) return st;
+            const hipStream_t s = static_cast<hipStream_t>(stream);
+            if (launch_workspace_init(ws, s) != hipSuccess ||
+                launch_workspace_status(ws, error_word, s) != hipSuccess)
+                return TBE_EHIP;
+        }
+        return TBE_OK;
+    }
+    void* ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != TBE_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // the control block must start at zero: the previous call on this GPU may
+    // have left its error word set (a fill kernel, so a captured graph holds
+    // no memset node)
+    if (launch_workspace_init(ws, s) != hipSuccess) return TBE_EHIP;
+    st = backward_whole(p, B, weights, nullptr, indices, num_indices, offsets, psw, grad_output,
+                        lr, 0.f, false, ws, kScratchBytes, stream);
+    if (st == TBE_OK && error_word && launch_workspace_status(ws, error_word, s) != hipSuccess)
+        st = TBE_EHIP;
+    return st;
+}
+
+size_t tbe_backward_noalloc_max_bytes(void) { return kScratchBytes; }
 
 tbe_status tbe_backward_sgd(const tbe_plan* p, int32_t B, void* weights, const void* indices,
                             int64_t num_indices, const void* offsets, const float* psw,

@@ -62,6 +62,10 @@ def lib():
         L.tbe_backward_workspace_bytes.restype = SZ
         L.tbe_backward_sgd.argtypes = [P, I32, P, P, I64, P, P, P, ctypes.c_float, P, SZ, P]
         L.tbe_backward_sgd.restype = I32
+        L.tbe_backward_sgd_noalloc.argtypes = [P, I32, P, P, I64, P, P, P, ctypes.c_float, P, P]
+        L.tbe_backward_sgd_noalloc.restype = I32
+        L.tbe_backward_noalloc_max_bytes.argtypes = []
+        L.tbe_backward_noalloc_max_bytes.restype = SZ
         L.tbe_backward_prepare.argtypes = [P, I32, P, I64, P, P, P, SZ, P]
         L.tbe_backward_prepare.restype = I32
         L.tbe_backward_apply.argtypes = [P, I32, I64, I32, P, P, ctypes.c_float, P, SZ, P]
@@ -282,6 +286,27 @@ def tbe_backward_sgd(plan: Plan, B: int, weights, indices, offsets, per_sample_w
                                   int(workspace.numel() * workspace.element_size()),
                                   _stream(stream)), "tbe_backward_sgd")
     return weights
+
+
+def tbe_backward_sgd_noalloc(plan: Plan, B: int, weights, indices, offsets, per_sample_weights,
+                             grad_output, lr: float, error_word=None, stream=None):
+    """tbe_backward_sgd with the library's own per-GPU workspace array (no
+    allocation by the library or the binding).  error_word: optional device
+    int32 tensor of one element that receives the call's error word."""
+    _check_jagged(plan, B, indices, offsets, per_sample_weights)
+    _check_dense(plan, B, weights, grad_output)
+    if error_word is not None:
+        _need(error_word, "error_word", torch.int32, 1)
+    _check(lib().tbe_backward_sgd_noalloc(plan.handle, int(B), _ptr(weights), _ptr(indices),
+                                          int(indices.numel()), _ptr(offsets),
+                                          _ptr(per_sample_weights), _ptr(grad_output), float(lr),
+                                          _ptr(error_word), _stream(stream)),
+           "tbe_backward_sgd_noalloc")
+    return weights
+
+
+def tbe_backward_noalloc_max_bytes() -> int:
+    return int(lib().tbe_backward_noalloc_max_bytes())
 
 
 def tbe_backward_prepare(plan: Plan, B: int, indices, offsets, per_sample_weights, workspace,
