@@ -15,7 +15,8 @@ import oracle
 from pooling_tbe_forward_amd import datagen as dg
 from pooling_tbe_forward_amd import tbe
 from tests import helpers as H
-from tests.test_gpu_backward import _gold_problem, _key_sample
+from tests import fullcheck
+from tests.test_gpu_backward import _gold_problem
 
 pytestmark = pytest.mark.gpu
 AGOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
@@ -135,22 +136,23 @@ def test_reduced_adagrad_vs_oracle(name, B, tau):
     w_dev = dg.packed_weights_torch(prob, "cuda")
     s_dev = torch.from_numpy(state0.copy()).cuda()
     gpu_adagrad(prob, w_dev, s_dev, tau=tau)
-    o = H.oracle_sort(prob, tau)
-    keys = o["unique_keys"] if o["num_runs"] <= 60000 else _key_sample(prob, o)
-    _check_sampled(prob, w_dev, s_dev, keys, state0, tbe.ADAGRAD_EPS)
-    _untouched(prob, w_dev, s_dev, state0, o["unique_keys"])
+    rep = fullcheck.backward_all(prob, w_dev, adagrad=(state0, s_dev, tbe.ADAGRAD_EPS))
+    assert rep["ok"], rep
+    fullcheck.untouched_all(prob, w_dev, state=(state0, s_dev))
 
 
 @pytest.mark.parametrize("name", ["stress", "uniform", "mixed", "band"])
-def test_full_size_adagrad_sampled(name):
+def test_full_size_adagrad_every_row(name):
+    """Full configuration at the plan's default tuning: every touched row and
+    its state against the oracle, every other row and state unchanged."""
     prob = dg.make_problem(name)
     state0 = _state0(prob, 9)
     w_dev = dg.packed_weights_torch(prob, "cuda")
     s_dev = torch.from_numpy(state0.copy()).cuda()
     gpu_adagrad(prob, w_dev, s_dev)
-    o = H.oracle_sort(prob, 256)
-    _check_sampled(prob, w_dev, s_dev, _key_sample(prob, o), state0, tbe.ADAGRAD_EPS)
-    _untouched(prob, w_dev, s_dev, state0, o["unique_keys"])
+    rep = fullcheck.backward_all(prob, w_dev, adagrad=(state0, s_dev, tbe.ADAGRAD_EPS))
+    assert rep["ok"], rep
+    fullcheck.untouched_all(prob, w_dev, state=(state0, s_dev))
     del w_dev, s_dev
     torch.cuda.empty_cache()
 
@@ -203,6 +205,9 @@ def test_prepare_apply_adagrad_matches_whole():
     torch.cuda.synchronize()
     assert torch.equal(w1.view(torch.int16), w2.view(torch.int16))
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    rep = fullcheck.backward_all(prob, w2, adagrad=(state0, s2, tbe.ADAGRAD_EPS))
+    assert rep["ok"], rep
+    fullcheck.untouched_all(prob, w2, state=(state0, s2))
 
 
 def test_adagrad_deterministic_and_lr_zero():

@@ -11,6 +11,7 @@ import torch
 import oracle
 from pooling_tbe_forward_amd import datagen as dg
 from pooling_tbe_forward_amd import tbe
+from tests import fullcheck
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -89,10 +90,13 @@ def test_sort_rle_vs_oracle(name, B, seed, tau):
 
 
 @pytest.mark.parametrize("name", ["uniform", "stress", "mixed", "band"])
-def test_sort_rle_full_size(name):
+@pytest.mark.parametrize("tau", [128, 256])
+def test_sort_rle_full_size(name, tau):
+    """All keys at full size, at the plan's default threshold (128) and the
+    pages' 256."""
     prob = dg.make_problem(name)
-    g = gpu_sort(prob, tau=256)
-    o = H.oracle_sort(prob, 256)
+    g = gpu_sort(prob, tau=tau)
+    o = H.oracle_sort(prob, tau)
     _compare_sort(g, o, prob.N)
 
 
@@ -183,50 +187,6 @@ def _check_rows(prob, w_after, keys, new_rows, packed_before):
     assert np.array_equal(w_after[~touched].view(u8), packed_before[~touched].view(u8))
 
 
-def _sampled_backward_check(prob, w_dev_before_rows, w_dev, keys_sample):
-    """Compare sampled updated rows with the oracle (rows generated on host)."""
-    tt, rr = H.key_to_table_row(prob, keys_sample)
-    rowsets = [np.unique(rr[tt == t]) for t in range(prob.T)]
-    tabs = H.sparse_tables(prob, rowsets)
-    _, nr = oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob), tabs,
-                                prob.indices, prob.offsets, prob.psw, prob.weighted, prob.grad,
-                                prob.lr, keys_sample)
-    got = np.zeros_like(nr)
-    for t in range(prob.T):
-        sel = np.flatnonzero(tt == t)
-        if sel.size == 0:
-            continue
-        D = int(prob.dims[t])
-        got[sel, :D] = H.rows_from_device(w_dev, prob, t, rr[sel]).astype(np.float64)
-        got[sel, D:] = nr[sel, D:]
-    return H.allclose_report(got, nr, *H.TOL[prob.wdtype])
-
-
-def _key_sample(prob, o, n_short=3000, seed=0):
-    rng = np.random.default_rng(seed)
-    uk = o["unique_keys"]
-    longk = uk[o["run_len"] >= 256]
-    pick = rng.choice(uk.size, size=min(n_short, uk.size), replace=False)
-    return np.unique(np.concatenate([longk, uk[pick], uk[:1], uk[-1:]]))
-
-
-def _untouched_check(prob, w_dev, o, n=2000, seed=1):
-    """Rows nobody read keep the generator's bits."""
-    rng = np.random.default_rng(seed)
-    hcs = np.concatenate([[0], np.cumsum(prob.rows)])
-    cand = rng.integers(0, int(hcs[-1]), size=n * 2)
-    cand = np.setdiff1d(cand, o["unique_keys"])[:n]
-    tt, rr = H.key_to_table_row(prob, cand)
-    for t in range(prob.T):
-        sel = rr[tt == t]
-        if sel.size == 0:
-            continue
-        got = H.rows_from_device(w_dev, prob, t, sel)
-        want = dg.weight_rows(prob, t, sel)
-        assert np.array_equal(got.view(np.uint16 if got.dtype == np.float16 else np.uint32),
-                              want.view(np.uint16 if want.dtype == np.float16 else np.uint32))
-
-
 @pytest.mark.parametrize("name,B,tau", [("uniform", 256, 256), ("stress", 256, 256),
                                         ("stress", 256, 16), ("mixed", 64, 256),
                                         ("hist", 64, 256), ("band", 512, 64),
@@ -235,22 +195,21 @@ def test_reduced_backward_vs_oracle(name, B, tau):
     prob = dg.make_problem(name, seed=600 + B, B=B)
     w_dev = dg.packed_weights_torch(prob, "cuda")
     gpu_backward(prob, w_dev, tau=tau)
-    o = H.oracle_sort(prob, tau)
-    keys = o["unique_keys"] if o["num_runs"] <= 60000 else _key_sample(prob, o)
-    rep = _sampled_backward_check(prob, None, w_dev, keys)
+    rep = fullcheck.backward_all(prob, w_dev)
     assert rep["ok"], rep
-    _untouched_check(prob, w_dev, o)
+    fullcheck.untouched_all(prob, w_dev)
 
 
 @pytest.mark.parametrize("name", ["stress", "uniform", "mixed", "band"])
-def test_full_size_backward_sampled(name):
+def test_full_size_backward_every_row(name):
+    """Full configuration at the plan's default tuning: every touched row
+    against the oracle, every other row bit-identical to the generator."""
     prob = dg.make_problem(name)
     w_dev = dg.packed_weights_torch(prob, "cuda")
     gpu_backward(prob, w_dev)
-    o = H.oracle_sort(prob, 256)
-    rep = _sampled_backward_check(prob, None, w_dev, _key_sample(prob, o))
+    rep = fullcheck.backward_all(prob, w_dev)
     assert rep["ok"], rep
-    _untouched_check(prob, w_dev, o)
+    fullcheck.untouched_all(prob, w_dev)
     del w_dev
     torch.cuda.empty_cache()
 
@@ -354,8 +313,7 @@ def test_workspace_reused_across_calls_and_sizes():
         tbe.tbe_backward_sgd(plan, prob.B, w0, d["indices"], d["offsets"], d["psw"], d["grad"],
                              prob.lr, ws)
         torch.cuda.synchronize()
-        o = H.oracle_sort(prob, 8)
-        rep = _sampled_backward_check(prob, None, w0, _key_sample(prob, o, n_short=500, seed=k))
+        rep = fullcheck.backward_all(prob, w0)
         assert rep["ok"], (k, rep)
         assert int(tbe.tbe_workspace_status(ws).item()) == 0   # error word stays clear
 
@@ -394,7 +352,7 @@ def test_stage_events_bracket_the_backward():
 def test_prepare_apply_overlapped_matches_backward_sgd(name, B, tau):
     """Integer stage on a second stream while the forward runs on the first,
     then the apply half: bit-identical weights to one tbe_backward_sgd call,
-    and the forward output is unaffected."""
+    the forward output unaffected, and both within tolerance of the oracle."""
     prob = dg.make_problem(name, B=B) if B else dg.make_problem(name)
     plan = H.make_plan(prob)
     tbe.tbe_set_tuning(plan, tau=tau)
@@ -424,6 +382,12 @@ def test_prepare_apply_overlapped_matches_backward_sgd(name, B, tau):
     assert torch.equal(out, out_ref)
     assert torch.equal(w_new, w_ref)
     assert int(tbe.tbe_workspace_status(ws2).item()) == 0
+    # and both against the oracle: every bag, every touched row
+    rep = fullcheck.forward_all(prob, out.cpu().numpy())
+    assert rep["ok"], rep
+    rep = fullcheck.backward_all(prob, w_new)
+    assert rep["ok"], rep
+    fullcheck.untouched_all(prob, w_new)
 
 
 def test_apply_refuses_a_payload_it_was_not_given():

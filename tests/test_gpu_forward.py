@@ -10,6 +10,7 @@ import torch
 import oracle
 from pooling_tbe_forward_amd import datagen as dg
 from pooling_tbe_forward_amd import tbe
+from tests import fullcheck
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -146,15 +147,15 @@ def test_reduced_configs_vs_oracle(name, B, index_dtype):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("name", ["uniform", "mixed", "hist"])
-def test_full_size_sampled(name):
-    """Full configuration, the launch configuration the benchmark times;
-    a sample of bags is recomputed by the oracle."""
+@pytest.mark.parametrize("name", ["uniform", "mixed", "hist", "stress", "band"])
+def test_full_size_every_bag(name):
+    """Full configuration, in the launch configuration the benchmark times:
+    every element of the output against the oracle."""
     prob = dg.make_problem(name)
     w_dev = dg.packed_weights_torch(prob, "cuda")
     out = _run_forward(prob, w_dev)
     assert np.isfinite(out).all()
-    rep = _sampled_forward_check(prob, w_dev, out, nbags=1500, seed=1)
+    rep = fullcheck.forward_all(prob, out)
     assert rep["ok"], rep
     del w_dev
     torch.cuda.empty_cache()

@@ -9,6 +9,7 @@ import torch
 import oracle
 from pooling_tbe_forward_amd import datagen as dg
 from pooling_tbe_forward_amd import tbe
+from tests import fullcheck
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -31,24 +32,10 @@ def test_mean_forward_vs_oracle(name, B):
     tbe.tbe_forward(plan, prob.B, w, d["indices"], d["offsets"], d["psw"], out)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    rng = np.random.default_rng(0)
-    bags = np.unique(np.concatenate([rng.choice(prob.T * prob.B, size=min(600, prob.T * prob.B),
-                                                replace=False),
-                                     np.flatnonzero(prob.lengths.ravel() == 0)[:20]]))
-    tt, bb = bags // prob.B, bags % prob.B
-    rowsets = [np.unique(prob.indices[prob.offsets[t * prob.B]:prob.offsets[(t + 1) * prob.B]])
-               for t in range(prob.T)]
-    ref = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob),
-                         H.sparse_tables(prob, rowsets), prob.indices, prob.offsets, prob.psw,
-                         prob.weighted, bag_list=bags, pooling="mean")
-    cols = np.concatenate([[0], np.cumsum(prob.dims)])
-    g = np.zeros_like(ref)
-    for k in range(bags.size):
-        D = int(prob.dims[tt[k]])
-        g[k, :D] = got[bb[k], cols[tt[k]]:cols[tt[k]] + D]
-        g[k, D:] = ref[k, D:]
-    rep = H.allclose_report(g, ref, 1e-5, 1e-6)
+    # every bag; fp32 accumulation of exact fp16 values stays inside the fp32 bound
+    rep = fullcheck.forward_all(prob, got, pooling="mean", tol=(1e-5, 1e-6))
     assert rep["ok"], rep
+    cols = np.concatenate([[0], np.cumsum(prob.dims)])
     if name == "toy":
         assert np.all(got[2, cols[1]:cols[2]] == 0)     # the forced empty bag (t=1, b=2)
 
@@ -96,18 +83,13 @@ def test_mean_backward_vs_oracle(name, B, tau, opt):
         tbe.tbe_backward_adagrad(plan, prob.B, w, s_dev, d["indices"], d["offsets"], d["psw"],
                                  d["grad"], prob.lr, ws)
     torch.cuda.synchronize()
-    o = H.oracle_sort(prob, tau)
-    keys = o["unique_keys"]
-    if keys.size > 20000:
-        keys = np.unique(np.random.default_rng(2).choice(keys, 20000, replace=False))
-    nr, st = _oracle_rows(prob, keys, "mean", state0 if opt == "adagrad" else None,
-                          tbe.ADAGRAD_EPS)
-    got = _rows_on_device(prob, w, keys, nr)
-    rep = H.allclose_report(got, nr, *H.TOL[prob.wdtype])
+    rep = fullcheck.backward_all(prob, w, pooling="mean",
+                                 adagrad=(state0, s_dev, tbe.ADAGRAD_EPS) if opt == "adagrad"
+                                 else None)
     assert rep["ok"], rep
-    if opt == "adagrad":
-        rep = H.allclose_report(s_dev.cpu().numpy()[keys], st, *H.TOL[prob.wdtype])
-        assert rep["ok"], rep
+    fullcheck.untouched_all(prob, w, state=(state0, s_dev))
+    keys = H.oracle_sort(prob, tau)["unique_keys"]
+    nr, _ = _oracle_rows(prob, keys[:50], "mean")
     # mean and sum differ wherever a bag has more than one lookup
     if name == "uniform":
         nr_sum, _ = _oracle_rows(prob, keys[:50], "sum")
@@ -127,6 +109,9 @@ def test_mean_prepare_apply_matches_whole():
     tbe.tbe_backward_apply(plan, prob.B, prob.N, d["psw"] is not None, w2, d["grad"], prob.lr, ws)
     torch.cuda.synchronize()
     assert torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    rep = fullcheck.backward_all(prob, w2, pooling="mean")
+    assert rep["ok"], rep
+    fullcheck.untouched_all(prob, w2)
 
 
 def test_pooling_mode_errors():

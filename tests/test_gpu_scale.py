@@ -4,21 +4,21 @@ quote for a production shard (83.9M lookups over 32 features, B = 131,072,
 282K times), run through the C ABI in the launch configuration the benchmark
 times:
 
-* forward: a sample of bags recomputed by the oracle;
+* forward: every element of the [131072, 4096] output against the oracle;
 * integer stage: sorted keys and positions, unique keys, run starts and
   lengths, short / long lists bit-exact against the oracle, all 83.9M keys;
-* backward-SGD: a sample of updated rows (every run of >= 256 lookups among
-  them) within tolerance of the oracle, untouched rows bit-identical.
+* backward-SGD: every updated row within tolerance of the oracle, every
+  other row bit-identical to the generator.
 """
 import numpy as np
 import pytest
 import torch
 
 from pooling_tbe_forward_amd import datagen as dg
+from tests import fullcheck
 from tests import helpers as H
-from tests.test_gpu_backward import (_compare_sort, _key_sample, _sampled_backward_check,
-                                     _untouched_check, gpu_backward, gpu_sort)
-from tests.test_gpu_forward import _run_forward, _sampled_forward_check
+from tests.test_gpu_backward import _compare_sort, gpu_backward, gpu_sort
+from tests.test_gpu_forward import _run_forward
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -29,17 +29,17 @@ def test_production_scale_forward_sort_backward():
     w_dev = dg.packed_weights_torch(prob, "cuda")
     out = _run_forward(prob, w_dev)
     assert np.isfinite(out).all()
-    rep = _sampled_forward_check(prob, w_dev, out, nbags=1500, seed=2)
+    rep = fullcheck.forward_all(prob, out)
     assert rep["ok"], rep
     del out
 
     o = H.oracle_sort(prob, 128)
     _compare_sort(gpu_sort(prob, tau=128), o, prob.N)
+    del o
 
     gpu_backward(prob, w_dev)
-    keys = _key_sample(prob, o, n_short=2000)
-    rep = _sampled_backward_check(prob, None, w_dev, keys)
+    rep = fullcheck.backward_all(prob, w_dev)
     assert rep["ok"], rep
-    _untouched_check(prob, w_dev, o)
+    fullcheck.untouched_all(prob, w_dev)
     del w_dev
     torch.cuda.empty_cache()

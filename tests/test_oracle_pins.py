@@ -333,3 +333,40 @@ def test_threads_do_not_change_bits(name, B):
         assert np.array_equal(f.view(np.uint64), res[0][0].view(np.uint64))
         assert np.array_equal(gr.view(np.uint64), res[0][1].view(np.uint64))
         assert np.array_equal(nr.view(np.uint64), res[0][2].view(np.uint64))
+
+
+@pytest.mark.parametrize("name,B,pooling", [("mixed", 40, "sum"), ("stress", 64, "mean"),
+                                            ("toy", None, "sum")])
+def test_table_split_equals_whole_problem(name, B, pooling):
+    """The full-size GPU checks run the oracle one table at a time
+    (tests/fullcheck.table_problem): each table's output columns and row
+    gradients must come out bit-identical to the oracle on the whole
+    multi-table problem."""
+    from tests import fullcheck
+    prob = dg.make_problem(name, seed=81, B=B) if B else dg.make_problem(name, seed=81)
+    tl = prob.table_of_lookup()
+    rowsets = [np.unique(prob.indices[tl == t]) for t in range(prob.T)]
+    tabs = H.sparse_tables(prob, rowsets)
+    code = H.wcode(prob)
+    whole = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
+                           prob.offsets, prob.psw, prob.weighted, pooling=pooling)
+    keys = H.oracle_sort(prob, 1 << 40)["unique_keys"]
+    _, nr = oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
+                                prob.offsets, prob.psw, prob.weighted, prob.grad, prob.lr, keys,
+                                pooling=pooling)
+    tt, _ = H.key_to_table_row(prob, keys)
+    cols = np.concatenate([[0], np.cumsum(prob.dims)])
+    for t in range(prob.T):
+        D = int(prob.dims[t])
+        sub = fullcheck.table_problem(prob, t)
+        rows, stabs = fullcheck._held(sub, t, prob)
+        f = oracle.forward(1, sub.B, sub.rows, sub.dims, code, stabs, sub.indices, sub.offsets,
+                           sub.psw, sub.weighted, pooling=pooling)
+        assert np.array_equal(f.view(np.uint64),
+                              np.ascontiguousarray(whole[:, cols[t]:cols[t] + D]).view(np.uint64))
+        if rows.size:
+            _, snr = oracle.backward_sgd(1, sub.B, sub.rows, sub.dims, code, stabs, sub.indices,
+                                         sub.offsets, sub.psw, sub.weighted, sub.grad, sub.lr,
+                                         rows, pooling=pooling)
+            assert np.array_equal(snr.view(np.uint64),
+                                  np.ascontiguousarray(nr[tt == t, :D]).view(np.uint64))
