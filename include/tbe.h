@@ -68,7 +68,10 @@ typedef struct {
     int32_t hist_mode;         /* 0 auto, 1 never, 2 always for eligible tables */
     int32_t hist_min_mean_len; /* auto: histogram path when N/(T*B) >= this */
     int32_t fwd_bags_per_wave; /* forward: consecutive bags handled by one wavefront */
-    int32_t bwd_runs_per_wave; /* backward: short runs handled by one wavefront per batch */
+    int32_t seg_slab_kib;      /* backward: target size (KiB) of the grad_output slab of one
+                                  column block of a table, B x columns x 4 bytes; rows
+                                  wider than that are reduced in column blocks of at least
+                                  16 lanes' loads (0 = whole rows) */
     int32_t reserved[10];
 } tbe_tuning;
 

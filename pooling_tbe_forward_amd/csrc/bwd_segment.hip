@@ -114,7 +114,9 @@ struct SegArgs {
     const uint32_t* hash_off;
     int32_t T;
     int32_t sumD;
-    int32_t lpr_log2;      // lanes per worker (log2)
+    int32_t lpr_log2;      // lanes per row slab of the combine (log2; from the widest row)
+    int32_t wl_log2;       // lanes per worker of the segment kernel (log2)
+    int32_t cw;            // columns per item (column block width)
     int32_t max_D;
     const float* grad;
     const void* sorted_payload;   // sample ids, or (sample, weight) pairs when weighted
@@ -129,7 +131,8 @@ struct SegArgs {
     float eps;                 // row-wise Adagrad only
     int32_t all_weighted;      // mean pooling: every table's payload weight applies
     float* state;              // row-wise Adagrad: fp32 state per row, by key
-    uint32_t chunk_blocks;     // the grid's last chunk_blocks blocks take long-run chunks
+    const uint32_t* tab_ranges;   // [3][T+1]: first short run, long run, chunk of each table
+    const uint2* chunk_info;      // {first sorted position, length} of each chunk
     const uint32_t* mode;      // payload the integer stage left in the workspace
     uint32_t expect_mode;      // ... and the payload this call was told to expect
     uint32_t* err;             // the workspace's error word
@@ -217,11 +220,12 @@ __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0
 #pragma unroll
     for (int u = 0; u < S; ++u) pre[u + 1] = pre[u] + len[u];
     const uint32_t C = pre[S];
-    for (uint32_t cb = 0; cb < C; cb += L) {
-        // lane `sub` fetches contribution cb + sub
+    // lane `sub` fetches the sample id (and weight) of contribution cb + sub;
+    // the next group's are fetched while the current group's rows are summed
+    auto fetch = [&](uint32_t cb, uint32_t& my_smp, float& my_w) {
         const uint32_t ci = cb + sub;
-        uint32_t my_smp = 0;
-        float my_w = 1.f;
+        my_smp = 0;
+        my_w = 1.f;
         int sl = 0;
 #pragma unroll
         for (int u = 1; u < S; ++u) sl += ci >= pre[u] ? 1 : 0;
@@ -255,6 +259,14 @@ __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0
                 if (need) my_smp = sv;
             }
         }
+    };
+    uint32_t nsmp;
+    float nw;
+    fetch(0, nsmp, nw);
+    for (uint32_t cb = 0; cb < C; cb += L) {
+        const uint32_t my_smp = nsmp;
+        const float my_w = nw;
+        if (cb + L < C) fetch(cb + L, nsmp, nw);
         const uint32_t n = min(static_cast<uint32_t>(L), C - cb);
         for (uint32_t j0 = 0; j0 < n; j0 += U) {
             // all U row loads are issued unconditionally (an idle slot reads
@@ -296,267 +308,177 @@ __device__ __forceinline__ void flat_sum(const SegArgs& c, const uint32_t (&pos0
     }
 }
 
-// One batch of S short runs per worker: prefetch the S weight rows, sum the
-// runs' contributions, apply SGD.
-// Table descriptor t: from the LDS copy when the block staged one, else from
-// global memory.
-template <bool LDSD>
-__device__ __forceinline__ TableDesc table_desc(const SegArgs& c, const TableDesc* sdesc, int t)
-{
-    if (LDSD) return sdesc[t];
-    return ldg(c.tables + t);
-}
-
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD, int OPT>
-__device__ __forceinline__ void short_batch(const SegArgs& c, WT* __restrict__ weights,
-                                            const TableDesc* sdesc,
-                                            const uint4 (&info)[S], const uint2 (&first)[S],
-                                            int sub, int L, int gbase)
-{
-    uint32_t fsmp[S];
-    float fw[S];
-#pragma unroll
-    for (int u = 0; u < S; ++u) {
-        fsmp[u] = first[u].x;
-        fw[u] = __uint_as_float(first[u].y);
-    }
-    for (int c0 = 0; c0 < c.max_D; c0 += VEC * L) {
-        const int col = c0 + sub * VEC;
-        Pack<WT, VEC> w_old[S];
-        ACC acc[S][VEC];
-        WT* wrow[S];
-        const float* gcol[S];
-        bool tw[S];
-        uint32_t len[S], pos0[S];
-        float s_old[S];
-        int Dr[S];
-#pragma unroll
-        for (int u = 0; u < S; ++u) {
-            const TableDesc d = table_desc<LDSD>(c, sdesc, static_cast<int>(info[u].w));
-            // a run whose table is narrower than this column slab contributes
-            // nothing here (its lanes keep the loop shape but load no rows)
-            const bool act = info[u].z > 0 && col < d.D;
-            len[u] = info[u].z;
-            pos0[u] = info[u].y;
-            wrow[u] = weights + d.w_off + static_cast<int64_t>(info[u].x - d.hash_off) * d.D + col;
-            gcol[u] = act ? c.grad + d.out_off + col : nullptr;
-            tw[u] = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
-            // unconditional (an idle slot reads the first row of the weights)
-            w_old[u] = ldg_stream(reinterpret_cast<const Pack<WT, VEC>*>(act ? wrow[u] : weights));
-            Dr[u] = d.D;
-            if (OPT == kAdagrad)   // every lane of the worker: the state feeds all of them
-                s_old[u] = ldg(c.state + (info[u].z > 0 ? info[u].x : 0u));
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) acc[u][q] = ACC(0);
-        }
-        flat_sum<ACC, VEC, S, U, WEIGHTED, true>(c, pos0, len, gcol, tw, fsmp, fw, sub, L, gbase,
-                                                 acc);
-        // all S updates first, then the stores (a wait for one row's old
-        // value never includes another row's store)
-        Pack<WT, VEC> o[S];
-        float s_new[S];
-#pragma unroll
-        for (int u = 0; u < S; ++u) {
-            if (OPT == kAdagrad)
-                o[u] = adagrad_row<WT, ACC, VEC>(w_old[u], acc[u], s_old[u], Dr[u], L, c.lr,
-                                                 c.eps, s_new[u]);
-            else
-                o[u] = sgd_row<WT, ACC, VEC>(w_old[u], acc[u], c.lr);
-        }
-#pragma unroll
-        for (int u = 0; u < S; ++u) {
-            if (gcol[u]) stg_stream(reinterpret_cast<Pack<WT, VEC>*>(wrow[u]), o[u]);
-            if (OPT == kAdagrad && sub == 0 && info[u].z > 0) c.state[info[u].x] = s_new[u];
-        }
-    }
-}
-
-// Short runs.  Batches of G*S consecutive run records are dealt to the
-// wavefronts round-robin (neighbouring runs of a Zipf table, which are the
-// long ones, land on different wavefronts); a batch is read with one load
-// (one record per lane, the next batch already in flight) and handed to the G
-// workers S at a time through lane shuffles.  Runs shorter than kF32Run
-// lookups sum in fp32 (error well inside tolerance); longer ones (only when
-// tau is raised) and fp16 tables use the ACC type.
+// Short runs are summed in fp32 below kF32Run lookups (error well inside
+// tolerance); longer ones (only when tau is raised) and fp16 tables use the
+// ACC type.
 constexpr uint32_t kF32Run = 256;
-// A wave loads a batch of G * S run records one per lane, so G = 64 / L must
+// A wave loads a unit of G * S run records one per lane, so G = 64 / L must
 // not exceed 64 / S: workers are at least 2^kMinLprLog2 lanes wide (S = 2),
 // even where a row fits one lane (the second lane then idles).
 constexpr int kMinLprLog2 = 1;
+constexpr int kLdsTables = 256;   // table descriptors and item offsets staged in LDS
 
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, bool LDSD, int OPT>
-__device__ __forceinline__ void short_runs(const SegArgs& c, WT* __restrict__ weights,
-                                           const TableDesc* sdesc, uint32_t wave, uint32_t nwaves)
+// A wave-uniform value kept in a scalar register (values read from LDS land in
+// vector registers, one copy per lane).
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ TableDesc uniform_desc(const TableDesc& d)
 {
-    const int lane = threadIdx.x & 63;
-    const int g_log2 = 6 - c.lpr_log2;
-    const int G = 1 << g_log2;
-    const int L = 1 << c.lpr_log2;
-    const int grp = lane >> c.lpr_log2;
-    const int sub = lane & (L - 1);
-    const int gbase = grp << c.lpr_log2;
-    const uint32_t nshort = ldg(c.counts + 1);
-    const uint32_t per = static_cast<uint32_t>(G * S);
-    const uint32_t kend = nshort;
-    uint32_t k0 = wave * per;
-    uint4 nxt = make_uint4(0, 0, 0, 0);
-    uint2 nxtf = make_uint2(0, 0);
-    if (lane < static_cast<int>(per) && k0 + lane < kend) {
-        nxt = ldg(c.short_info + k0 + lane);
-        nxtf = ldg(c.short_first + k0 + lane);
+    TableDesc r;
+    uint32_t w[8];
+    __builtin_memcpy(w, &d, sizeof(TableDesc));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = uni(w[k]);
+    __builtin_memcpy(&r, w, sizeof(TableDesc));
+    return r;
+}
+
+// One unit of short runs: up to G*S consecutive short runs of one table (one
+// record per lane), S per worker, for one column block of the table.  Each
+// worker prefetches its S weight rows, walks the runs' contributions as one
+// flat sequence (U gradient rows in flight), then applies the update; all S
+// updates are computed before the stores (a wait for one row's old value
+// never includes another row's store).
+// The unit's run records, one per lane (zero past the unit's end).
+__device__ __forceinline__ void unit_records(const SegArgs& c, uint32_t k0, uint32_t n, int lane,
+                                             uint4& rec, uint2& first)
+{
+    rec = make_uint4(0, 0, 0, 0);
+    first = make_uint2(0, 0);
+    if (lane < static_cast<int>(n)) {
+        rec = ldg(c.short_info + k0 + lane);
+        first = ldg(c.short_first + k0 + lane);
     }
-    for (; k0 < kend; k0 += nwaves * per) {
-        const uint4 mine = nxt;
-        const uint2 minef = nxtf;
-        const uint32_t k1 = k0 + nwaves * per;
-        nxt = make_uint4(0, 0, 0, 0);
-        nxtf = make_uint2(0, 0);
-        if (lane < static_cast<int>(per) && k1 + lane < kend) {
-            nxt = ldg(c.short_info + k1 + lane);
-            nxtf = ldg(c.short_first + k1 + lane);
-        }
-        uint4 info[S];
-        uint2 first[S];
-        uint32_t maxlen = 0;
+}
+
+// Updated rows of a short unit, stored during the next unit: the vector memory
+// counter is one in-order counter for loads and stores, so stores issued
+// before a unit's first loads would make every wait for those loads wait for
+// the stores too; issued after them, they complete while the loads are in
+// flight.
+template <typename WT, int VEC, int S, int OPT>
+struct PendingRows {
+    Pack<WT, VEC> o[S];
+    WT* wrow[S];
+    float s_new[S];
+    uint32_t skey[S];
+    uint32_t on = 0;    // bit u: row u is to be stored
+    uint32_t son = 0;   // bit u: state u is to be stored (row-wise Adagrad)
+
+    __device__ __forceinline__ void flush(float* state)
+    {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int src = u * G + grp;
-            info[u].x = __shfl(mine.x, src);
-            info[u].y = __shfl(mine.y, src);
-            info[u].z = __shfl(mine.z, src);
-            info[u].w = __shfl(mine.w, src);
-            first[u].x = __shfl(minef.x, src);
-            first[u].y = __shfl(minef.y, src);
-            maxlen = max(maxlen, info[u].z);
+            if (on & (1u << u)) stg_stream(reinterpret_cast<Pack<WT, VEC>*>(wrow[u]), o[u]);
+            if (OPT == kAdagrad && (son & (1u << u))) state[skey[u]] = s_new[u];
         }
-        if (sizeof(ACC) == 8 && maxlen < kF32Run)
-            short_batch<WT, float, VEC, S, U, WEIGHTED, LDSD, OPT>(c, weights, sdesc, info, first,
-                                                                   sub, L, gbase);
-        else
-            short_batch<WT, ACC, VEC, S, U, WEIGHTED, LDSD, OPT>(c, weights, sdesc, info, first,
-                                                                 sub, L, gbase);
+        on = son = 0;
     }
+};
+
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, int OPT>
+__device__ __forceinline__ void short_unit(const SegArgs& c, WT* __restrict__ weights,
+                                           const TableDesc& d, const uint4& mine,
+                                           const uint2& minef, int col, int sub, int L, int G,
+                                           int grp, int gbase, PendingRows<WT, VEC, S, OPT>& pend)
+{
+    const bool tw = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
+    const bool act_col = col < d.D;
+    uint32_t len[S], pos0[S], fsmp[S], key[S];
+    float fw[S];
+    bool twa[S];
+    uint32_t maxlen = 0;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+        const int src = u * G + grp;
+        key[u] = __shfl(mine.x, src);
+        pos0[u] = __shfl(mine.y, src);
+        len[u] = __shfl(mine.z, src);
+        fsmp[u] = __shfl(minef.x, src);
+        fw[u] = __uint_as_float(__shfl(minef.y, src));
+        twa[u] = tw;
+        maxlen = max(maxlen, len[u]);
+    }
+    auto body = [&](auto acc_tag) {
+        using A = decltype(acc_tag);
+        Pack<WT, VEC> w_old[S];
+        A acc[S][VEC];
+        WT* wrow[S];
+        const float* gcol[S];
+        float s_old[S];
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            // a slot without a run (len 0) or a lane past the row keeps the
+            // loop shape but loads no gradient rows
+            const bool act = len[u] > 0 && act_col;
+            wrow[u] = weights + d.w_off + static_cast<int64_t>(key[u] - d.hash_off) * d.D + col;
+            gcol[u] = act ? c.grad + d.out_off + col : nullptr;
+            // unconditional (an idle slot reads the first row of the weights)
+            w_old[u] = ldg_stream(reinterpret_cast<const Pack<WT, VEC>*>(act ? wrow[u] : weights));
+            if (OPT == kAdagrad)   // every lane of the worker: the state feeds all of them
+                s_old[u] = ldg(c.state + (len[u] > 0 ? key[u] : 0u));
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) acc[u][q] = A(0);
+        }
+        pend.flush(c.state);   // the previous unit's rows, now that this unit's loads are out
+        flat_sum<A, VEC, S, U, WEIGHTED, true>(c, pos0, len, gcol, twa, fsmp, fw, sub, L, gbase,
+                                               acc);
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            if (OPT == kAdagrad)
+                pend.o[u] = adagrad_row<WT, A, VEC>(w_old[u], acc[u], s_old[u], d.D, L, c.lr,
+                                                    c.eps, pend.s_new[u]);
+            else
+                pend.o[u] = sgd_row<WT, A, VEC>(w_old[u], acc[u], c.lr);
+            pend.wrow[u] = wrow[u];
+            if (gcol[u]) pend.on |= 1u << u;
+            if (OPT == kAdagrad) {
+                pend.skey[u] = key[u];
+                if (sub == 0 && len[u] > 0) pend.son |= 1u << u;
+            }
+        }
+    };
+    if (sizeof(ACC) == 8 && maxlen < kF32Run)
+        body(float(0));
+    else
+        body(ACC(0));
 }
 
-// One wavefront per chunk (rows of L = 64 lanes): the wave keeps 8 gradient
-// rows in flight over the whole chunk and writes its partial; the four waves
-// of a block take four chunks.
+// One long-run chunk (`chunk` consecutive lookups of one long run) for one
+// column block: the wave's G workers take consecutive shares of it, each
+// with 8 gradient rows in flight, and are folded in a fixed order (lane
+// swaps), so the partial does not depend on scheduling; worker 0 writes the
+// chunk's partial (fp64 for fp32 tables) to the workspace.
 template <typename ACC, int VEC, bool WEIGHTED>
-__device__ __forceinline__ void long_chunks_wave(const SegArgs& c, ACC* __restrict__ partials,
-                                                 uint32_t wave, uint32_t nwaves)
+__device__ __forceinline__ void chunk_unit(const SegArgs& c, ACC* __restrict__ partials,
+                                           const TableDesc& d, uint32_t q, int col, int lane,
+                                           int sub, int L, int G, int grp, int gbase)
 {
-    const int lane = threadIdx.x & 63;
-    const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
-    const uint32_t nchunks = min(ldg(c.counts + 3), c.max_chunks);
-    for (uint32_t q = wave; q < nchunks; q += nwaves) {
-        uint32_t lo = 0, hi = nlong;  // long run owning chunk q: last with first chunk <= q
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (ldg(c.long_info + mid).w <= q) lo = mid; else hi = mid;
-        }
-        const uint4 li = ldg(c.long_info + lo);
-        const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
-        const bool tw = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
-        const uint32_t i0 = li.y + (q - li.w) * c.chunk;
-        const uint32_t i1 = min(li.y + li.z, i0 + c.chunk);
-        ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
-        for (int c0 = 0; c0 < d.D; c0 += 64 * VEC) {
-            const int col = c0 + lane * VEC;
-            const uint32_t p0[1] = {i0};
-            const uint32_t ln[1] = {i1 - i0};
-            const float* const gc[1] = {col < d.D ? c.grad + d.out_off + col : nullptr};
-            const bool twa[1] = {tw};
-            ACC acc[1][VEC];
+    const uint2 ci = ldg(c.chunk_info + q);
+    const bool tw = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
+    const uint32_t i0 = ci.x;
+    const uint32_t len = ci.y;
+    const uint32_t per = (len + G - 1) / G;   // this worker's share
+    const uint32_t s0 = min(len, static_cast<uint32_t>(grp) * per);
+    const uint32_t s1 = min(len, s0 + per);
+    const uint32_t p0[1] = {i0 + s0};
+    const uint32_t ln[1] = {s1 - s0};
+    const float* const gc[1] = {col < d.D ? c.grad + d.out_off + col : nullptr};
+    const bool twa[1] = {tw};
+    ACC acc[1][VEC];
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
-            const uint32_t nof[1] = {0};
-            const float now[1] = {1.f};
-            flat_sum<ACC, VEC, 1, 8, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, lane, 64, 0,
-                                                      acc);
-            if (col < d.D) {
-                Pack<ACC, VEC> o;
+    for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
+    const uint32_t nof[1] = {0};
+    const float now[1] = {1.f};
+    flat_sum<ACC, VEC, 1, 8, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, sub, L, gbase, acc);
+    for (int m = 32; m >= L; m >>= 1)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) o.v[k] = acc[0][k];
-                *reinterpret_cast<Pack<ACC, VEC>*>(prow + col) = o;
-            }
-        }
-    }
-}
-
-// Long runs, step 1: one block per chunk of `chunk` lookups writes the
-// chunk's partial sum (fp64 for fp32 tables) to the workspace.  The block's
-// 256 / L slots of L lanes take consecutive sub-ranges of the chunk, each
-// with 8 gradient rows in flight; the slots are folded in a fixed order (lane
-// swaps inside a wave, then the four waves through LDS), so the partial does
-// not depend on scheduling and a chunk's dependent chain is one slot's share
-// of it rather than the whole chunk (stress workload: segment kernel 101 ->
-// 89 us, band 94 -> 77 us).  Rows as wide as a wavefront (L = 64) take
-// long_chunks_wave instead: there the block form measured slower (mixed
-// workload 526 -> 552 us).
-template <typename ACC, int VEC, bool WEIGHTED>
-__device__ __forceinline__ void long_chunks_block(const SegArgs& c, ACC* __restrict__ partials,
-                                                  Pack<ACC, VEC> (*red)[64], uint32_t blk,
-                                                  uint32_t nblk)
-{
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int lpr = c.lpr_log2;
-    const int L = 1 << lpr;
-    const int sub = lane & (L - 1);
-    const int gbase = (lane >> lpr) << lpr;
-    const uint32_t slot = static_cast<uint32_t>(tid >> lpr);
-    const uint32_t nslots = 256u >> lpr;
-    const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
-    const uint32_t nchunks = min(ldg(c.counts + 3), c.max_chunks);
-    for (uint32_t q = blk; q < nchunks; q += nblk) {
-        uint32_t lo = 0, hi = nlong;  // long run owning chunk q: last with first chunk <= q
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (ldg(c.long_info + mid).w <= q) lo = mid; else hi = mid;
-        }
-        const uint4 li = ldg(c.long_info + lo);
-        const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
-        const bool tw = WEIGHTED && (c.all_weighted || (d.flags & TD_WEIGHTED));
-        const uint32_t i0 = li.y + (q - li.w) * c.chunk;
-        const uint32_t len = min(li.y + li.z, i0 + c.chunk) - i0;
-        const uint32_t per = (len + nslots - 1) / nslots;   // this slot's share
-        const uint32_t s0 = min(len, slot * per);
-        const uint32_t s1 = min(len, s0 + per);
-        ACC* __restrict__ prow = partials + static_cast<int64_t>(q) * c.max_D;
-        for (int c0 = 0; c0 < d.D; c0 += (VEC << lpr)) {
-            const int col = c0 + sub * VEC;
-            const uint32_t p0[1] = {i0 + s0};
-            const uint32_t ln[1] = {s1 - s0};
-            const float* const gc[1] = {col < d.D ? c.grad + d.out_off + col : nullptr};
-            const bool twa[1] = {tw};
-            ACC acc[1][VEC];
+        for (int k = 0; k < VEC; ++k) acc[0][k] += __shfl_xor(acc[0][k], m);
+    if (grp == 0 && col < d.D) {
+        Pack<ACC, VEC> o;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[0][k] = ACC(0);
-            const uint32_t nof[1] = {0};
-            const float now[1] = {1.f};
-            flat_sum<ACC, VEC, 1, 8, WEIGHTED, false>(c, p0, ln, gc, twa, nof, now, sub, L,
-                                                      gbase, acc);
-            for (int m = 32; m >= L; m >>= 1)
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) acc[0][k] += __shfl_xor(acc[0][k], m);
-            if (lane < L) {
-                Pack<ACC, VEC> o;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) o.v[k] = acc[0][k];
-                red[wave][lane] = o;
-            }
-            __syncthreads();
-            if (wave == 0 && lane < L && col < d.D) {
-                Pack<ACC, VEC> o;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    o.v[k] = ((red[0][lane].v[k] + red[1][lane].v[k]) + red[2][lane].v[k]) +
-                             red[3][lane].v[k];
-                *reinterpret_cast<Pack<ACC, VEC>*>(prow + col) = o;
-            }
-            __syncthreads();   // red is reused by the next slab or chunk
-        }
+        for (int k = 0; k < VEC; ++k) o.v[k] = acc[0][k];
+        *reinterpret_cast<Pack<ACC, VEC>*>(partials + static_cast<int64_t>(q) * c.max_D + col) = o;
     }
 }
 
@@ -653,42 +575,115 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
     }
 }
 
-constexpr int kLdsTables = 256;   // table descriptors staged in LDS
-
-// BLOCKCHUNK: long-run chunks take a block each (rows narrower than a
-// wavefront) rather than a wavefront each; an instantiation of its own, since
-// the block form's code measured slower in the other kernels (mixed workload
-// 527 -> 558 us) even where it never runs.
-template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, int OPT,
-          bool BLOCKCHUNK>
-__global__ __launch_bounds__(256) void k_segment(SegArgs c, WT* __restrict__ weights,
-                                                 ACC* __restrict__ partials)
+// Segment reduce + update, one persistent launch.  Work is cut into items, a
+// table's column block (cw columns: the table's grad_output slab is then
+// B x cw x 4 bytes, sized to stay in one XCD's L2), and an item's units are
+// its long-run chunks and its short-run units.  Blocks are dealt to the eight
+// XCDs round-robin (block b runs on XCD b mod 8), so XCD x takes items x,
+// x + 8, ... and its waves split each item's units round-robin; an XCD's L2
+// then holds the slabs of the one or two items its waves are on, rather than
+// the slabs of every table the chip is working on.  Column blocks of equal
+// width make items of one workload cost about the same, which keeps the XCDs
+// even; with fewer than 16 items each is dealt as several slices (slice s
+// of n takes the item's units u = s mod n, so every slice gets its share of
+// the dearer chunks), so no XCD idles.  (A shared cursor handing units out
+// one atomic at a time measured about nine times slower: atomics on one
+// address complete one after another.)
+template <typename WT, typename ACC, int VEC, int S, int U, bool WEIGHTED, int OPT>
+__global__ __launch_bounds__(256, sizeof(ACC) == 4 ? 5 : 1) void k_segment(
+    SegArgs c, WT* __restrict__ weights, ACC* __restrict__ partials)
 {
-    static_assert((S << (6 - kMinLprLog2)) <= 64, "a batch is loaded one record per lane");
+    static_assert((S << (6 - kMinLprLog2)) <= 64, "a unit is loaded one record per lane");
     __shared__ TableDesc sdesc[kLdsTables];
-    __shared__ Pack<ACC, VEC> red[BLOCKCHUNK ? 4 : 1][64];
+    __shared__ uint32_t sitem[kLdsTables + 1];   // first item of each table
     if (payload_mismatch(c)) return;
-    const uint32_t wib = threadIdx.x >> 6;
-    // blocks [0, gridDim.x - chunk_blocks) take short runs (dispatched first:
-    // measured faster than chunks first), the rest long-run chunks
-    const uint32_t short_blocks = gridDim.x - c.chunk_blocks;
-    if (blockIdx.x < short_blocks) {
-        const uint32_t wave = blockIdx.x * 4 + wib;
-        const uint32_t nwaves = short_blocks * 4;
-        if (c.T <= kLdsTables) {
-            for (int i = threadIdx.x; i < c.T; i += 256) sdesc[i] = ldg(c.tables + i);
-            __syncthreads();
-            short_runs<WT, ACC, VEC, S, U, WEIGHTED, true, OPT>(c, weights, sdesc, wave, nwaves);
-        } else {
-            short_runs<WT, ACC, VEC, S, U, WEIGHTED, false, OPT>(c, weights, sdesc, wave, nwaves);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const bool lds = c.T <= kLdsTables;
+    const int L = 1 << c.wl_log2;
+    const int G = 64 >> c.wl_log2;
+    const int grp = lane >> c.wl_log2;
+    const int sub = lane & (L - 1);
+    const int gbase = grp << c.wl_log2;
+    if (lds) {
+        for (int i = tid; i < c.T; i += 256) sdesc[i] = ldg(c.tables + i);
+        __syncthreads();
+        if (tid < 64) {   // items per table: its column blocks
+            uint32_t run = 0;
+            for (int b0 = 0; b0 < c.T; b0 += 64) {
+                const int t = b0 + lane;
+                const uint32_t nb = t < c.T ? static_cast<uint32_t>((sdesc[t].D + c.cw - 1) / c.cw)
+                                            : 0u;
+                uint32_t inc = nb;
+#pragma unroll
+                for (int dd = 1; dd < 64; dd <<= 1) {
+                    const uint32_t o = __shfl_up(inc, dd);
+                    if (lane >= dd) inc += o;
+                }
+                if (t < c.T) sitem[t] = run + inc - nb;
+                run += __shfl(inc, 63);
+            }
+            if (lane == 0) sitem[c.T] = run;
+        }
+        __syncthreads();
+    }
+    // without the LDS staging (very many tables) an item is a whole table
+    const uint32_t nitems = lds ? sitem[c.T] : static_cast<uint32_t>(c.T);
+    const uint32_t nsplit = nitems >= 16 ? 1u : (16u + nitems - 1) / nitems;
+    const uint32_t npieces = nitems * nsplit;
+    const uint32_t T1 = static_cast<uint32_t>(c.T) + 1;
+    const uint32_t xcd = blockIdx.x & 7u;
+    const uint32_t wx = (blockIdx.x >> 3) * 4 + (tid >> 6);
+    const uint32_t nwx = (gridDim.x >> 3) * 4;
+    const uint32_t GS = static_cast<uint32_t>(G * S);
+    PendingRows<WT, VEC, S, OPT> pend;
+    for (uint32_t pc = xcd; pc < npieces; pc += 8) {
+        const uint32_t it = pc / nsplit, sl = pc - it * nsplit;
+        int t = static_cast<int>(it), cb = 0;
+        if (lds) {   // last table whose first item is <= it
+            int lo = 0, hi = c.T;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (sitem[mid] <= it) lo = mid; else hi = mid;
+            }
+            t = lo;
+            cb = static_cast<int>(it - sitem[t]);
+        }
+        t = static_cast<int>(uni(static_cast<uint32_t>(t)));
+        cb = static_cast<int>(uni(static_cast<uint32_t>(cb)));
+        const TableDesc d = uniform_desc(lds ? sdesc[t] : ldg(c.tables + t));
+        const int col = cb * c.cw + sub * VEC;
+        const uint32_t fs0 = uni(ldg(c.tab_ranges + t)), fs1 = uni(ldg(c.tab_ranges + t + 1));
+        const uint32_t fc0 = uni(ldg(c.tab_ranges + 2 * T1 + t));
+        const uint32_t nch = uni(ldg(c.tab_ranges + 2 * T1 + t + 1)) - fc0;
+        const uint32_t nu = nch + (fs1 - fs0 + GS - 1) / GS;   // chunks, then short units
+        // the waves that take a piece's (dearer) chunks move with the piece
+        const uint32_t rot = (pc >> 3) * 131u % nwx;
+        const uint32_t step = nsplit * nwx;
+        uint32_t u = sl + nsplit * ((wx + rot) % nwx);
+        // a short unit's records are fetched one unit ahead
+        uint4 nrec;
+        uint2 nfirst;
+        auto fetch = [&](uint32_t uu) {
+            const uint32_t k0 = fs0 + (uu - nch) * GS;
+            unit_records(c, k0, uu >= nch && uu < nu ? min(GS, fs1 - k0) : 0u, lane, nrec, nfirst);
+        };
+        fetch(u);
+        for (; u < nu; u += step) {
+            const uint4 rec = nrec;
+            const uint2 first = nfirst;
+            fetch(u + step);
+            if (u < nch) {
+                pend.flush(c.state);
+                chunk_unit<ACC, VEC, WEIGHTED>(c, partials, d, fc0 + u, col, lane, sub, L, G, grp,
+                                               gbase);
+            } else {
+                short_unit<WT, ACC, VEC, S, U, WEIGHTED, OPT>(c, weights, d, rec, first, col, sub,
+                                                              L, G, grp, gbase, pend);
+            }
         }
     }
-    else if constexpr (BLOCKCHUNK)
-        long_chunks_block<ACC, VEC, WEIGHTED>(c, partials, red, blockIdx.x - short_blocks,
-                                              c.chunk_blocks);
-    else
-        long_chunks_wave<ACC, VEC, WEIGHTED>(c, partials, (blockIdx.x - short_blocks) * 4 + wib,
-                                             c.chunk_blocks * 4);
+    pend.flush(c.state);
 }
 
 uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
@@ -699,24 +694,23 @@ uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
     return static_cast<uint32_t>(b);
 }
 
-template <typename WT, typename ACC, int VEC, int S, int U, int OPT, bool BLOCKCHUNK>
-void launch_seg_c(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
+// Resident blocks of a 256-thread kernel on the whole device (all XCDs), a
+// multiple of 8 so every XCD gets the same number of persistent blocks; one
+// cached value per kernel (the devices a process uses are alike).
+template <auto Kernel>
+uint32_t persistent_blocks()
 {
-    if (a.payload_pairs)
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, true, OPT, BLOCKCHUNK>), grid,
-                           dim3(256), 0, a.stream, c, w, partials);
-    else
-        hipLaunchKernelGGL((k_segment<WT, ACC, VEC, S, U, false, OPT, BLOCKCHUNK>), grid,
-                           dim3(256), 0, a.stream, c, w, partials);
-}
-
-template <typename WT, typename ACC, int VEC, int S, int U, int OPT>
-void launch_seg(const BwdArgs& a, dim3 grid, const SegArgs& c, WT* w, ACC* partials)
-{
-    if (c.lpr_log2 < 6)   // rows narrower than a wavefront: a block per chunk
-        launch_seg_c<WT, ACC, VEC, S, U, OPT, true>(a, grid, c, w, partials);
-    else
-        launch_seg_c<WT, ACC, VEC, S, U, OPT, false>(a, grid, c, w, partials);
+    static int cached = 0;
+    if (!cached) {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, Kernel, 256, 0) != hipSuccess ||
+            cus <= 0 || per <= 0)
+            return 2048;
+        cached = ((cus * per + 7) / 8) * 8;
+    }
+    return static_cast<uint32_t>(cached);
 }
 
 template <typename WT, typename ACC, int VEC, int OPT>
@@ -726,19 +720,20 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     char* ws = a.ws;
     ACC* partials = reinterpret_cast<ACC*>(ws + L.off_partials);
     WT* w = static_cast<WT*>(a.weights);
-    const int G = 1 << (6 - c.lpr_log2);
-    const uint32_t short_blocks = blocks_for(L.N, int64_t(4) * G * 2, 2048);  // G*S runs per wave batch
-    // a block per chunk (rows narrower than a wave), else a wave per chunk
-    c.chunk_blocks = c.lpr_log2 == 6 ? blocks_for(L.max_chunks, 4, 1024)
-                                     : blocks_for(L.max_chunks, 1, 4096);
     // a block per long run (at most 4096: measured best of 1024..8192 on the
     // stress, band and mixed workloads)
     const uint32_t b_long = blocks_for(L.max_long, 1, 4096);
-    const dim3 grid(short_blocks + c.chunk_blocks);
-    // short-run batches: S = 2 runs per worker, U = 4 gradient rows in flight
-    // (measured best of S in {1,2,4,8} x U in {4,8} on the uniform, stress and
-    // mixed workloads)
-    launch_seg<WT, ACC, VEC, 2, 4, OPT>(a, grid, c, w, partials);
+    // short-run units: S = 2 runs per worker, U = 4 gradient rows in flight
+    constexpr int S = 2, U = 4;
+    if (a.payload_pairs) {
+        constexpr auto k = k_segment<WT, ACC, VEC, S, U, true, OPT>;
+        hipLaunchKernelGGL(k, dim3(persistent_blocks<k>()), dim3(256), 0, a.stream, c, w,
+                           partials);
+    } else {
+        constexpr auto k = k_segment<WT, ACC, VEC, S, U, false, OPT>;
+        hipLaunchKernelGGL(k, dim3(persistent_blocks<k>()), dim3(256), 0, a.stream, c, w,
+                           partials);
+    }
     stage_mark(a.plan, 4, a.stream);
     hipLaunchKernelGGL((k_long_combine<WT, ACC, VEC, OPT>), dim3(b_long), dim3(256), 0, a.stream,
                        c, w, static_cast<const ACC*>(partials));
@@ -795,6 +790,17 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     const int lanes = (p->max_D + vec - 1) / vec;
     int lpr_log2 = kMinLprLog2;
     while ((1 << lpr_log2) < lanes && lpr_log2 < 6) ++lpr_log2;
+    // Worker width: a column block of cw = vec * 2^wl columns makes a
+    // table's grad_output slab B * cw * 4 bytes; the widest block within the
+    // tuning's slab target, but workers of at least 16 lanes (narrower ones
+    // measured slower: each block re-reads its runs' records and payload),
+    // whole rows when the update needs them (row-wise Adagrad) or the tables
+    // are too many to stage.
+    int wl_log2 = lpr_log2;
+    const int64_t slab = int64_t(p->tuning.seg_slab_kib) * 1024;
+    if (!a.state && slab > 0 && p->T <= kLdsTables) {
+        while (wl_log2 > 4 && int64_t(a.B) * (int64_t(vec) << wl_log2) * 4 > slab) --wl_log2;
+    }
 
     char* ws = a.ws;
     SegArgs c;
@@ -803,6 +809,8 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.T = p->T;
     c.sumD = p->sum_D;
     c.lpr_log2 = lpr_log2;
+    c.wl_log2 = wl_log2;
+    c.cw = vec << wl_log2;
     c.max_D = p->max_D;
     c.grad = a.grad;
     c.sorted_payload = ws + L.off_vals[a.final_buf];
@@ -817,7 +825,8 @@ hipError_t run_segment_sgd(const BwdArgs& a)
     c.eps = a.eps;
     c.state = a.state;
     c.all_weighted = p->pooling == TBE_POOL_MEAN ? 1 : 0;
-    c.chunk_blocks = 0;
+    c.tab_ranges = reinterpret_cast<const uint32_t*>(ws + L.off_tab_ranges);
+    c.chunk_info = reinterpret_cast<const uint2*>(ws + L.off_chunk_info);
     c.mode = reinterpret_cast<const uint32_t*>(ws + L.off_ctl) + kCtlMode;
     c.expect_mode = a.payload_pairs ? kModePairs : kModeSample;
     c.err = reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlError;

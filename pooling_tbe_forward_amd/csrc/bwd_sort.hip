@@ -123,6 +123,8 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_short_info = take(size_t(N + 1) * 16);
     L.off_short_first = take(size_t(N + 1) * 8);
     L.off_long_info = take(size_t(ml + 1) * 16);
+    L.off_tab_ranges = take(size_t(3) * (p->T + 1) * 4);
+    L.off_chunk_info = take(size_t(mc > 0 ? mc : 1) * 8);
     const size_t acc = p->wdtype == TBE_F32 ? 8 : 4;
     L.off_partials = take(size_t(mc > 0 ? mc : 1) * p->max_D * acc);
     L.total = o;
@@ -694,7 +696,8 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     uint32_t* __restrict__ mode_word, uint32_t max_long, uint32_t* __restrict__ prev_totals,
     uint32_t* __restrict__ unique, uint32_t* __restrict__ run_start,
     uint32_t* __restrict__ run_len, uint32_t* __restrict__ short_ids,
-    uint32_t* __restrict__ long_ids)
+    uint32_t* __restrict__ long_ids, uint32_t* __restrict__ tab_ranges,
+    uint2* __restrict__ chunk_info, uint32_t max_chunks)
 {
     constexpr int NW = kRleThreads / 64;
     constexpr int kTile = kRleThreads * Q;
@@ -816,6 +819,15 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
         const uint32_t R = texcl[0] + s_tot[0];
         counts[1] = R - (texcl[1] + s_tot[1]);
         if (API) run_start[R] = N;
+        // per-table ranges past the last table that has lookups: empty, at
+        // the end of every list
+        const uint32_t klast = keys[N - 1];
+        const int tl = lds_hash ? find_table(s_hash, T, klast) : find_table(hash_off, T, klast);
+        for (int u = tl + 1; u <= T; ++u) {
+            tab_ranges[u] = R - (texcl[1] + s_tot[1]);
+            tab_ranges[(T + 1) + u] = texcl[1] + s_tot[1];
+            tab_ranges[2 * (T + 1) + u] = texcl[2] + s_tot[2];
+        }
         // which payload the sorted entries carry, for the segment kernels'
         // check of what their caller says
         *mode_word = FIRST == 2 ? kModePairs : (FIRST == 1 ? kModeSample : kModeNone);
@@ -834,16 +846,48 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
             run_start[r] = i;
             run_len[r] = len[q];
         }
+        const int t = lds_hash ? find_table(s_hash, T, key) : find_table(hash_off, T, key);
+        // chunks of the long runs before this one
+        const uint32_t cb = texcl[2] + cnt[2][q * NW + wave] + ce[q];
+        // the first run of its table (the previous key is in an earlier
+        // table) starts that table's ranges, and those of the tables without
+        // lookups before it
+        const uint32_t tkey0 = lds_hash ? s_hash[t] : hash_off[t];
+        if (i == 0 || kp[q] < tkey0) {
+            const int tp = i == 0 ? -1
+                         : (lds_hash ? find_table(s_hash, T, kp[q]) : find_table(hash_off, T, kp[q]));
+            for (int u = tp + 1; u <= t; ++u) {
+                tab_ranges[u] = r - lb;
+                tab_ranges[(T + 1) + u] = lb;
+                tab_ranges[2 * (T + 1) + u] = cb;
+            }
+        }
         if (len[q] >= tau) {
-            const uint32_t cb = texcl[2] + cnt[2][q * NW + wave] + ce[q];
             if (lb < max_long) long_info[lb] = make_uint4(key, i, len[q], cb);
             if (API) long_ids[lb] = r;
         } else {
-            const uint32_t t = static_cast<uint32_t>(
-                lds_hash ? find_table(s_hash, T, key) : find_table(hash_off, T, key));
-            short_info[r - lb] = make_uint4(key, i, len[q], t);
+            short_info[r - lb] = make_uint4(key, i, len[q], static_cast<uint32_t>(t));
             if (FIRST) short_first[r - lb] = pay[q];
             if (API) short_ids[r - lb] = r;
+        }
+    }
+    // every chunk's {first sorted position, length}, written by the whole
+    // wavefront run by run (a run of 100K lookups has hundreds of chunks)
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const bool isl = head[q] && len[q] >= tau;
+        uint64_t m = __ballot(isl);
+        if (!m) continue;
+        const uint32_t cb = texcl[2] + cnt[2][q * NW + wave] + ce[q];
+        const uint32_t start = t0 + q * kRleThreads + tid;
+        while (m) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t cbl = __shfl(cb, l), st = __shfl(start, l), ln = __shfl(len[q], l);
+            const uint32_t ncl = (ln + chunk - 1) / chunk;
+            for (uint32_t j = lane; j < ncl; j += 64)
+                if (cbl + j < max_chunks)
+                    chunk_info[cbl + j] = make_uint2(st + j * chunk, min(chunk, ln - j * chunk));
         }
     }
 }
@@ -998,7 +1042,10 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                        reinterpret_cast<uint32_t*>(ws + L.off_run_start),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_len),
                        reinterpret_cast<uint32_t*>(ws + L.off_short),
-                       reinterpret_cast<uint32_t*>(ws + L.off_long));
+                       reinterpret_cast<uint32_t*>(ws + L.off_long),
+                       reinterpret_cast<uint32_t*>(ws + L.off_tab_ranges),
+                       reinterpret_cast<uint2*>(ws + L.off_chunk_info),
+                       static_cast<uint32_t>(L.max_chunks));
     stage_mark(p, 3, a.stream);
     return hipGetLastError();
 }

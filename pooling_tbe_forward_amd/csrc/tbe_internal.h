@@ -123,6 +123,8 @@ struct BwdLayout {
     size_t off_short_info;      // [N] {key, start, len, table}
     size_t off_short_first;     // [N] {sample, per-sample weight bits} of each short run's first lookup
     size_t off_long_info;       // [max_long] {key, start, len, first chunk}
+    size_t off_tab_ranges;      // [3][T+1] per table: first short run, first long run, first chunk
+    size_t off_chunk_info;      // [max_chunks] {first sorted position, length} of each chunk
     size_t off_partials;        // [max_chunks * max_D] (fp64 or fp32)
     size_t total = 0;
 };
