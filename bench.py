@@ -510,15 +510,26 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
+TRAFFIC_TUNING = ("tau", "chunk", "seg_slab_kib")
+
+
+def plan_tuning(plan):
+    t = tbe.tbe_get_tuning(plan)
+    return {k: int(getattr(t, k)) for k in TRAFFIC_TUNING}
+
+
+def measured_traffic(workload, tuning):
     """HBM bytes per k_segment launch from the committed PMC summary of this
-    workload, or None when the kernel source changed since the counters were
-    taken (or there is no summary)."""
+    workload, or None when the kernel source or the launch knobs that shape
+    its work (tuning: plan_tuning of the plan timed) changed since the
+    counters were taken, or there is no summary."""
     try:
         t = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if t.get("source_sha256_16") != source_hash(SEGMENT_SRC):
+        return None
+    if t.get("tuning") != tuning:
         return None
     return t.get("traffic_bytes")
 
@@ -537,7 +548,7 @@ def summarize(r):
     return out
 
 
-def segment_roofline(r, workload):
+def segment_roofline(r, workload, tuning):
     """Roofline entry of the dominant kernel, k_segment: its algorithmic bytes
     per launch over its average launch time from the library's stage events."""
     seg_us = float(np.mean(r["stage_ms"][:, 3])) * 1e3
@@ -545,7 +556,7 @@ def segment_roofline(r, workload):
     seg_gbps = seg_bytes / (seg_us * 1e-6) / 1e9
     return dict(bound="hbm", kernel="k_segment (backward segment-reduce + SGD)",
                 achieved=round(seg_gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                frac=round(seg_gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(workload),
+                frac=round(seg_gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(workload, tuning),
                 avg_launch_us=round(seg_us, 2), bytes_per_launch=int(seg_bytes))
 
 
@@ -557,6 +568,7 @@ def measure(wl, steps, warmup, hip, schedule, extras=True):
     r_graph = run_graph_steps(wl, capture_steps(wl), steps, warmup)
     r_eager = run_plain_steps(wl, steps, warmup)
     r_cold = run_steps(wl, max(5, steps // 2), 2, hip, cold=True)
+    tun = plan_tuning(wl.plan)
     wl.close()
     r = dict(serial=r_serial, overlap=r_over, graph=r_graph, eager=r_eager)[schedule]
     p0 = wl.probs[0]
@@ -569,12 +581,12 @@ def measure(wl, steps, warmup, hip, schedule, extras=True):
                ms_per_step_graph=1e3 * r_graph["wall_s"] / steps,
                ms_per_step_eager=1e3 * r_eager["wall_s"] / steps,
                **summarize(r_serial),
-               roofline=segment_roofline(r_serial, wl.name),
+               roofline=segment_roofline(r_serial, wl.name, tun),
                cold=dict(note="an untimed 1 GiB read before each forward and each backward, "
                               "outside the stage events", fwd_ms=cold["fwd_ms"], bwd_ms=cold["bwd_ms"],
                          fwd_pct_peak=cold["fwd_pct_peak"], bwd_pct_peak=cold["bwd_pct_peak"],
                          bwd_stage_us=cold["bwd_stage_us"],
-                         segment_roofline=segment_roofline(r_cold, wl.name)))
+                         segment_roofline=segment_roofline(r_cold, wl.name, tun)))
     out["overlap_stage_us"] = stage_us(r_over)
     if extras:
         out["adagrad"] = adagrad_summary(wl, steps, warmup, hip)
@@ -647,7 +659,8 @@ def _kernel_avg(rows, pattern, counter):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out, command, workload):
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out, command, workload,
+                  tuning):
     """Per-launch HBM bytes of the library's kernels from FETCH_SIZE /
     WRITE_SIZE (KiB per dispatch), each scaled by the ratio of a 1 GiB copy's
     known bytes to what the same counter reported for it."""
@@ -659,7 +672,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out, com
     w_scale = gib_kib / cw if cw else None
     res = dict(kernel="k_segment", workload=workload, command=command,
                copy_fetch_kib=cf, copy_write_kib=cw, fetch_scale=f_scale, write_scale=w_scale,
-               source_sha256_16=source_hash(SEGMENT_SRC), kernels={})
+               source_sha256_16=source_hash(SEGMENT_SRC), tuning=tuning, kernels={})
     fetch_rows, write_rows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     for name, pat in [("k_segment", r"k_segment"), ("k_fwd_gather", r"k_fwd_gather"),
                       ("k_fwd_hist", r"k_fwd_hist"),
@@ -700,10 +713,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"))
     ap.add_argument("--pmc-workload", default="mixed")
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--pmc-log", default="",
+                    help="stdout of the profiled --quick run (its launch knobs)")
     args = ap.parse_args()
     if args.summarize_pmc:
+        tuning = None
+        if args.pmc_log:
+            for line in open(args.pmc_log):
+                if line.startswith("{") and '"tuning"' in line:
+                    tuning = json.loads(line)["tuning"]
         summarize_pmc(*args.summarize_pmc, traffic_file(args.pmc_workload), args.pmc_command,
-                      args.pmc_workload)
+                      args.pmc_workload, tuning)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this operator's hot path runs on a single "
@@ -732,7 +752,8 @@ def main():
     if args.quick:
         r = run_plain_steps(wl, args.steps, args.warmup)
         print(json.dumps(dict(config=args.config, steps=args.steps,
-                              ms_per_step=1e3 * r["wall_s"] / args.steps)), flush=True)
+                              ms_per_step=1e3 * r["wall_s"] / args.steps,
+                              tuning=plan_tuning(wl.plan))), flush=True)
         return
     m = measure(wl, args.steps, args.warmup, hip, args.schedule)
     probs = wl.probs

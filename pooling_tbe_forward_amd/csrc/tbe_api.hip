@@ -20,7 +20,7 @@ constexpr int64_t kMaxD = 4096;
 tbe_tuning default_tuning()
 {
     tbe_tuning t{};
-    t.tau = 128;              // long-run threshold (runs >= tau are split); measured
+    t.tau = 64;               // long-run threshold (runs >= tau are split); measured
     t.chunk = 256;            // lookups per long-run chunk
     t.hist_mode = 0;          // auto
     t.hist_min_mean_len = 64; // histogram path pays once bags are this long

@@ -54,3 +54,20 @@ def test_weighted_counts():
     # the payload is a (sample, weight) pair: 8 bytes
     assert b["bwd_min"] == jag + 24 + 2 * 32 + 6 * 12 * 2 + 5 * 16
     assert b["seg_min"] == 2 * 32 + 24 + 6 * 8 + 5 * 16
+
+
+def test_traffic_keyed_to_source_and_tuning(tmp_path, monkeypatch):
+    """A committed PMC summary counts only for the kernel source and the
+    launch knobs it was taken with."""
+    tun = dict(tau=64, chunk=256, seg_slab_kib=1024)
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda w: str(path))
+    rec = dict(source_sha256_16=bench.source_hash(bench.SEGMENT_SRC), tuning=tun,
+               traffic_bytes=12345)
+    path.write_text(json.dumps(rec))
+    assert bench.measured_traffic("mixed", tun) == 12345
+    assert bench.measured_traffic("mixed", dict(tun, tau=128)) is None
+    path.write_text(json.dumps(dict(rec, source_sha256_16="0" * 16)))
+    assert bench.measured_traffic("mixed", tun) is None
+    path.write_text(json.dumps({k: v for k, v in rec.items() if k != "tuning"}))
+    assert bench.measured_traffic("mixed", tun) is None
