@@ -474,7 +474,7 @@ def cpu_baseline(config="mixed", budget_s=20.0, samples=256):
             oracle.forward(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
                            prob.offsets, prob.psw, prob.weighted)
             t1 = time.perf_counter()
-            r = oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, 128)
+            r = oracle.sort_rle(prob.T, prob.B, prob.rows, prob.indices, prob.offsets, 64)
             t2 = time.perf_counter()
             oracle.backward_sgd(prob.T, prob.B, prob.rows, prob.dims, code, tabs, prob.indices,
                                 prob.offsets, prob.psw, prob.weighted, prob.grad, prob.lr,
@@ -514,6 +514,7 @@ TRAFFIC_TUNING = ("tau", "chunk", "seg_slab_kib")
 
 
 def plan_tuning(plan):
+    from pooling_tbe_forward_amd import tbe
     t = tbe.tbe_get_tuning(plan)
     return {k: int(getattr(t, k)) for k in TRAFFIC_TUNING}
 

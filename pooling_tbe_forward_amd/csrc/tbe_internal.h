@@ -32,7 +32,7 @@ static_assert(sizeof(TableDesc) == 32, "descriptor layout");
 // Histogram path limits: table rows (the contraction depth) and width.
 constexpr int kHistMaxRows = 256;
 constexpr int kHistMaxD = 256;
-constexpr int kHistBags = 32;        // bags per MFMA tile (M)
+constexpr int kHistBags = 16;        // bags per workgroup = M of the MFMA tile
 constexpr int kHistWindow = 2048;    // ids counted per window: counts stay exact in fp16
 
 }  // namespace tbe
