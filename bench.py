@@ -507,7 +507,14 @@ def cpu_baseline(config="mixed", budget_s=20.0, samples=256):
 
 
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 prefix of a source file's code: comments and blank lines are
+    dropped first, so an edit of the comments keeps counters taken on the
+    same code valid."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 TRAFFIC_TUNING = ("tau", "chunk", "seg_slab_kib")

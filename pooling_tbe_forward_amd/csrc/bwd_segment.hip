@@ -12,19 +12,26 @@
 // speed is latency hiding -- how many independent row loads are in flight.
 //
 // gfx950 design:
-//  * a gradient row of D fp32 elements is covered by L lanes (VEC elements,
+//  * work is cut into items, one column block of one table (cw columns, so
+//    the table's grad_output slab B x cw x 4 bytes stays in one XCD's L2),
+//    dealt to the eight XCDs in a fixed order; one persistent launch, whose
+//    waves walk their XCD's items (see k_segment below);
+//  * a column block of a gradient row is covered by L lanes (VEC elements,
 //    up to 16-byte loads); a 64-lane wavefront holds G = 64/L workers;
 //  * short runs: each worker owns S runs at once.  It issues their weight-row
 //    loads up front, then walks their contributions as one flat sequence:
 //    L sample ids at once, U gradient rows in flight across run boundaries,
-//    so a run of one lookup costs one dependent step, not one each;
-//  * long runs: the same launch carries chunk workers (a block per chunk of
-//    `chunk` lookups, or a wavefront for rows of 64 lanes) that write partial
-//    sums; the next launch (a block per long run) adds each run's partials in
-//    a fixed order and applies the update, so the result does not depend on
-//    scheduling.  (Combining in the same launch, last arrival wins, needs a
-//    device-scope release per chunk, which on gfx950 writes back and
-//    invalidates the whole L2 -- far dearer than one more launch);
+//    so a run of one lookup costs one dependent step, not one each.  The
+//    next unit's run records and sample ids are fetched while the current
+//    unit is summed, and its updated rows are stored after those loads;
+//  * long runs: an item's units also include its long runs' chunks (`chunk`
+//    lookups each; a wave's workers split a chunk and are folded in a fixed
+//    order) whose partial sums go to the workspace; the next launch (a block
+//    per long run) adds each run's partials in a fixed order and applies the
+//    update, so the result does not depend on scheduling.  (Combining in the
+//    same launch, last arrival wins, needs a device-scope release per chunk,
+//    which on gfx950 writes back and invalidates the whole L2 -- far dearer
+//    than one more launch);
 //  * weight rows are read and written with streaming (non-temporal) hints;
 //  * accumulation is fp64 for fp32 tables (long Zipf runs would otherwise
 //    drift past 1e-5 relative) and fp32 for fp16 tables; w - lr*g is rounded
@@ -33,7 +40,8 @@
 //    row's mean squared gradient, step lr / (sqrt(state) + eps)): the row's
 //    sum of squares is reduced across the worker's lanes with lane swaps, so
 //    a row must fit one worker (D <= 64 * VEC); one lane stores the state;
-//  * work counts are read from device memory; grids are persistent loops.
+//  * work counts and per-table run ranges are read from device memory (the
+//    run-length encode writes them); nothing goes back to the host.
 #include "tbe_internal.h"
 
 namespace tbe {

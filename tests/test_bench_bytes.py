@@ -71,3 +71,14 @@ def test_traffic_keyed_to_source_and_tuning(tmp_path, monkeypatch):
     assert bench.measured_traffic("mixed", tun) is None
     path.write_text(json.dumps({k: v for k, v in rec.items() if k != "tuning"}))
     assert bench.measured_traffic("mixed", tun) is None
+
+
+def test_source_hash_ignores_comments(tmp_path):
+    a = tmp_path / "a.hip"
+    a.write_text("// header\nint f(int x) { return x + 1; }  // inline\n\n/* block\n */\n")
+    b = tmp_path / "b.hip"
+    b.write_text("// other words\n\nint f(int x) { return x + 1; }\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_hash(str(a)) == bench.source_hash(str(b))
+    assert bench.source_hash(str(a)) != bench.source_hash(str(c))
