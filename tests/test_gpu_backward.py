@@ -90,10 +90,10 @@ def test_sort_rle_vs_oracle(name, B, seed, tau):
 
 
 @pytest.mark.parametrize("name", ["uniform", "stress", "mixed", "band"])
-@pytest.mark.parametrize("tau", [128, 256])
+@pytest.mark.parametrize("tau", [64, 128, 256])
 def test_sort_rle_full_size(name, tau):
-    """All keys at full size, at the plan's default threshold (128) and the
-    pages' 256."""
+    """All keys at full size, at the plan's default threshold (64), the
+    previous default (128) and the pages' 256."""
     prob = dg.make_problem(name)
     g = gpu_sort(prob, tau=tau)
     o = H.oracle_sort(prob, tau)

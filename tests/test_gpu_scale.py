@@ -33,8 +33,8 @@ def test_production_scale_forward_sort_backward():
     assert rep["ok"], rep
     del out
 
-    o = H.oracle_sort(prob, 128)
-    _compare_sort(gpu_sort(prob, tau=128), o, prob.N)
+    o = H.oracle_sort(prob, 64)
+    _compare_sort(gpu_sort(prob, tau=64), o, prob.N)
     del o
 
     gpu_backward(prob, w_dev)
