@@ -144,12 +144,12 @@ size_t tbe_backward_workspace_bytes(const tbe_plan* plan, int32_t B, int64_t num
 
 /*
  * Prepare a backward workspace before its first use (enqueued on `stream`).
- * The first 32832 bytes of a workspace are a control block (tile tickets and
+ * The first 65600 bytes of a workspace are a control block (tile tickets and
  * digit totals of the sort, counts, an error word) that must be zero when a
  * call starts; every tbe_backward_sgd / tbe_sort_rle call leaves it zero
  * again, so one init per allocation is enough, whatever plan, B or
  * num_indices later calls use.  A zero-filled allocation is also initialised.
- * Errors: TBE_EINVAL (NULL, not 256-byte aligned, fewer than 32832 bytes),
+ * Errors: TBE_EINVAL (NULL, not 256-byte aligned, fewer than 65600 bytes),
  * TBE_EHIP.
  */
 tbe_status tbe_workspace_init(void* workspace, size_t workspace_bytes, void* stream);

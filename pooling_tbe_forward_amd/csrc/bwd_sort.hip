@@ -40,6 +40,10 @@ namespace tbe {
 
 namespace {
 constexpr int kRadix = 256;
+// Digits are at most this wide: keys of 25-27 bits take three 9-bit passes
+// instead of four of 7 or fewer, and 17-18 bits two instead of three.
+constexpr int kMaxDigitBits = 9;
+static_assert((1 << kMaxDigitBits) <= kRadixMax, "digit totals hold the widest digit");
 constexpr int kSortThreads = 1024;   // 16 waves per radix tile
 constexpr int kRleThreads = 1024;
 constexpr int kRleItems = 8;         // sorted positions per thread (two 16-byte loads)
@@ -73,7 +77,7 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     int bits = 0;
     while (bits < 32 && (uint64_t(1) << bits) < uint64_t(p->sum_rows)) ++bits;
     L.nbits = bits;
-    L.npasses = bits == 0 ? 1 : (bits + 7) / 8;
+    L.npasses = bits == 0 ? 1 : (bits + kMaxDigitBits - 1) / kMaxDigitBits;
     const int per = bits == 0 ? 1 : (bits + L.npasses - 1) / L.npasses;
     int left = bits == 0 ? 1 : bits;
     for (int i = 0; i < L.npasses; ++i) {
@@ -111,7 +115,7 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_keys[1] = take(n4);
     L.off_vals[0] = take(2 * n4);   // payload: 4 bytes, or 8 with per-sample weights
     L.off_vals[1] = take(2 * n4);
-    L.off_status = take(size_t(L.npasses) * kRadix * (L.sort_blocks > 0 ? L.sort_blocks : 1) * 4);
+    L.off_status = take(size_t(L.npasses) * kRadixMax * (L.sort_blocks > 0 ? L.sort_blocks : 1) * 4);
     L.off_rle_status = take(size_t(3) * (L.rle_blocks > 0 ? L.rle_blocks : 1) * 4);
     L.status_words = (L.off_rle_status - L.off_status) / 4 +
                      size_t(3) * (L.rle_blocks > 0 ? L.rle_blocks : 1);
@@ -258,12 +262,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     uint32_t* __restrict__ totals, PassBits pb, uint32_t* __restrict__ status,
     size_t status_words)
 {
-    __shared__ uint32_t hist[4][kRadix];
+    __shared__ uint32_t hist[4][kRadixMax];
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
     __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
     __shared__ uint32_t hwt[MODE == kPayloadMean ? kPrepMaxBags + 1 : 1];   // tables' weighted flag
     const int tid = threadIdx.x;
-    for (int i = tid; i < 4 * kRadix; i += kPrepThreads) (&hist[0][0])[i] = 0u;
+    for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) (&hist[0][0])[i] = 0u;
     const uint32_t g0 = blockIdx.x * bags_per_block;
     const uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
     const uint32_t t_first = nb ? g0 / B : 0;
@@ -356,10 +360,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     }
     __syncthreads();
     // digit totals are spread over kTotCopies copies (fewer adds per address)
-    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadix);
-    for (int i = tid; i < 4 * kRadix; i += kPrepThreads) {
-        const int q = i >> 8;
-        const uint32_t c = hist[q][i & (kRadix - 1)];
+    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadixMax);
+    for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) {
+        const int q = i / kRadixMax;
+        const uint32_t c = hist[q][i % kRadixMax];
         if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
     }
     // the look-back words of the radix passes and the run-length encode
@@ -387,12 +391,16 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     uint32_t* __restrict__ prev_totals)
 {
     constexpr int NW = kSortThreads / 64;
-    __shared__ uint32_t wcnt[NW][kRadix];
-    __shared__ uint32_t part[4][kRadix];
-    __shared__ uint32_t gofs[kRadix];
-    __shared__ uint32_t lbase[kRadix];
-    __shared__ uint32_t delta[kRadix];
-    __shared__ uint32_t wsum[4];
+    constexpr int RX = NB > 8 ? 512 : 256;   // digit counters
+    constexpr int NQ = kSortThreads / RX;    // thread groups covering every digit
+    static_assert(!LOWLDS || NB <= 8, "the low-LDS tile stages digits as bytes");
+    static_assert(RX <= kRadixMax && NW % NQ == 0, "digit layout");
+    __shared__ uint32_t wcnt[NW][RX];
+    __shared__ uint32_t part[NQ][RX];
+    __shared__ uint32_t gofs[RX];
+    __shared__ uint32_t lbase[RX];
+    __shared__ uint32_t delta[RX];
+    __shared__ uint32_t wsum[RX / 64];
     __shared__ uint32_t s_tile;
     __shared__ uint32_t sk[kSortThreads * R];
     __shared__ PT sv[LOWLDS ? 1 : kSortThreads * R];
@@ -401,24 +409,24 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     // the ticket is taken by a wave that loads no totals, so the two overlap
-    if (tid == kRadix) s_tile = take_ticket(ticket, ntiles);
+    if (tid == RX) s_tile = take_ticket(ticket, ntiles);
     uint32_t tot = 0;
-    if (tid < kRadix) {
+    if (tid < RX) {
 #pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) tot += totals[cp * 4 * kRadix + tid];
+        for (int cp = 0; cp < kTotCopies; ++cp) tot += totals[cp * 4 * kRadixMax + tid];
     }
     // the previous pass's digit totals are no longer needed: leave them zero
-    if (blockIdx.x == 0 && prev_totals && tid < kRadix)
+    if (blockIdx.x == 0 && prev_totals && tid < kRadixMax)
 #pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
-    for (int i = tid; i < NW * kRadix; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
+        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadixMax + tid] = 0u;
+    for (int i = tid; i < NW * RX; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
     uint32_t inc = 0;
-    if (tid < kRadix) {
+    if (tid < RX) {
         inc = wave_incl_scan(tot, lane);
         if (lane == 63) wsum[wave] = inc;
     }
     __syncthreads();
-    if (tid < kRadix) {
+    if (tid < RX) {
         uint32_t pre = 0;
         for (int w = 0; w < wave; ++w) pre += wsum[w];
         gofs[tid] = pre + inc - tot;   // first output position of digit tid
@@ -469,12 +477,12 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
         rk[r] = base + below;
     }
     __syncthreads();
-    // per digit: exclusive prefix over the waves (four groups of NW/4 waves),
+    // per digit: exclusive prefix over the waves (NQ groups of NW/NQ waves),
     // the tile's digit total, and its exclusive prefix over digits (lbase)
-    const int d = tid & (kRadix - 1), q = tid >> 8;
+    const int d = tid & (RX - 1), q = tid / RX;
     uint32_t all = 0, dinc = 0;
     {
-        constexpr int G = NW / 4;
+        constexpr int G = NW / NQ;
         uint32_t run = 0;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -490,7 +498,8 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 #pragma unroll
             for (int j = 0; j < G; ++j) wcnt[q * G + j][d] += pre;
         if (q == 0) {
-            all = part[0][d] + part[1][d] + part[2][d] + part[3][d];
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) all += part[j][d];
             dinc = wave_incl_scan(all, lane);
             if (lane == 63) wsum[wave] = dinc;
         }
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
                 sv[lp] = v[r];
         }
     }
-    if (q == 0) delta[d] = gofs[d] + lookback<16>(status + d, kRadix, tile, all, err) - lb;
+    if (q == 0) delta[d] = gofs[d] + lookback<16>(status + d, RX, tile, all, err) - lb;
     __syncthreads();
     // write out: consecutive threads store consecutive positions of a digit
     const uint32_t t0 = tile * (uint32_t(kSortThreads) * R);
@@ -712,9 +721,9 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     const int wave = tid >> 6;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (tid == 0) s_tile = take_ticket(ticket, ntiles);
-    if (blockIdx.x == 0 && prev_totals && tid < kRadix)   // the last radix pass is done with them
+    if (blockIdx.x == 0 && prev_totals && tid < kRadixMax)   // the last radix pass is done with them
 #pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadix + tid] = 0u;
+        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadixMax + tid] = 0u;
     const bool lds_hash = T <= kRleMaxT;
     if (lds_hash)
         for (int i = tid; i <= T; i += kRleThreads) s_hash[i] = hash_off[i];
@@ -898,19 +907,23 @@ void launch_onesweep(BwdArgs& a, uint32_t nb, const uint32_t* keys_in, const PT*
                      uint32_t* ctl, uint32_t* status)
 {
     hipLaunchKernelGGL((k_onesweep<R, PT, NB, LOWLDS>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys_in,
-                       vals_in, keys_out, vals_out, N, shift, ctl + kCtlTotals + pass * kRadix,
-                       status + static_cast<size_t>(pass) * kRadix * nb,
+                       vals_in, keys_out, vals_out, N, shift, ctl + kCtlTotals + pass * kRadixMax,
+                       status + static_cast<size_t>(pass) * kRadixMax * nb,
                        ctl + kCtlTicket + pass, ctl + kCtlError, nb,
-                       pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadix : nullptr);
+                       pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadixMax : nullptr);
 }
 
+// The low-LDS tile stages digits as bytes, so a 9-bit pass takes the
+// full-LDS tile whatever the tile count.
 template <int R, typename PT, bool LOWLDS>
 auto pick_onesweep(int nbits)
 {
-    return nbits <= 1 ? launch_onesweep<R, PT, 1, LOWLDS> : nbits == 2 ? launch_onesweep<R, PT, 2, LOWLDS>
+    auto f = nbits <= 1 ? launch_onesweep<R, PT, 1, LOWLDS> : nbits == 2 ? launch_onesweep<R, PT, 2, LOWLDS>
          : nbits == 3 ? launch_onesweep<R, PT, 3, LOWLDS> : nbits == 4 ? launch_onesweep<R, PT, 4, LOWLDS>
          : nbits == 5 ? launch_onesweep<R, PT, 5, LOWLDS> : nbits == 6 ? launch_onesweep<R, PT, 6, LOWLDS>
          : nbits == 7 ? launch_onesweep<R, PT, 7, LOWLDS> : launch_onesweep<R, PT, 8, LOWLDS>;
+    if (nbits >= 9) f = launch_onesweep<R, PT, 9, false>;
+    return f;
 }
 
 // Passes of many tiles (more than four per CU of an MI355X) with a 4-byte
@@ -1037,7 +1050,7 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                        reinterpret_cast<uint4*>(ws + L.off_short_info),
                        reinterpret_cast<uint4*>(ws + L.off_long_info), ctl + kCtlCounts,
                        ctl + kCtlMode, static_cast<uint32_t>(L.max_long),
-                       ctl + kCtlTotals + (L.npasses - 1) * kRadix,
+                       ctl + kCtlTotals + (L.npasses - 1) * kRadixMax,
                        reinterpret_cast<uint32_t*>(ws + L.off_unique),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_start),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_len),

@@ -97,8 +97,9 @@ constexpr uint32_t kModeNone = 0u;        // none yet, or tbe_sort_rle's lookup 
 constexpr uint32_t kModeSample = 1u;      // sample ids
 constexpr uint32_t kModePairs = 2u;       // (sample id, weight) pairs
 constexpr int kTotCopies = 8;      // digit totals are kept in this many copies
-constexpr int kCtlTotals = 16;     // [kTotCopies][4][256] digit totals of every radix pass
-constexpr int kCtlWords = 16 + kTotCopies * 4 * 256;
+constexpr int kRadixMax = 512;     // digit counters of the widest radix pass (9-bit digits)
+constexpr int kCtlTotals = 16;     // [kTotCopies][4][kRadixMax] digit totals of every radix pass
+constexpr int kCtlWords = 16 + kTotCopies * 4 * kRadixMax;
 
 // Workspace carve-up (byte offsets), computed on the host.
 struct BwdLayout {
