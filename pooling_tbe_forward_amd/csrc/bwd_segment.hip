@@ -52,14 +52,34 @@ struct alignas(sizeof(T) * N) Pack {
     T v[N];
 };
 
+template <int BYTES>
+struct RawVec;
+template <> struct RawVec<32> { typedef uint32_t T __attribute__((ext_vector_type(8))); };
+template <> struct RawVec<16> { typedef uint32_t T __attribute__((ext_vector_type(4))); };
+template <> struct RawVec<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <> struct RawVec<4> { typedef uint32_t T; };
+template <> struct RawVec<2> { typedef uint16_t T; };
+
 // Load through a global-address-space pointer: the pointers here come out of
 // a by-value argument struct, where the compiler would otherwise emit flat
-// loads (which also count against the LDS counter).
+// loads (which also count against the LDS counter, so every wait for an LDS
+// or lane-shuffle result would also wait for them).  A struct (a Pack, a
+// HIP vector type) is loaded as a plain vector and copied: a struct copied
+// straight out of the cast pointer is rewritten into element loads through
+// the original, generic pointer, and so compiles to flat loads again.
 template <typename T>
 __device__ __forceinline__ T ldg(const T* p)
 {
 #if __HIP_DEVICE_COMPILE__
-    return *(const __attribute__((address_space(1))) T*)(p);
+    if constexpr (__is_class(T)) {
+        typedef typename RawVec<sizeof(T)>::T R;
+        const R x = *(const __attribute__((address_space(1))) R*)(p);
+        T r;
+        __builtin_memcpy(&r, &x, sizeof(T));
+        return r;
+    } else {
+        return *(const __attribute__((address_space(1))) T*)(p);
+    }
 #else
     return *p;   // host pass: never executed
 #endif
@@ -72,12 +92,6 @@ __device__ __forceinline__ T ldg(const T* p)
 // kernel to write back (measured on the uniform step: segment kernel 84 -> 71
 // us, and the forward that follows it 48 -> 38 us).  P is a Pack of 2, 4, 8
 // or 16 bytes.
-template <int BYTES>
-struct RawVec;
-template <> struct RawVec<16> { typedef uint32_t T __attribute__((ext_vector_type(4))); };
-template <> struct RawVec<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
-template <> struct RawVec<4> { typedef uint32_t T; };
-template <> struct RawVec<2> { typedef uint16_t T; };
 
 template <typename P>
 __device__ __forceinline__ P ldg_stream(const P* p)

@@ -137,6 +137,28 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
 
 namespace {
 
+// Load through a global-address-space pointer (a pointer cast from void*
+// otherwise compiles to a flat load, which also counts against the LDS
+// counter); a HIP vector type is loaded as a plain vector and copied.
+template <typename T>
+__device__ __forceinline__ T gload(const T* p)
+{
+#if __HIP_DEVICE_COMPILE__
+    if constexpr (sizeof(T) == 8 && __is_class(T)) {
+        typedef uint32_t V __attribute__((ext_vector_type(2)));
+        const V x = *(const __attribute__((address_space(1))) V*)(p);
+        T r;
+        __builtin_memcpy(&r, &x, sizeof(T));
+        return r;
+    } else {
+        static_assert(!__is_class(T), "scalars and 8-byte vector types only");
+        return *(const __attribute__((address_space(1))) T*)(p);
+    }
+#else
+    return *p;   // host pass: never executed
+#endif
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
 #pragma unroll
@@ -645,12 +667,16 @@ __device__ __forceinline__ uint32_t scan_table(uint32_t* tab, int lane)
     return __shfl(inc, 63);
 }
 
+// GLOBAL: hash_off is in global memory (loaded as such, so the compiler cannot
+// merge the LDS and global searches into one flat-load search).
+template <bool GLOBAL>
 __device__ __forceinline__ int find_table(const uint32_t* hash_off, int T, uint32_t key)
 {
     int lo = 0, hi = T;  // hash_off[lo] <= key < hash_off[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (hash_off[mid] <= key) lo = mid; else hi = mid;
+        const uint32_t h = GLOBAL ? gload(hash_off + mid) : hash_off[mid];
+        if (h <= key) lo = mid; else hi = mid;
     }
     return lo;
 }
@@ -748,8 +774,8 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
         kk[q] = keys[pc];
         kp[q] = keys[pc > 0 ? pc - 1 : 0];
         pay[q] = make_uint2(0u, 0x3f800000u);   // weight 1.0 unless the payload has one
-        if (FIRST == 1) pay[q].x = static_cast<const uint32_t*>(payload)[pc];
-        if (FIRST == 2) pay[q] = static_cast<const uint2*>(payload)[pc];
+        if (FIRST == 1) pay[q].x = gload(static_cast<const uint32_t*>(payload) + pc);
+        if (FIRST == 2) pay[q] = gload(static_cast<const uint2*>(payload) + pc);
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -831,7 +857,7 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
         // per-table ranges past the last table that has lookups: empty, at
         // the end of every list
         const uint32_t klast = keys[N - 1];
-        const int tl = lds_hash ? find_table(s_hash, T, klast) : find_table(hash_off, T, klast);
+        const int tl = lds_hash ? find_table<false>(s_hash, T, klast) : find_table<true>(hash_off, T, klast);
         for (int u = tl + 1; u <= T; ++u) {
             tab_ranges[u] = R - (texcl[1] + s_tot[1]);
             tab_ranges[(T + 1) + u] = texcl[1] + s_tot[1];
@@ -855,16 +881,16 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
             run_start[r] = i;
             run_len[r] = len[q];
         }
-        const int t = lds_hash ? find_table(s_hash, T, key) : find_table(hash_off, T, key);
+        const int t = lds_hash ? find_table<false>(s_hash, T, key) : find_table<true>(hash_off, T, key);
         // chunks of the long runs before this one
         const uint32_t cb = texcl[2] + cnt[2][q * NW + wave] + ce[q];
         // the first run of its table (the previous key is in an earlier
         // table) starts that table's ranges, and those of the tables without
         // lookups before it
-        const uint32_t tkey0 = lds_hash ? s_hash[t] : hash_off[t];
+        const uint32_t tkey0 = lds_hash ? s_hash[t] : gload(hash_off + t);
         if (i == 0 || kp[q] < tkey0) {
             const int tp = i == 0 ? -1
-                         : (lds_hash ? find_table(s_hash, T, kp[q]) : find_table(hash_off, T, kp[q]));
+                         : (lds_hash ? find_table<false>(s_hash, T, kp[q]) : find_table<true>(hash_off, T, kp[q]));
             for (int u = tp + 1; u <= t; ++u) {
                 tab_ranges[u] = r - lb;
                 tab_ranges[(T + 1) + u] = lb;
