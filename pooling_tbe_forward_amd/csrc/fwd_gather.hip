@@ -63,10 +63,13 @@ __device__ __forceinline__ int64_t lane_bcast(IT v, int src) {
     return static_cast<int64_t>(__shfl(v, src));
 }
 
-// Issue the U row loads of one round: slot grp of row r0 + u*G + grp.  Rows
-// past the bag's end (or lanes past D) read the table's first row and are
-// masked out when summed, so every load is unconditional and all U stay in
-// flight.
+// Issue the U row loads of one round: slot grp of row r0 + u*G + grp.  Slots
+// past the end of the 64-id chunk read the chunk's last row again, and lanes
+// past D read column 0 of their slot's row; both are masked out when summed,
+// so every load is unconditional and all U stay in flight.  A repeated row is
+// one this wave fetches anyway, so these loads add no new lines (pointing
+// them at the table's first row sent about 30% of the mixed workload's row
+// requests to the same few L2 lines; the time did not change measurably).
 template <typename WT, typename IT, int VEC, int U>
 __device__ __forceinline__ void issue_round(Pack<WT, VEC> (&v)[U], float (&w)[U], bool (&on)[U],
                                             const WT* tcol, int D, IT my_id,
@@ -77,9 +80,9 @@ __device__ __forceinline__ void issue_round(Pack<WT, VEC> (&v)[U], float (&w)[U]
     for (int u = 0; u < U; ++u) {
         const int r = r0 + (u << g_log2) + grp;
         on[u] = r < n && active;
-        const int64_t id = lane_bcast(my_id, r & 63);
-        const int64_t row = on[u] ? id : 0;
-        w[u] = tw ? __shfl(my_w, r & 63) : 1.f;
+        const int src = r < n ? r : n - 1;  // n >= 1 inside a chunk
+        const int64_t row = lane_bcast(my_id, src);
+        w[u] = tw ? __shfl(my_w, src) : 1.f;
         v[u] = *reinterpret_cast<const Pack<WT, VEC>*>(tcol + row * D);
     }
 }
@@ -109,15 +112,14 @@ __device__ __forceinline__ void sum_round(float (&acc)[VEC], const Pack<WT, VEC>
 }
 
 template <typename WT, typename IT, int VEC, int U, bool WEIGHTED>
-__global__ __launch_bounds__(256) void k_fwd_gather(
+__global__ __launch_bounds__(64) void k_fwd_gather(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, int32_t sumD,
     const WT* weights, const IT* __restrict__ indices,
     const IT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
     uint32_t bags_per_wave, int32_t hist_active, int32_t mean)
 {
     const int lane = threadIdx.x & 63;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) +
-                                                         (threadIdx.x >> 6));
+    const uint32_t wave = blockIdx.x;  // one wave per workgroup
     const uint32_t g0 = wave * bags_per_wave;
     if (g0 >= total_bags) return;
     const uint32_t g1 = min(g0 + bags_per_wave, total_bags);
@@ -125,12 +127,21 @@ __global__ __launch_bounds__(256) void k_fwd_gather(
     for (uint32_t g = g0; g < g1; ++g) {
         const uint32_t t = g / B;
         const uint32_t b = g - t * B;
+        const IT s_raw = offsets[g];
+        const IT e_raw = offsets[g + 1];
         const TableDesc d = tables[t];
+        // the bag's bounds do not depend on its table's record: every field
+        // used below is consumed here, before any branch or conversion, so the
+        // wave waits once for both (the compiler would otherwise sink each
+        // load to the block that uses it, making the chain record -> bounds ->
+        // ids -> rows)
+        asm volatile("" ::"s"(s_raw), "s"(e_raw), "s"(d.w_off), "s"(d.D), "s"(d.out_off),
+                     "s"(d.flags));
+        const int64_t s = static_cast<int64_t>(s_raw);
+        const int64_t e = static_cast<int64_t>(e_raw);
         if (hist_active && (d.flags & TD_HIST_OK) && !(WEIGHTED && (d.flags & TD_WEIGHTED)))
             continue;  // pooled by the histogram kernel
         const bool tw = WEIGHTED && (d.flags & TD_WEIGHTED);
-        const int64_t s = static_cast<int64_t>(offsets[g]);
-        const int64_t e = static_cast<int64_t>(offsets[g + 1]);
         const int D = d.D;
         const int lanes = D / VEC;
         const int lpr_log2 = lanes >= 64 ? 6 : (lanes <= 1 ? 0 : 32 - __builtin_clz(lanes - 1));
@@ -174,8 +185,8 @@ __global__ __launch_bounds__(256) void k_fwd_gather(
                 issue_round<WT, IT, VEC, U>(va, wa, oa, tcol, D, my_id, my_w, 0, n, g_log2, grp,
                                             active, tw);
                 issue_fence();
-                // the next round is always issued (past the end it reads row 0,
-                // masked): a load under a branch would make the compiler wait
+                // the next round is always issued (past the end it re-reads a
+                // row, masked): a load under a branch would make the compiler wait
                 // for every outstanding load where the branches meet
                 // (issue_fence keeps the compiler from moving a round's loads down
                 // to their use, or a sum above the next round's loads, which
@@ -216,7 +227,12 @@ hipError_t launch_vec(const FwdArgs& a)
     const uint32_t total = static_cast<uint32_t>(p->T) * static_cast<uint32_t>(a.B);
     const uint32_t bpw = static_cast<uint32_t>(max(1, p->tuning.fwd_bags_per_wave));
     const uint32_t waves = (total + bpw - 1) / bpw;
-    const uint32_t blocks = (waves + 3) / 4;
+    // one-wave workgroups: the waves of a workgroup are placed one per SIMD of
+    // a CU, so a four-wave workgroup waits for a free slot on all four SIMDs
+    // at once, and with bags of unequal length that left about 5,300 of the
+    // chip's 8,192 wave slots busy (mixed workload; about 7,250 with one-wave
+    // workgroups, forward 236 -> 211 us)
+    const uint32_t blocks = waves;
     if (blocks == 0) return hipSuccess;
     // rows per lane per round (2U in flight with the double buffer): 2 with
     // 16-byte loads, 8 with narrower ones.  The kernel is bound by how many
@@ -225,7 +241,7 @@ hipError_t launch_vec(const FwdArgs& a)
     // workload with hot rows (mixed forward 280 -> 235 us, stress 58 -> 52,
     // band 57 -> 50; uniform unchanged; U = 1 was slower on stress).
     constexpr int U = (VEC * sizeof(WT) >= 16) ? 2 : 8;
-    const dim3 grid(blocks), block(256);
+    const dim3 grid(blocks), block(64);
     const auto* w = static_cast<const WT*>(a.weights);
     const auto* ix = static_cast<const IT*>(a.indices);
     const auto* of = static_cast<const IT*>(a.offsets);
