@@ -716,24 +716,36 @@ uint32_t blocks_for(int64_t work_items, int64_t per_block, int64_t cap)
     return static_cast<uint32_t>(b);
 }
 
-// Resident blocks of a 256-thread kernel on the whole device (all XCDs), a
-// multiple of 8 so every XCD gets the same number of persistent blocks; one
-// cached value per kernel (the devices a process uses are alike).
+// Persistent blocks of a 256-thread kernel on the whole device (all XCDs): as
+// many as are resident, at most max_per_cu per CU, a multiple of 8 so every
+// XCD gets the same number.  The occupancy query is cached per kernel (the
+// devices a process uses are alike).
 template <auto Kernel>
-uint32_t persistent_blocks()
+uint32_t persistent_blocks(int max_per_cu)
 {
-    static int cached = 0;
-    if (!cached) {
-        int dev = 0, cus = 0, per = 0;
+    static int cus = 0, per = 0;
+    if (!per) {
+        int dev = 0, c = 0, r = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, Kernel, 256, 0) != hipSuccess ||
-            cus <= 0 || per <= 0)
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, Kernel, 256, 0) != hipSuccess ||
+            c <= 0 || r <= 0)
             return 2048;
-        cached = ((cus * per + 7) / 8) * 8;
+        cus = c;
+        per = r;
     }
-    return static_cast<uint32_t>(cached);
+    const int b = cus * (per < max_per_cu ? per : max_per_cu);
+    return static_cast<uint32_t>(((b + 7) / 8) * 8);
 }
+
+// Blocks per CU when a column block's grad_output slab (B x cw x 4 bytes) is
+// larger than an XCD's 4 MB L2, so the waves' gradient reads miss whatever
+// their number: then fewer waves are faster.  Measured on the production-scale
+// workload (33.5 MB slabs; segment kernel, ms, by waves per SIMD): 6: 6.40,
+// 5: 5.93, 4: 5.60-5.67, 3: 5.50, 2: 5.68.  Slabs that fit keep every resident
+// wave (the small-table workload's 4 MB slabs: 6: 88 us, 5: 92, 4: 97).
+constexpr int kBigSlabBlocksPerCu = 3;
+constexpr int64_t kXcdL2Bytes = int64_t(4) << 20;
 
 template <typename WT, typename ACC, int VEC, int OPT>
 hipError_t launch_all(const BwdArgs& a, SegArgs c)
@@ -747,14 +759,16 @@ hipError_t launch_all(const BwdArgs& a, SegArgs c)
     const uint32_t b_long = blocks_for(L.max_long, 1, 4096);
     // short-run units: S = 2 runs per worker, U = 4 gradient rows in flight
     constexpr int S = 2, U = 4;
+    const int max_per_cu =
+        int64_t(a.B) * c.cw * 4 > kXcdL2Bytes ? kBigSlabBlocksPerCu : 1 << 30;
     if (a.payload_pairs) {
         constexpr auto k = k_segment<WT, ACC, VEC, S, U, true, OPT>;
-        hipLaunchKernelGGL(k, dim3(persistent_blocks<k>()), dim3(256), 0, a.stream, c, w,
-                           partials);
+        hipLaunchKernelGGL(k, dim3(persistent_blocks<k>(max_per_cu)), dim3(256), 0, a.stream, c,
+                           w, partials);
     } else {
         constexpr auto k = k_segment<WT, ACC, VEC, S, U, false, OPT>;
-        hipLaunchKernelGGL(k, dim3(persistent_blocks<k>()), dim3(256), 0, a.stream, c, w,
-                           partials);
+        hipLaunchKernelGGL(k, dim3(persistent_blocks<k>(max_per_cu)), dim3(256), 0, a.stream, c,
+                           w, partials);
     }
     stage_mark(a.plan, 4, a.stream);
     hipLaunchKernelGGL((k_long_combine<WT, ACC, VEC, OPT>), dim3(b_long), dim3(256), 0, a.stream,
