@@ -319,9 +319,9 @@ tbe_status tbe_set_tuning(tbe_plan* plan, const tbe_tuning* tuning);
  * (per-sample-weighted) sum of the bag's rows.  TBE_POOL_MEAN: that sum
  * divided by the bag's length; an empty bag still pools to zero.  The
  * backward of a mean-pooled plan divides each lookup's contribution by the
- * length of its bag.  Applies to every later call on the plan; mean-pooled
- * plans do not take the histogram path.  Errors: TBE_EINVAL (NULL plan,
- * unknown mode).
+ * length of its bag.  Applies to every later call on the plan (the
+ * histogram path, where it applies, divides its sums the same way).  Errors:
+ * TBE_EINVAL (NULL plan, unknown mode).
  */
 tbe_status tbe_plan_set_pooling(tbe_plan* plan, int32_t pooling);
 

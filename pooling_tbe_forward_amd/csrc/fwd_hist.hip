@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, KS > 0 ? 4 : 1) void k_fwd_hist(
     const TableDesc* __restrict__ tables, HistTables list, uint32_t B, uint32_t groups_per_table,
     int32_t sumD, const _Float16* __restrict__ weights, const IT* __restrict__ indices,
     const IT* __restrict__ offsets, float* __restrict__ out, int32_t stage_elems,
-    int32_t cnt_off, int32_t cnt_buf_words, uint32_t blocks_per_table)
+    int32_t cnt_off, int32_t cnt_buf_words, uint32_t blocks_per_table, int32_t mean)
 {
     static_assert(KS * TPW <= kRegFrags && TPW <= kMaxTilesPerWave, "register B operands");
     constexpr int kTpw = KS > 0 ? TPW : kMaxTilesPerWave;   // accumulator tiles per wave
@@ -461,8 +461,13 @@ __global__ __launch_bounds__(256, KS > 0 ? 4 : 1) void k_fwd_hist(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 4 * (lane >> 4) + v;
+                float val = acc[m][v];
+                if (mean) {   // one rounding of sum / length; an empty bag stays 0
+                    const int64_t len = gi.e[row] - gi.s[row];
+                    if (len > 0) val = val / static_cast<float>(len);
+                }
                 if (row < cur.nb)
-                    out[static_cast<int64_t>(cur.b0 + row) * sumD + d.out_off + col] = acc[m][v];
+                    out[static_cast<int64_t>(cur.b0 + row) * sumD + d.out_off + col] = val;
             }
         }
         if (!has_next) break;
@@ -505,7 +510,7 @@ void launch_one(size_t lds, const tbe_plan* p, const HistTables& list, uint32_t 
     hipLaunchKernelGGL(k, dim3(bpt * n), dim3(256), lds, a.stream, p->d_tables, list, B, gpt,
                        p->sum_D, static_cast<const _Float16*>(a.weights),
                        static_cast<const IT*>(a.indices), static_cast<const IT*>(a.offsets), a.out,
-                       stage, cnt_off, cnt_buf_words, bpt);
+                       stage, cnt_off, cnt_buf_words, bpt, a.mean ? 1 : 0);
 }
 
 // Register-operand shape (k steps, tiles per wave) for a launch whose tables

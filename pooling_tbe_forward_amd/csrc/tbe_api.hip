@@ -47,9 +47,8 @@ tbe_status check_call(const tbe_plan* p, int32_t B, int64_t num_indices, const v
 
 bool use_hist(const tbe_plan* p, int32_t B, int64_t N)
 {
-    // the histogram kernel pools sums only (a speed path: the gather kernel
-    // gives the same results)
-    if (p->tuning.hist_mode == 1 || p->pooling == TBE_POOL_MEAN) return false;
+    // a speed path: the gather kernel gives the same results (sum and mean)
+    if (p->tuning.hist_mode == 1) return false;
     bool any = false;
     for (int t = 0; t < p->T; ++t) any |= (p->h_tables[t].flags & TD_HIST_OK) != 0;
     if (!any) return false;

@@ -40,6 +40,42 @@ def test_mean_forward_vs_oracle(name, B):
         assert np.all(got[2, cols[1]:cols[2]] == 0)     # the forced empty bag (t=1, b=2)
 
 
+
+@pytest.mark.parametrize("seed,max_len", [(71, 90), (72, 2600)])
+def test_mean_histogram_path_bit_exact(seed, max_len):
+    """Mean pooling on the histogram path: small fp16 tables with integer
+    weights, so every bag's sum is exact on both forward paths and the one
+    division per bag gives the same bits; both equal the fp64 quotient to an
+    ulp.  max_len 2600 makes bags longer than one 2048-id counting window."""
+    prob, packed = dg.exact_problem(seed, T=3, B=45, dims=(64, 128, 16), wdtype="f16",
+                                    weighted=False, max_len=max_len, max_rows=40)
+    # empty bags (one per table) must stay zero on both paths
+    keep = np.ones(prob.indices.size, bool)
+    for t in range(prob.T):
+        g = t * prob.B + 3 + t
+        keep[prob.offsets[g]:prob.offsets[g + 1]] = False
+        prob.lengths[t, 3 + t] = 0
+    prob.indices = prob.indices[keep]
+    prob.offsets = np.concatenate([[0], np.cumsum(prob.lengths.ravel())]).astype(np.int64)
+    w = H.device_weights_from_host(packed)
+    outs = []
+    for mode in (2, 1):   # histogram path forced, then the gather alone
+        plan = _plan(prob)
+        tbe.tbe_set_tuning(plan, hist_mode=mode)
+        d = H.device_inputs(prob)
+        out = torch.full((prob.B, prob.sum_D), float("nan"), dtype=torch.float32, device="cuda")
+        tbe.tbe_forward(plan, prob.B, w, d["indices"], d["offsets"], d["psw"], out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    tabs = oracle.dense_tables(packed, prob.rows, prob.dims)
+    ref = oracle.forward(prob.T, prob.B, prob.rows, prob.dims, H.wcode(prob), tabs, prob.indices,
+                         prob.offsets, prob.psw, prob.weighted, pooling="mean")
+    rep = H.allclose_report(outs[0], ref, 1e-6, 0.0)
+    assert rep["ok"], rep
+    assert (prob.lengths == 0).any()
+
+
 def _oracle_rows(prob, keys, pooling, state_in=None, eps=None):
     tt, rr = H.key_to_table_row(prob, keys)
     tabs = H.sparse_tables(prob, [np.unique(rr[tt == t]) for t in range(prob.T)])
