@@ -72,7 +72,11 @@ typedef struct {
                                   column block of a table, B x columns x 4 bytes; rows
                                   wider than that are reduced in column blocks of at least
                                   16 lanes' loads (0 = whole rows) */
-    int32_t reserved[10];
+    int32_t sort_mode;         /* backward sort: 0 auto, 1 one sort over every table's keys,
+                                  2 per table (each table's lookups sorted on their rows
+                                  inside the table's own positions; up to 1024 tables,
+                                  else as 1) */
+    int32_t reserved[9];
 } tbe_tuning;
 
 /* Bits of a backward workspace's error word (tbe_workspace_status; also

@@ -68,14 +68,32 @@ constexpr int kSortRoundsSmall = 4;  // ... for small batches (see kSmallN)
 // workload (328K lookups) radix 45 -> 43 us and encode 17 -> 14 us; stress
 // (1.6M) and mixed (4.9M) slower with the short tiles.
 constexpr int64_t kSmallN = int64_t(1) << 19;
+constexpr int kSegMaxTables = 1024;  // segmented sort: tables laid out by one block
 }  // namespace
 
 BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
 {
     BwdLayout L;
     L.N = N;
+    const bool small = N <= kSmallN;
+    L.sort_tile = kSortThreads * (small ? kSortRoundsSmall : kSortRounds);
+    const int64_t gtiles = (N + L.sort_tile - 1) / L.sort_tile;
+    // Keys of different tables never collide and a batch's lookups come table
+    // by table, so each table's segment of lookup positions can be sorted on
+    // its own: on row bits only (the widest table's, not those of the sum of
+    // all rows), with look-back chains that stay inside one table.  Taken
+    // when tables are few against the tiles (each table then adds at most one
+    // part-filled tile).
+    const int sm = p->tuning.sort_mode;
+    L.seg = p->T > 0 && N > 0 && p->T <= kSegMaxTables && sm != 1 &&
+            (sm == 2 || 2 * int64_t(p->T) <= gtiles);
+    int64_t key_range = p->sum_rows;
+    if (L.seg) {
+        key_range = 1;
+        for (int t = 0; t < p->T; ++t) key_range = p->rows[t] > key_range ? p->rows[t] : key_range;
+    }
     int bits = 0;
-    while (bits < 32 && (uint64_t(1) << bits) < uint64_t(p->sum_rows)) ++bits;
+    while (bits < 32 && (uint64_t(1) << bits) < uint64_t(key_range)) ++bits;
     L.nbits = bits;
     L.npasses = bits == 0 ? 1 : (bits + kMaxDigitBits - 1) / kMaxDigitBits;
     const int per = bits == 0 ? 1 : (bits + L.npasses - 1) / L.npasses;
@@ -84,9 +102,7 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
         L.digit_bits[i] = per < left ? per : left;
         left -= L.digit_bits[i];
     }
-    const bool small = N <= kSmallN;
-    L.sort_tile = kSortThreads * (small ? kSortRoundsSmall : kSortRounds);
-    L.sort_blocks = static_cast<int32_t>((N + L.sort_tile - 1) / L.sort_tile);
+    L.sort_blocks = static_cast<int32_t>(gtiles + (L.seg ? p->T : 0));
     L.rle_tile = kRleThreads * (small ? kRleItemsSmall : kRleItems);
     L.rle_blocks = static_cast<int32_t>((N + L.rle_tile - 1) / L.rle_tile);
     const int64_t total_bags = int64_t(p->T) * B;
@@ -98,6 +114,15 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     if (pb < 1) pb = 1;
     L.prep_blocks = static_cast<int32_t>(pb);
     L.prep_bags = static_cast<int32_t>((total_bags + pb - 1) / pb);
+    if (L.seg) {   // blocks of one table each (its digit counts are the table's)
+        int64_t bpb = L.prep_bags;
+        if (bpb > B) bpb = B;
+        if (bpb < 1) bpb = 1;
+        L.prep_bags = static_cast<int32_t>(bpb);
+        L.prep_bpt = static_cast<int32_t>((B + bpb - 1) / bpb);
+        L.prep_blocks = L.prep_bpt * p->T;
+        L.seg_copies = L.prep_bpt < kTotCopies ? L.prep_bpt : kTotCopies;
+    }
     const int64_t tau = p->tuning.tau > 0 ? p->tuning.tau : 1;
     const int64_t C = p->tuning.chunk > 0 ? p->tuning.chunk : 1;
     int64_t mc = N / C + N / tau + 1;
@@ -131,6 +156,10 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     L.off_chunk_info = take(size_t(mc > 0 ? mc : 1) * 8);
     const size_t acc = p->wdtype == TBE_F32 ? 8 : 4;
     L.off_partials = take(size_t(mc > 0 ? mc : 1) * p->max_D * acc);
+    if (L.seg) {
+        L.off_tab_tot = take(size_t(p->T) * L.seg_copies * L.npasses * kRadixMax * 4);
+        L.off_seg_tiles = take(size_t(L.sort_blocks) * 16);
+    }
     L.total = o;
     return L;
 }
@@ -276,13 +305,17 @@ enum PayloadMode : int {
 // thread per step: the bag of a lookup comes from a branchless binary search
 // over the block's bag starts in LDS, so the searches of a thread's lookups
 // interleave.
+// Segmented sort (tab_tot set): seg_bpt blocks per table, each within one
+// table; digits are of the row (the id), and each block adds its digit counts
+// to one of its table's seg_copies copies ([T][seg_copies][npasses][kRadixMax],
+// zeroed by k_seg_setup).
 template <typename IT, int MODE>
 __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
     const IT* __restrict__ indices, const IT* __restrict__ offsets,
     const float* __restrict__ psw, uint32_t* __restrict__ keys, void* __restrict__ vals,
     uint32_t* __restrict__ totals, PassBits pb, uint32_t* __restrict__ status,
-    size_t status_words)
+    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot)
 {
     __shared__ uint32_t hist[4][kRadixMax];
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
@@ -290,8 +323,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     __shared__ uint32_t hwt[MODE == kPayloadMean ? kPrepMaxBags + 1 : 1];   // tables' weighted flag
     const int tid = threadIdx.x;
     for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) (&hist[0][0])[i] = 0u;
-    const uint32_t g0 = blockIdx.x * bags_per_block;
-    const uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
+    const bool seg = tab_tot != nullptr;
+    uint32_t g0 = blockIdx.x * bags_per_block;
+    uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
+    if (seg) {
+        const uint32_t t = blockIdx.x / seg_bpt, j = blockIdx.x - t * seg_bpt;
+        const uint32_t b0 = j * bags_per_block;
+        g0 = t * B + b0;
+        nb = b0 < B ? min(bags_per_block, B - b0) : 0u;
+    }
     const uint32_t t_first = nb ? g0 / B : 0;
     const uint32_t t_count = nb ? (g0 + nb - 1) / B - t_first + 1 : 0;   // <= nb
     const int64_t P0 = nb ? static_cast<int64_t>(offsets[g0]) : 0;
@@ -356,9 +396,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const bool ok = base + u * kPrepThreads + tid < len;
+            // (segmented sort: the row's digits)
+            const uint32_t dk = seg ? static_cast<uint32_t>(id[u]) : key[u];
             if (ok)
                 for (int q = 0; q < pb.npasses; ++q) {
-                    const uint32_t d = (key[u] >> pb.shift[q]) & pb.mask[q];
+                    const uint32_t d = (dk >> pb.shift[q]) & pb.mask[q];
                     const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
                     const uint64_t same = __ballot(d == d0);
                     if (d != d0)
@@ -381,17 +423,83 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         }
     }
     __syncthreads();
-    // digit totals are spread over kTotCopies copies (fewer adds per address)
-    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadixMax);
-    for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) {
-        const int q = i / kRadixMax;
-        const uint32_t c = hist[q][i % kRadixMax];
-        if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
+    if (seg) {   // one copy of this table's counts (blocks of the table share the copies)
+        const uint32_t t = blockIdx.x / seg_bpt, j = blockIdx.x - t * seg_bpt;
+        uint32_t* tt = tab_tot + (size_t(t) * seg_copies + j % seg_copies) * pb.npasses * kRadixMax;
+        for (int i = tid; i < pb.npasses * kRadixMax; i += kPrepThreads) {
+            const uint32_t c = hist[i / kRadixMax][i % kRadixMax];
+            if (c) atomicAdd(&tt[i], c);
+        }
+    } else {
+        // digit totals are spread over kTotCopies copies (fewer adds per address)
+        uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadixMax);
+        for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) {
+            const int q = i / kRadixMax;
+            const uint32_t c = hist[q][i % kRadixMax];
+            if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
+        }
     }
     // the look-back words of the radix passes and the run-length encode
     for (size_t i = blockIdx.x * size_t(kPrepThreads) + tid; i < status_words;
          i += size_t(gridDim.x) * kPrepThreads)
         status[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Segmented sort set-up, before the key pass.  Block 0 lays out the tiles,
+// each inside one table's segment of lookup positions, in table order (slots
+// past the last tile are marked unused: table 0xFFFFFFFF); the other blocks
+// zero the per-table digit counts the key pass adds to.  Everything is written
+// whole, every call.
+template <typename IT>
+__global__ __launch_bounds__(1024) void k_seg_setup(
+    const IT* __restrict__ offsets, uint32_t B, int32_t T, uint32_t* __restrict__ tab_tot,
+    uint32_t tot_words, uint4* __restrict__ tiles, uint32_t ntiles, uint32_t tile)
+{
+    const int tid = threadIdx.x;
+    if (blockIdx.x > 0) {
+        for (size_t i = size_t(blockIdx.x - 1) * 1024 + tid; i < tot_words;
+             i += size_t(gridDim.x - 1) * 1024)
+            tab_tot[i] = 0u;
+        return;
+    }
+    static_assert(kSegMaxTables <= 1024, "one thread per table");
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t first_of[kSegMaxTables + 1], seg_s[kSegMaxTables], seg_e[kSegMaxTables];
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t s = 0, e = 0, n = 0;
+    if (tid < T) {
+        s = static_cast<uint32_t>(offsets[size_t(tid) * B]);
+        e = static_cast<uint32_t>(offsets[size_t(tid + 1) * B]);
+        n = e > s ? (e - s + tile - 1) / tile : 0u;
+    }
+    const uint32_t inc = wave_incl_scan(n, lane);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t first = inc - n;
+    for (int w = 0; w < wave; ++w) first += wsum[w];
+    if (tid < T) {
+        first_of[tid] = first;
+        seg_s[tid] = s;
+        seg_e[tid] = e;
+    }
+    if (tid == T - 1) first_of[T] = first + n;
+    __syncthreads();
+    const uint32_t used = first_of[T];
+    for (uint32_t i = tid; i < ntiles; i += 1024) {
+        if (i >= used) {
+            tiles[i] = make_uint4(0u, 0u, 0u, 0xFFFFFFFFu);
+            continue;
+        }
+        int lo = 0, hi = T - 1;   // the last table whose first tile is at or before i
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first_of[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        const uint32_t k = i - first_of[lo];
+        tiles[i] = make_uint4(seg_s[lo] + k * tile, min(seg_e[lo], seg_s[lo] + (k + 1) * tile),
+                              seg_s[lo], static_cast<uint32_t>(lo));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -404,13 +512,26 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 // (with each staged position's digit beside it, for its output position), so
 // a tile needs about 63 KB of LDS instead of 89 KB and, with a 4-byte payload
 // (at most 64 VGPRs), two tiles share a CU.
+// Segmented sort (seg.tiles set): a tile's keys, positions and digit counts
+// come from its slot in seg.tiles (one table's segment), digits are of the
+// row (key - the table's first key), and the look-back stops at the table's
+// first tile.
+struct SegPass {
+    const uint4* tiles;      // [ntiles] {first position, end, table's first position, table}
+    const uint32_t* tot;     // this pass's digit counts of table t, copy c at
+    uint32_t stride;         //   tot + t * stride + c * cstride
+    uint32_t cstride;
+    uint32_t copies;
+    const uint32_t* hash_off;
+};
+
 template <int R, typename PT, int NB, bool LOWLDS>
-__global__ __launch_bounds__(kSortThreads) void k_onesweep(
+__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LOWLDS ? 8 : 4))) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const PT* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, PT* __restrict__ vals_out, uint32_t N, int shift,
     const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ err, uint32_t ntiles,
-    uint32_t* __restrict__ prev_totals)
+    uint32_t* __restrict__ prev_totals, SegPass seg)
 {
     constexpr int NW = kSortThreads / 64;
     constexpr int RX = NB > 8 ? 512 : 256;   // digit counters
@@ -430,18 +551,57 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    // the ticket is taken by a wave that loads no totals, so the two overlap
-    if (tid == RX) s_tile = take_ticket(ticket, ntiles);
-    uint32_t tot = 0;
-    if (tid < RX) {
+    constexpr uint32_t kTile = uint32_t(kSortThreads) * R;
+    uint32_t tot = 0, tile, t0, tend, base0 = 0, hoff = 0, lb_base = 0, lb_tile;
+    if (seg.tiles == nullptr) {
+        // the ticket is taken by a wave that loads no totals, so the two overlap
+        if (tid == RX % kSortThreads) s_tile = take_ticket(ticket, ntiles);
+        if (tid < RX) {
 #pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) tot += totals[cp * 4 * kRadixMax + tid];
+            for (int cp = 0; cp < kTotCopies; ++cp) tot += totals[cp * 4 * kRadixMax + tid];
+        }
+        // the previous pass's digit totals are no longer needed: leave them zero
+        if (blockIdx.x == 0 && prev_totals && tid < kRadixMax)
+#pragma unroll
+            for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadixMax + tid] = 0u;
+        for (int i = tid; i < NW * RX; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
+        __syncthreads();
+        tile = __builtin_amdgcn_readfirstlane(s_tile);
+        if (tile >= ntiles) {          // only with an uninitialised control block
+            if (tid == 0) atomicOr(err, kErrControl);
+            return;
+        }
+        t0 = tile * kTile;
+        tend = (N - t0) < kTile ? N : t0 + kTile;
+        lb_tile = tile;
+    } else {
+        if (tid == 0) s_tile = take_ticket(ticket, ntiles);
+        for (int i = tid; i < NW * RX; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
+        __syncthreads();
+        tile = __builtin_amdgcn_readfirstlane(s_tile);
+        if (tile >= ntiles) {
+            if (tid == 0) atomicOr(err, kErrControl);
+            return;
+        }
+        const uint4 sl = seg.tiles[tile];
+        const uint32_t t = __builtin_amdgcn_readfirstlane(sl.w);
+        if (t == 0xFFFFFFFFu) return;   // a slot past the last tile
+        t0 = __builtin_amdgcn_readfirstlane(sl.x);
+        tend = __builtin_amdgcn_readfirstlane(sl.y);
+        base0 = __builtin_amdgcn_readfirstlane(sl.z);
+        hoff = seg.hash_off[t];
+        if (tid < RX) {   // branch-free, so the loads of the copies overlap
+            const uint32_t* tp = seg.tot + size_t(t) * seg.stride + tid;
+            uint32_t v[kTotCopies];
+#pragma unroll
+            for (int c = 0; c < kTotCopies; ++c)
+                v[c] = tp[size_t(c < seg.copies ? c : 0) * seg.cstride];
+#pragma unroll
+            for (int c = 0; c < kTotCopies; ++c) tot += c < seg.copies ? v[c] : 0u;
+        }
+        lb_tile = (t0 - base0) / kTile;   // the tile's index inside its table
+        lb_base = tile - lb_tile;         // the table's first tile
     }
-    // the previous pass's digit totals are no longer needed: leave them zero
-    if (blockIdx.x == 0 && prev_totals && tid < kRadixMax)
-#pragma unroll
-        for (int cp = 0; cp < kTotCopies; ++cp) prev_totals[cp * 4 * kRadixMax + tid] = 0u;
-    for (int i = tid; i < NW * RX; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
     uint32_t inc = 0;
     if (tid < RX) {
         inc = wave_incl_scan(tot, lane);
@@ -451,30 +611,25 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     if (tid < RX) {
         uint32_t pre = 0;
         for (int w = 0; w < wave; ++w) pre += wsum[w];
-        gofs[tid] = pre + inc - tot;   // first output position of digit tid
-    }
-    const uint32_t tile = s_tile;
-    if (tile >= ntiles) {          // only with an uninitialised control block
-        if (tid == 0) atomicOr(err, kErrControl);
-        return;
+        gofs[tid] = base0 + pre + inc - tot;   // first output position of digit tid
     }
 
     constexpr uint32_t mask = (1u << NB) - 1u;
-    const uint32_t wbase = tile * (uint32_t(kSortThreads) * R) + static_cast<uint32_t>(wave) * (64u * R);
+    const uint32_t wbase = t0 + static_cast<uint32_t>(wave) * (64u * R);
     uint32_t k[R], dg[R], rk[R];
     PT v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = wbase + r * 64u + lane;
-        const bool ok = i < N;
+        const bool ok = i < tend;
         k[r] = ok ? keys_in[i] : 0u;
         if (ok) v[r] = vals_in[i];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = wbase + r * 64u + lane;
-        const bool ok = i < N;
-        const uint32_t d = (k[r] >> shift) & mask;
+        const bool ok = i < tend;
+        const uint32_t d = ((k[r] - hoff) >> shift) & mask;
         // lanes whose digit differs from this lane's in some bit, as two
         // 32-bit halves: per bit, the ballot of the bit xor this lane's bit
         // spread over a word (this shape compiles to three-input bit ops)
@@ -539,7 +694,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = wbase + r * 64u + lane;
-        if (i < N) {
+        if (i < tend) {
             const uint32_t lp = lbase[dg[r]] + wcnt[wave][dg[r]] + rk[r];
             sk[lp] = k[r];
             if constexpr (LOWLDS)
@@ -548,18 +703,18 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
                 sv[lp] = v[r];
         }
     }
-    if (q == 0) delta[d] = gofs[d] + lookback<16>(status + d, RX, tile, all, err) - lb;
+    if (q == 0)
+        delta[d] = gofs[d] + lookback<16>(status + size_t(lb_base) * RX + d, RX, lb_tile, all, err) - lb;
     __syncthreads();
     // write out: consecutive threads store consecutive positions of a digit
-    const uint32_t t0 = tile * (uint32_t(kSortThreads) * R);
-    const uint32_t cnt = (N - t0) < uint32_t(kSortThreads * R) ? N - t0 : uint32_t(kSortThreads * R);
+    const uint32_t cnt = tend - t0;
     if constexpr (!LOWLDS) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t e = r * kSortThreads + tid;
             if (e < cnt) {
                 const uint32_t key = sk[e];
-                const uint32_t pos = delta[(key >> shift) & mask] + e;
+                const uint32_t pos = delta[((key - hoff) >> shift) & mask] + e;
                 if (pos >= N) continue;  // unreachable when the counts are consistent
                 keys_out[pos] = key;
                 vals_out[pos] = sv[e];
@@ -582,7 +737,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t i = wbase + r * 64u + lane;
-                if (i < N) {
+                if (i < tend) {
                     const uint32_t lp = lbase[dg[r]] + wcnt[wave][dg[r]] + rk[r];
                     uint32_t word[W];
                     __builtin_memcpy(word, &v[r], sizeof(PT));
@@ -932,11 +1087,22 @@ void launch_onesweep(BwdArgs& a, uint32_t nb, const uint32_t* keys_in, const PT*
                      uint32_t* keys_out, PT* vals_out, uint32_t N, int shift, int pass,
                      uint32_t* ctl, uint32_t* status)
 {
+    const BwdLayout& L = a.L;
+    SegPass seg{};
+    if (L.seg) {
+        seg.tiles = reinterpret_cast<const uint4*>(a.ws + L.off_seg_tiles);
+        seg.tot = reinterpret_cast<const uint32_t*>(a.ws + L.off_tab_tot) + pass * kRadixMax;
+        seg.cstride = static_cast<uint32_t>(L.npasses * kRadixMax);
+        seg.stride = seg.cstride * L.seg_copies;
+        seg.copies = static_cast<uint32_t>(L.seg_copies);
+        seg.hash_off = a.plan->d_hash_off;
+    }
     hipLaunchKernelGGL((k_onesweep<R, PT, NB, LOWLDS>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys_in,
                        vals_in, keys_out, vals_out, N, shift, ctl + kCtlTotals + pass * kRadixMax,
                        status + static_cast<size_t>(pass) * kRadixMax * nb,
                        ctl + kCtlTicket + pass, ctl + kCtlError, nb,
-                       pass > 0 ? ctl + kCtlTotals + (pass - 1) * kRadixMax : nullptr);
+                       pass > 0 && !L.seg ? ctl + kCtlTotals + (pass - 1) * kRadixMax : nullptr,
+                       seg);
 }
 
 // The low-LDS tile stages digits as bytes, so a 9-bit pass takes the
@@ -994,6 +1160,16 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
 {
     const BwdLayout& L = a.L;
     char* ws = a.ws;
+    if (L.seg) {
+        const uint32_t words = static_cast<uint32_t>(a.plan->T) * L.seg_copies * L.npasses * kRadixMax;
+        const uint32_t zb = (words + 16 * 1024 - 1) / (16 * 1024);
+        hipLaunchKernelGGL((k_seg_setup<IT>), dim3(1 + zb), dim3(1024), 0, a.stream,
+                           static_cast<const IT*>(a.offsets), static_cast<uint32_t>(a.B),
+                           a.plan->T, reinterpret_cast<uint32_t*>(ws + L.off_tab_tot), words,
+                           reinterpret_cast<uint4*>(ws + L.off_seg_tiles),
+                           static_cast<uint32_t>(L.sort_blocks),
+                           static_cast<uint32_t>(L.sort_tile));
+    }
     hipLaunchKernelGGL((k_prep<IT, MODE>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
                        a.plan->d_tables, static_cast<uint32_t>(a.B), total_bags,
                        static_cast<uint32_t>(L.prep_bags), static_cast<const IT*>(a.indices),
@@ -1001,7 +1177,9 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                        reinterpret_cast<uint32_t*>(ws + L.off_keys[0]),
                        static_cast<void*>(ws + L.off_vals[0]),
                        reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlTotals, pb,
-                       reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words);
+                       reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words,
+                       static_cast<uint32_t>(L.prep_bpt), static_cast<uint32_t>(L.seg_copies),
+                       L.seg ? reinterpret_cast<uint32_t*>(ws + L.off_tab_tot) : nullptr);
 }
 
 }  // namespace
@@ -1076,7 +1254,7 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                        reinterpret_cast<uint4*>(ws + L.off_short_info),
                        reinterpret_cast<uint4*>(ws + L.off_long_info), ctl + kCtlCounts,
                        ctl + kCtlMode, static_cast<uint32_t>(L.max_long),
-                       ctl + kCtlTotals + (L.npasses - 1) * kRadixMax,
+                       L.seg ? nullptr : ctl + kCtlTotals + (L.npasses - 1) * kRadixMax,
                        reinterpret_cast<uint32_t*>(ws + L.off_unique),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_start),
                        reinterpret_cast<uint32_t*>(ws + L.off_run_len),

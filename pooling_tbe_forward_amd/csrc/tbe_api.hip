@@ -26,6 +26,7 @@ tbe_tuning default_tuning()
     t.hist_min_mean_len = 64; // histogram path pays once bags are this long
     t.fwd_bags_per_wave = 1;
     t.seg_slab_kib = 1024;   // grad_output slab per column block: a quarter of an XCD's L2
+    t.sort_mode = 0;         // auto
     return t;
 }
 
@@ -190,7 +191,7 @@ tbe_status tbe_set_tuning(tbe_plan* p, const tbe_tuning* t)
     if (!p || !t) return TBE_EINVAL;
     if (t->tau < 1 || t->chunk < 1 || t->hist_mode < 0 || t->hist_mode > 2 ||
         t->hist_min_mean_len < 0 || t->fwd_bags_per_wave < 1 || t->fwd_bags_per_wave > 1024 ||
-        t->seg_slab_kib < 0)
+        t->seg_slab_kib < 0 || t->sort_mode < 0 || t->sort_mode > 2)
         return TBE_EINVAL;
     p->tuning = *t;
     return TBE_OK;

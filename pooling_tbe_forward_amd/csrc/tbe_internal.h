@@ -127,6 +127,13 @@ struct BwdLayout {
     size_t off_tab_ranges;      // [3][T+1] per table: first short run, first long run, first chunk
     size_t off_chunk_info;      // [max_chunks] {first sorted position, length} of each chunk
     size_t off_partials;        // [max_chunks * max_D] (fp64 or fp32)
+    // Segmented sort (seg): each table's keys are sorted within the table's
+    // own segment of lookup positions, on the widest table's row bits.
+    bool seg = false;
+    int32_t prep_bpt = 0;       // k_prep blocks per table (segmented sort)
+    int32_t seg_copies = 0;     // copies of each table's digit counts (fewer adds per address)
+    size_t off_tab_tot = 0;     // [T][seg_copies][npasses][kRadixMax] digit counts of each table
+    size_t off_seg_tiles = 0;   // [sort_blocks] {first position, end, table's first position, table}
     size_t total = 0;
 };
 BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N);

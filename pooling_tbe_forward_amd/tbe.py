@@ -33,7 +33,7 @@ class tbe_tuning(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("hist_mode", ctypes.c_int32), ("hist_min_mean_len", ctypes.c_int32),
                 ("fwd_bags_per_wave", ctypes.c_int32), ("seg_slab_kib", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 10)]
+                ("sort_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 9)]
 
 
 class tbe_sort_view(ctypes.Structure):

@@ -71,9 +71,10 @@ def _gold_problem(weighted, wdtype):
 
 # ------------------------------------------------------------ integer stage
 @pytest.mark.parametrize("index_dtype", ["i32", "i64"])
-def test_handworked_sort(index_dtype):
+@pytest.mark.parametrize("sort_mode", [1, 2])
+def test_handworked_sort(index_dtype, sort_mode):
     prob, _ = _gold_problem(False, "f32")
-    g = gpu_sort(prob, index_dtype, tau=GOLD["tau"])
+    g = gpu_sort(prob, index_dtype, tau=GOLD["tau"], sort_mode=sort_mode)
     for k in ("sorted_keys", "sorted_pos", "unique_keys", "run_start", "run_len",
               "long_runs", "short_runs"):
         assert g[k].tolist() == GOLD[k], k
@@ -82,9 +83,12 @@ def test_handworked_sort(index_dtype):
 @pytest.mark.parametrize("name,B,seed", [("toy", None, 1), ("uniform", 256, 2), ("stress", 300, 3),
                                          ("mixed", 100, 4), ("hist", 50, 5)])
 @pytest.mark.parametrize("tau", [1, 32, 256, 2 ** 31 - 1])
-def test_sort_rle_vs_oracle(name, B, seed, tau):
+@pytest.mark.parametrize("sort_mode", [1, 2])
+def test_sort_rle_vs_oracle(name, B, seed, tau, sort_mode):
+    """One sort over every table's keys (1) and per-table sorts (2): the
+    stable order is the same either way."""
     prob = dg.make_problem(name, seed=seed, B=B)
-    g = gpu_sort(prob, tau=tau)
+    g = gpu_sort(prob, tau=tau, sort_mode=sort_mode)
     o = H.oracle_sort(prob, tau)
     _compare_sort(g, o, prob.N)
 
@@ -100,9 +104,19 @@ def test_sort_rle_full_size(name, tau):
     _compare_sort(g, o, prob.N)
 
 
-def test_sort_int64_indices():
+@pytest.mark.parametrize("name", ["uniform", "stress", "mixed", "band", "hist"])
+def test_sort_rle_full_size_single_sort(name):
+    """Full size with one sort over every table's keys (the automatic choice
+    at these sizes sorts per table)."""
+    prob = dg.make_problem(name)
+    _compare_sort(gpu_sort(prob, tau=64, sort_mode=1), H.oracle_sort(prob, 64), prob.N)
+
+
+@pytest.mark.parametrize("sort_mode", [1, 2])
+def test_sort_int64_indices(sort_mode):
     prob = dg.make_problem("stress", seed=9, B=128)
-    _compare_sort(gpu_sort(prob, "i64", tau=64), H.oracle_sort(prob, 64), prob.N)
+    _compare_sort(gpu_sort(prob, "i64", tau=64, sort_mode=sort_mode), H.oracle_sort(prob, 64),
+                  prob.N)
 
 
 # ------------------------------------------------------------ backward + SGD

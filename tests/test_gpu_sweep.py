@@ -33,7 +33,7 @@ def _cases(n=64, seed=2024):
             max_len=int(rng.choice([3, 12, 40, 90])), max_rows=int(rng.choice([5, 40, 300])),
             tau=int(rng.choice([1, 2, 8, 64, 2 ** 31 - 1])),
             chunk=int(rng.choice([1, 3, 16, 256])),
-            hist_mode=int(rng.choice([0, 1, 2]))))
+            hist_mode=int(rng.choice([0, 1, 2])), sort_mode=int(rng.choice([0, 1, 2]))))
     return out
 
 
@@ -47,7 +47,8 @@ def test_random_exact_case(case):
                                     wdtype=c["wdtype"], weighted=c["weighted"],
                                     max_len=c["max_len"], max_rows=c["max_rows"])
     plan = H.make_plan(prob, c["index_dtype"])
-    tbe.tbe_set_tuning(plan, tau=c["tau"], chunk=c["chunk"], hist_mode=c["hist_mode"])
+    tbe.tbe_set_tuning(plan, tau=c["tau"], chunk=c["chunk"], hist_mode=c["hist_mode"],
+                       sort_mode=c["sort_mode"])
     d = H.device_inputs(prob, c["index_dtype"])
     w = H.device_weights_from_host(packed)
 
