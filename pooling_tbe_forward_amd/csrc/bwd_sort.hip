@@ -1118,12 +1118,13 @@ auto pick_onesweep(int nbits)
     return f;
 }
 
-// Passes of many tiles (more than four per CU of an MI355X) with a 4-byte
-// payload take the low-LDS tile, two per CU.  Measured: production-scale
-// workload (10K tiles) radix sort 1765 -> 1477 us; at 500-600 tiles it was
-// slightly slower (small-table 46 -> 48 us), and with an 8-byte payload it
-// needs more than 64 VGPRs (spills when forced; mixed 196 -> 203 us).
-constexpr uint32_t kLowLdsMinTiles = 1024;
+// Passes of more tiles than an MI355X has CUs with a 4-byte payload take the
+// low-LDS tile, two per CU.  Measured: production-scale workload (10K tiles)
+// radix sort 1765 -> 1477 us, small-table workload (514 tiles) 41 -> 37 us;
+// at 88 tiles of 4096 keys (uniform) it was slower (35 -> 37 us).  With an
+// 8-byte payload it needs more than 64 VGPRs (8-16 spilled when forced;
+// mixed 133 -> 181 us).
+constexpr uint32_t kLowLdsMinTiles = 256;
 
 template <int R, typename PT>
 hipError_t sort_passes(BwdArgs& a)
