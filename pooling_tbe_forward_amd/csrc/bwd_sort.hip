@@ -159,6 +159,8 @@ BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N)
     if (L.seg) {
         L.off_tab_tot = take(size_t(p->T) * L.seg_copies * L.npasses * kRadixMax * 4);
         L.off_seg_tiles = take(size_t(L.sort_blocks) * 16);
+        L.off_tile_bag = take(size_t(L.sort_blocks) * 4);
+        L.off_seg_first = take(size_t(p->T + 1) * 4);
     }
     L.total = o;
     return L;
@@ -203,6 +205,23 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
         if (lane >= d) v += o;
     }
     return v;
+}
+
+// Inclusive maximum over a wavefront's lanes in lane order (values >= 0),
+// with data-parallel-primitive moves: shifts by 1, 2, 4, 8 inside each row of
+// 16 lanes, then row 0's and row 2's last lanes into rows 1 and 3, then lane
+// 31 into rows 2 and 3.  Lanes with no source lane take 0.
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, uint32_t o) { return o > v ? o : v; }
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v)
+{
+    int x = static_cast<int>(v);
+    x = static_cast<int>(dpp_max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false)));  // row_shr:1
+    x = static_cast<int>(dpp_max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false)));  // row_shr:2
+    x = static_cast<int>(dpp_max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false)));  // row_shr:4
+    x = static_cast<int>(dpp_max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false)));  // row_shr:8
+    x = static_cast<int>(dpp_max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false)));  // row_bcast:15
+    x = static_cast<int>(dpp_max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false)));  // row_bcast:31
+    return static_cast<uint32_t>(x);
 }
 
 __device__ __forceinline__ uint32_t ld_acq(const uint32_t* p)
@@ -309,14 +328,19 @@ enum PayloadMode : int {
 // table; digits are of the row (the id), and each block adds its digit counts
 // to one of its table's seg_copies copies ([T][seg_copies][npasses][kRadixMax],
 // zeroed by k_seg_setup).
-template <typename IT, int MODE>
+// LITE (segmented sort whose first radix pass reads the ids itself): digit
+// counts only, no keys or payloads; for each radix tile that starts among the
+// block's lookups, the bag holding that first position goes to tile_bag.
+template <typename IT, int MODE, bool LITE>
 __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
     const IT* __restrict__ indices, const IT* __restrict__ offsets,
     const float* __restrict__ psw, uint32_t* __restrict__ keys, void* __restrict__ vals,
     uint32_t* __restrict__ totals, PassBits pb, uint32_t* __restrict__ status,
-    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot)
+    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot,
+    uint32_t* __restrict__ tile_bag, const uint32_t* __restrict__ seg_first, uint32_t sort_tile)
 {
+    static_assert(!LITE || MODE != kPayloadMean, "mean pooling keeps the full key pass");
     __shared__ uint32_t hist[4][kRadixMax];
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
     __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
@@ -345,6 +369,23 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const uint32_t len = nb ? boff[nb] : 0u;
     uint32_t top = 1;
     while (top < nb) top <<= 1;
+    if constexpr (LITE) {
+        // tiles of this table whose first position (relative to the table's
+        // first lookup) falls in [rel0, rel0 + len)
+        const uint32_t t = blockIdx.x / seg_bpt;
+        const uint32_t rel0 =
+            static_cast<uint32_t>(P0 - static_cast<int64_t>(offsets[size_t(t) * B]));
+        for (uint32_t kt = (rel0 + sort_tile - 1) / sort_tile + tid; kt * sort_tile < rel0 + len;
+             kt += kPrepThreads) {
+            const uint32_t rp = kt * sort_tile - rel0;
+            uint32_t g = 0;   // the last bag whose start is <= rp (not empty)
+            for (uint32_t st = top; st > 0; st >>= 1) {
+                const uint32_t c = g + st;
+                g = (c < nb && boff[c] <= rp) ? c : g;
+            }
+            tile_bag[seg_first[t] + kt] = g0 + g - t * B;
+        }
+    }
     constexpr int UN = 8;
     for (uint32_t base = 0; base < len; base += kPrepThreads * UN) {
         IT id[UN];
@@ -354,14 +395,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         for (int u = 0; u < UN; ++u) {
             const uint32_t rp = base + u * kPrepThreads + tid;
             id[u] = rp < len ? indices[P0 + rp] : IT(0);
-            wv[u] = ((MODE == kPayloadSampleW || (MODE == kPayloadMean && psw)) && rp < len)
+            wv[u] = (!LITE && (MODE == kPayloadSampleW || (MODE == kPayloadMean && psw)) && rp < len)
                         ? psw[P0 + rp] : 1.f;
             g[u] = 0;
         }
         // g[u]: the last bag whose start is <= rp (that bag is not empty);
         // branch-free, so the searches of the used slots interleave
-        const uint32_t nu = (len - base + kPrepThreads - 1) / kPrepThreads;   // slots in use
-        for (uint32_t st = top; st > 0; st >>= 1) {
+        const uint32_t nu = LITE ? 0u : (len - base + kPrepThreads - 1) / kPrepThreads;   // slots in use
+        for (uint32_t st = LITE ? 0u : top; st > 0; st >>= 1) {
 #pragma unroll
             for (int u = 0; u < UN; ++u) {
                 if (u < nu) {
@@ -376,7 +417,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         // registers are not reused before the loop ends, so no wait on it
         uint32_t key[UN], pay[UN];
 #pragma unroll
-        for (int u = 0; u < UN; ++u) {
+        for (int u = 0; u < UN && !LITE; ++u) {
             const uint32_t gg = g0 + g[u];
             const uint32_t t = gg / B;
             key[u] = hoff[t - t_first] + static_cast<uint32_t>(id[u]);
@@ -397,7 +438,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         for (int u = 0; u < UN; ++u) {
             const bool ok = base + u * kPrepThreads + tid < len;
             // (segmented sort: the row's digits)
-            const uint32_t dk = seg ? static_cast<uint32_t>(id[u]) : key[u];
+            const uint32_t dk = (LITE || seg) ? static_cast<uint32_t>(id[u]) : key[u];
             if (ok)
                 for (int q = 0; q < pb.npasses; ++q) {
                     const uint32_t d = (dk >> pb.shift[q]) & pb.mask[q];
@@ -410,7 +451,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
                 }
         }
 #pragma unroll
-        for (int u = 0; u < UN; ++u) {
+        for (int u = 0; u < UN && !LITE; ++u) {
             const uint32_t rp = base + u * kPrepThreads + tid;
             if (rp < len) {
                 const int64_t p = P0 + rp;
@@ -448,13 +489,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 // ---------------------------------------------------------------------------
 // Segmented sort set-up, before the key pass.  Block 0 lays out the tiles,
 // each inside one table's segment of lookup positions, in table order (slots
-// past the last tile are marked unused: table 0xFFFFFFFF); the other blocks
-// zero the per-table digit counts the key pass adds to.  Everything is written
-// whole, every call.
+// past the last tile are marked unused: table 0xFFFFFFFF), and writes each
+// table's first tile slot to first_out[T + 1]; the other blocks zero the
+// per-table digit counts the key pass adds to.  Everything is written whole,
+// every call.
 template <typename IT>
 __global__ __launch_bounds__(1024) void k_seg_setup(
     const IT* __restrict__ offsets, uint32_t B, int32_t T, uint32_t* __restrict__ tab_tot,
-    uint32_t tot_words, uint4* __restrict__ tiles, uint32_t ntiles, uint32_t tile)
+    uint32_t tot_words, uint4* __restrict__ tiles, uint32_t ntiles, uint32_t tile,
+    uint32_t* __restrict__ first_out)
 {
     const int tid = threadIdx.x;
     if (blockIdx.x > 0) {
@@ -480,10 +523,14 @@ __global__ __launch_bounds__(1024) void k_seg_setup(
     for (int w = 0; w < wave; ++w) first += wsum[w];
     if (tid < T) {
         first_of[tid] = first;
+        first_out[tid] = first;
         seg_s[tid] = s;
         seg_e[tid] = e;
     }
-    if (tid == T - 1) first_of[T] = first + n;
+    if (tid == T - 1) {
+        first_of[T] = first + n;
+        first_out[T] = first + n;
+    }
     __syncthreads();
     const uint32_t used = first_of[T];
     for (uint32_t i = tid; i < ntiles; i += 1024) {
@@ -516,6 +563,21 @@ __global__ __launch_bounds__(1024) void k_seg_setup(
 // come from its slot in seg.tiles (one table's segment), digits are of the
 // row (key - the table's first key), and the look-back stops at the table's
 // first tile.
+// FIRST (the first pass of a segmented sort, after a counts-only key pass):
+// a tile reads the ids itself (key = the table's first key + row) and makes
+// its payload: the bag of each position comes from marks at the bags' first
+// positions in LDS and a running maximum over positions, starting from the
+// bag that holds the tile's first position (tile_bag).
+struct FirstPass {
+    const void* indices;        // int32, or int64 when i64
+    const void* offsets;        // [T * B + 1], same type
+    const float* psw;           // per-sample weights (payload pairs)
+    const uint32_t* tile_bag;   // [ntiles] bag (within its table) of each tile's first position
+    uint32_t B;
+    uint32_t i64;
+    uint32_t pos_payload;       // payload = lookup position instead of the bag
+};
+
 struct SegPass {
     const uint4* tiles;      // [ntiles] {first position, end, table's first position, table}
     const uint32_t* tot;     // this pass's digit counts of table t, copy c at
@@ -525,14 +587,15 @@ struct SegPass {
     const uint32_t* hash_off;
 };
 
-template <int R, typename PT, int NB, bool LOWLDS>
+template <int R, typename PT, int NB, bool LOWLDS, bool FIRST>
 __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LOWLDS ? 8 : 4))) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const PT* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, PT* __restrict__ vals_out, uint32_t N, int shift,
     const uint32_t* __restrict__ totals, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ err, uint32_t ntiles,
-    uint32_t* __restrict__ prev_totals, SegPass seg)
+    uint32_t* __restrict__ prev_totals, SegPass seg, FirstPass fp)
 {
+    static_assert(!FIRST || sizeof(PT) == 4 || sizeof(PT) == 8, "payload: bag, position or pair");
     constexpr int NW = kSortThreads / 64;
     constexpr int RX = NB > 8 ? 512 : 256;   // digit counters
     constexpr int NQ = kSortThreads / RX;    // thread groups covering every digit
@@ -548,11 +611,12 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
     __shared__ uint32_t sk[kSortThreads * R];
     __shared__ PT sv[LOWLDS ? 1 : kSortThreads * R];
     __shared__ uint8_t sdig[LOWLDS ? kSortThreads * R : 1];
+    __shared__ uint32_t wmax[FIRST ? kSortThreads / 64 : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     constexpr uint32_t kTile = uint32_t(kSortThreads) * R;
-    uint32_t tot = 0, tile, t0, tend, base0 = 0, hoff = 0, lb_base = 0, lb_tile;
+    uint32_t tot = 0, tile, t0, tend, base0 = 0, hoff = 0, lb_base = 0, lb_tile, tab = 0;
     if (seg.tiles == nullptr) {
         // the ticket is taken by a wave that loads no totals, so the two overlap
         if (tid == RX % kSortThreads) s_tile = take_ticket(ticket, ntiles);
@@ -577,6 +641,8 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
     } else {
         if (tid == 0) s_tile = take_ticket(ticket, ntiles);
         for (int i = tid; i < NW * RX; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
+        if constexpr (FIRST)   // bag marks
+            for (int i = tid; i < static_cast<int>(kTile); i += kSortThreads) sk[i] = 0u;
         __syncthreads();
         tile = __builtin_amdgcn_readfirstlane(s_tile);
         if (tile >= ntiles) {
@@ -586,6 +652,7 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
         const uint4 sl = seg.tiles[tile];
         const uint32_t t = __builtin_amdgcn_readfirstlane(sl.w);
         if (t == 0xFFFFFFFFu) return;   // a slot past the last tile
+        tab = t;
         t0 = __builtin_amdgcn_readfirstlane(sl.x);
         tend = __builtin_amdgcn_readfirstlane(sl.y);
         base0 = __builtin_amdgcn_readfirstlane(sl.z);
@@ -602,6 +669,41 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
         lb_tile = (t0 - base0) / kTile;   // the tile's index inside its table
         lb_base = tile - lb_tile;         // the table's first tile
     }
+    constexpr uint32_t mask = (1u << NB) - 1u;
+    const uint32_t wbase = t0 + static_cast<uint32_t>(wave) * (64u * R);
+    uint32_t k[R], dg[R], rk[R];
+    PT v[R];
+    // FIRST: the bag holding the tile's first position, and the first 1024
+    // bags after it (their first positions), loaded under the rank
+    uint32_t fb = 0u, st_first = 0u;
+    size_t ob = 0;
+    auto bag_start = [&](uint32_t c) {
+        return fp.i64 ? static_cast<uint32_t>(static_cast<const int64_t*>(fp.offsets)[ob + c])
+                      : static_cast<uint32_t>(static_cast<const int32_t*>(fp.offsets)[ob + c]);
+    };
+    if constexpr (FIRST) {
+        fb = __builtin_amdgcn_readfirstlane(fp.tile_bag[tile]);
+        if (fb >= fp.B) {   // only with an inconsistent tile_bag
+            if (tid == 0) atomicOr(err, kErrControl);
+            fb = 0u;
+        }
+        ob = size_t(tab) * fp.B;
+        // the ids (an int64 id's low word: rows are below 2^32) and weights
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t i = wbase + r * 64u + lane;
+            const bool ok = i < tend;
+            uint32_t row = 0u;
+            if (ok) row = static_cast<const uint32_t*>(fp.indices)[fp.i64 ? 2u * i : i];   // i < 2^30
+            k[r] = hoff + row;
+            if constexpr (sizeof(PT) == 8) {
+                uint32_t wb = 0u;
+                if (ok) wb = __float_as_uint(fp.psw[i]);
+                v[r].y = wb;
+            }
+        }
+        if (fb + 1u + tid < fp.B) st_first = bag_start(fb + 1u + tid);
+    }
     uint32_t inc = 0;
     if (tid < RX) {
         inc = wave_incl_scan(tot, lane);
@@ -614,16 +716,14 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
         gofs[tid] = base0 + pre + inc - tot;   // first output position of digit tid
     }
 
-    constexpr uint32_t mask = (1u << NB) - 1u;
-    const uint32_t wbase = t0 + static_cast<uint32_t>(wave) * (64u * R);
-    uint32_t k[R], dg[R], rk[R];
-    PT v[R];
+    if constexpr (!FIRST) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint32_t i = wbase + r * 64u + lane;
-        const bool ok = i < tend;
-        k[r] = ok ? keys_in[i] : 0u;
-        if (ok) v[r] = vals_in[i];
+        for (int r = 0; r < R; ++r) {
+            const uint32_t i = wbase + r * 64u + lane;
+            const bool ok = i < tend;
+            k[r] = ok ? keys_in[i] : 0u;
+            if (ok) v[r] = vals_in[i];
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -653,7 +753,40 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
         dg[r] = d;
         rk[r] = base + below;
     }
-    __syncthreads();
+    if constexpr (FIRST) {
+        // mark each bag that starts inside the tile at its first position
+        // (the largest of bags starting together is the one not empty); the
+        // barrier that ends the rank ends the first 1024 bags' marks
+        uint32_t c = fb + 1u + tid;
+        uint32_t st = st_first;
+        for (;;) {
+            const bool more = c < fp.B && st < tend;
+            if (more && st > t0) atomicMax(&sk[st - t0], c);
+            if (!__syncthreads_or(tid == kSortThreads - 1 && more)) break;
+            c += kSortThreads;
+            if (c < fp.B) st = bag_start(c);
+        }
+        // each position's bag: running maximum over the wave's positions
+        // (the rounds are scanned side by side, then carried in order)
+        uint32_t bm[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            bm[r] = wave_incl_max(sk[static_cast<uint32_t>(wave) * (64u * R) + r * 64u + lane]);
+        uint32_t run = fb;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t m = bm[r] > run ? bm[r] : run;
+            if constexpr (sizeof(PT) == 8)
+                v[r].x = m;
+            else
+                v[r] = m;
+            const uint32_t last = __builtin_amdgcn_readlane(bm[r], 63);
+            run = last > run ? last : run;
+        }
+        if (lane == 0) wmax[wave] = run;   // read after the next barrier
+    } else {
+        __syncthreads();
+    }
     // per digit: exclusive prefix over the waves (NQ groups of NW/NQ waves),
     // the tile's digit total, and its exclusive prefix over digits (lbase)
     const int d = tid & (RX - 1), q = tid / RX;
@@ -689,6 +822,19 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
         lbase[d] = lb;
     }
     __syncthreads();
+    if constexpr (FIRST) {   // the bags carried in from earlier waves
+        uint32_t prior = 0u;
+        for (int w = 0; w < wave; ++w) prior = wmax[w] > prior ? wmax[w] : prior;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if constexpr (sizeof(PT) == 8) {
+                v[r].x = v[r].x > prior ? v[r].x : prior;
+            } else {
+                const uint32_t b = v[r] > prior ? v[r] : prior;
+                v[r] = fp.pos_payload ? wbase + r * 64u + lane : b;
+            }
+        }
+    }
     // stage the tile in LDS in output order; meanwhile waves 0-3 look back
     // for the tile's global digit offsets
 #pragma unroll
@@ -1082,7 +1228,7 @@ __global__ __launch_bounds__(kRleThreads) void k_rle(
     }
 }
 
-template <int R, typename PT, int NB, bool LOWLDS>
+template <int R, typename PT, int NB, bool LOWLDS, bool FIRST>
 void launch_onesweep(BwdArgs& a, uint32_t nb, const uint32_t* keys_in, const PT* vals_in,
                      uint32_t* keys_out, PT* vals_out, uint32_t N, int shift, int pass,
                      uint32_t* ctl, uint32_t* status)
@@ -1097,24 +1243,38 @@ void launch_onesweep(BwdArgs& a, uint32_t nb, const uint32_t* keys_in, const PT*
         seg.copies = static_cast<uint32_t>(L.seg_copies);
         seg.hash_off = a.plan->d_hash_off;
     }
-    hipLaunchKernelGGL((k_onesweep<R, PT, NB, LOWLDS>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys_in,
+    FirstPass fp{};
+    if (FIRST) {
+        fp.indices = a.indices;
+        fp.offsets = a.offsets;
+        fp.psw = a.psw;
+        fp.tile_bag = reinterpret_cast<const uint32_t*>(a.ws + L.off_tile_bag);
+        fp.B = static_cast<uint32_t>(a.B);
+        fp.i64 = a.plan->idtype == TBE_I64 ? 1u : 0u;
+        fp.pos_payload = a.payload_mode == kPayloadPos ? 1u : 0u;
+    }
+    hipLaunchKernelGGL((k_onesweep<R, PT, NB, LOWLDS, FIRST>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys_in,
                        vals_in, keys_out, vals_out, N, shift, ctl + kCtlTotals + pass * kRadixMax,
                        status + static_cast<size_t>(pass) * kRadixMax * nb,
                        ctl + kCtlTicket + pass, ctl + kCtlError, nb,
                        pass > 0 && !L.seg ? ctl + kCtlTotals + (pass - 1) * kRadixMax : nullptr,
-                       seg);
+                       seg, fp);
 }
 
 // The low-LDS tile stages digits as bytes, so a 9-bit pass takes the
 // full-LDS tile whatever the tile count.
-template <int R, typename PT, bool LOWLDS>
+template <int R, typename PT, bool LOWLDS, bool FIRST>
 auto pick_onesweep(int nbits)
 {
-    auto f = nbits <= 1 ? launch_onesweep<R, PT, 1, LOWLDS> : nbits == 2 ? launch_onesweep<R, PT, 2, LOWLDS>
-         : nbits == 3 ? launch_onesweep<R, PT, 3, LOWLDS> : nbits == 4 ? launch_onesweep<R, PT, 4, LOWLDS>
-         : nbits == 5 ? launch_onesweep<R, PT, 5, LOWLDS> : nbits == 6 ? launch_onesweep<R, PT, 6, LOWLDS>
-         : nbits == 7 ? launch_onesweep<R, PT, 7, LOWLDS> : launch_onesweep<R, PT, 8, LOWLDS>;
-    if (nbits >= 9) f = launch_onesweep<R, PT, 9, false>;
+    auto f = nbits <= 1 ? launch_onesweep<R, PT, 1, LOWLDS, FIRST>
+           : nbits == 2 ? launch_onesweep<R, PT, 2, LOWLDS, FIRST>
+           : nbits == 3 ? launch_onesweep<R, PT, 3, LOWLDS, FIRST>
+           : nbits == 4 ? launch_onesweep<R, PT, 4, LOWLDS, FIRST>
+           : nbits == 5 ? launch_onesweep<R, PT, 5, LOWLDS, FIRST>
+           : nbits == 6 ? launch_onesweep<R, PT, 6, LOWLDS, FIRST>
+           : nbits == 7 ? launch_onesweep<R, PT, 7, LOWLDS, FIRST>
+                        : launch_onesweep<R, PT, 8, LOWLDS, FIRST>;
+    if (nbits >= 9) f = launch_onesweep<R, PT, 9, false, FIRST>;
     return f;
 }
 
@@ -1144,10 +1304,13 @@ hipError_t sort_passes(BwdArgs& a)
     const bool low = sizeof(PT) == 4 && nb > kLowLdsMinTiles;
     for (int pass = 0; pass < L.npasses; ++pass) {
         const int nbits = L.digit_bits[pass];
-        // one instantiation per digit width: the rank tests only the digit's bits
-        auto* f = pick_onesweep<R, PT, false>(nbits);
+        // one instantiation per digit width: the rank tests only the digit's bits;
+        // a fused first pass reads the ids itself
+        const bool first = pass == 0 && a.fused != 0;
+        auto* f = first ? pick_onesweep<R, PT, false, true>(nbits) : pick_onesweep<R, PT, false, false>(nbits);
         if constexpr (sizeof(PT) == 4)
-            if (low) f = pick_onesweep<R, PT, true>(nbits);
+            if (low)
+                f = first ? pick_onesweep<R, PT, true, true>(nbits) : pick_onesweep<R, PT, true, false>(nbits);
         f(a, nb, keys[cur], vals[cur], keys[cur ^ 1], vals[cur ^ 1], N, shift, pass, ctl, status);
         cur ^= 1;
         shift += nbits;
@@ -1156,7 +1319,7 @@ hipError_t sort_passes(BwdArgs& a)
     return hipGetLastError();
 }
 
-template <typename IT, int MODE>
+template <typename IT, int MODE, bool LITE>
 void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
 {
     const BwdLayout& L = a.L;
@@ -1169,9 +1332,10 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                            a.plan->T, reinterpret_cast<uint32_t*>(ws + L.off_tab_tot), words,
                            reinterpret_cast<uint4*>(ws + L.off_seg_tiles),
                            static_cast<uint32_t>(L.sort_blocks),
-                           static_cast<uint32_t>(L.sort_tile));
+                           static_cast<uint32_t>(L.sort_tile),
+                           reinterpret_cast<uint32_t*>(ws + L.off_seg_first));
     }
-    hipLaunchKernelGGL((k_prep<IT, MODE>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
+    hipLaunchKernelGGL((k_prep<IT, MODE, LITE>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
                        a.plan->d_tables, static_cast<uint32_t>(a.B), total_bags,
                        static_cast<uint32_t>(L.prep_bags), static_cast<const IT*>(a.indices),
                        static_cast<const IT*>(a.offsets), a.psw,
@@ -1180,7 +1344,10 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                        reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlTotals, pb,
                        reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words,
                        static_cast<uint32_t>(L.prep_bpt), static_cast<uint32_t>(L.seg_copies),
-                       L.seg ? reinterpret_cast<uint32_t*>(ws + L.off_tab_tot) : nullptr);
+                       L.seg ? reinterpret_cast<uint32_t*>(ws + L.off_tab_tot) : nullptr,
+                       reinterpret_cast<uint32_t*>(ws + L.off_tile_bag),
+                       reinterpret_cast<const uint32_t*>(ws + L.off_seg_first),
+                       static_cast<uint32_t>(L.sort_tile));
 }
 
 }  // namespace
@@ -1213,19 +1380,33 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                    : p->pooling == TBE_POOL_MEAN ? kPayloadMean
                    : (a.psw ? kPayloadSampleW : kPayloadSample);
     a.payload_pairs = mode == kPayloadSampleW || mode == kPayloadMean;
+    // per-table sort: the first radix pass reads the ids and makes the
+    // payloads itself (mean pooling's 1/L payload keeps the full key pass)
+    a.fused = L.seg && mode != kPayloadMean ? 1 : 0;
+    a.payload_mode = mode;
     const bool i64 = p->idtype == TBE_I64;
-    if (mode == kPayloadPos)
-        i64 ? launch_prep<int64_t, kPayloadPos>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadPos>(a, pb, total_bags);
+    if (a.fused) {
+        if (mode == kPayloadPos)
+            i64 ? launch_prep<int64_t, kPayloadPos, true>(a, pb, total_bags)
+                : launch_prep<int32_t, kPayloadPos, true>(a, pb, total_bags);
+        else if (mode == kPayloadSample)
+            i64 ? launch_prep<int64_t, kPayloadSample, true>(a, pb, total_bags)
+                : launch_prep<int32_t, kPayloadSample, true>(a, pb, total_bags);
+        else
+            i64 ? launch_prep<int64_t, kPayloadSampleW, true>(a, pb, total_bags)
+                : launch_prep<int32_t, kPayloadSampleW, true>(a, pb, total_bags);
+    } else if (mode == kPayloadPos)
+        i64 ? launch_prep<int64_t, kPayloadPos, false>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadPos, false>(a, pb, total_bags);
     else if (mode == kPayloadSample)
-        i64 ? launch_prep<int64_t, kPayloadSample>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadSample>(a, pb, total_bags);
+        i64 ? launch_prep<int64_t, kPayloadSample, false>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSample, false>(a, pb, total_bags);
     else if (mode == kPayloadSampleW)
-        i64 ? launch_prep<int64_t, kPayloadSampleW>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadSampleW>(a, pb, total_bags);
+        i64 ? launch_prep<int64_t, kPayloadSampleW, false>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSampleW, false>(a, pb, total_bags);
     else
-        i64 ? launch_prep<int64_t, kPayloadMean>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadMean>(a, pb, total_bags);
+        i64 ? launch_prep<int64_t, kPayloadMean, false>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadMean, false>(a, pb, total_bags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     stage_mark(p, 1, a.stream);

@@ -134,6 +134,8 @@ struct BwdLayout {
     int32_t seg_copies = 0;     // copies of each table's digit counts (fewer adds per address)
     size_t off_tab_tot = 0;     // [T][seg_copies][npasses][kRadixMax] digit counts of each table
     size_t off_seg_tiles = 0;   // [sort_blocks] {first position, end, table's first position, table}
+    size_t off_tile_bag = 0;    // [sort_blocks] bag (within its table) of each tile's first position
+    size_t off_seg_first = 0;   // [T + 1] each table's first tile slot
     size_t total = 0;
 };
 BwdLayout bwd_layout(const tbe_plan* p, int32_t B, int64_t N);
@@ -159,6 +161,10 @@ struct BwdArgs {
     // and whether its payload is (sample, weight) pairs or sample ids
     int final_buf;
     int payload_pairs;
+    // nonzero when the first radix pass of a per-table sort reads the ids
+    // itself after a counts-only key pass; the payload's kind
+    int fused;
+    int payload_mode;
 };
 // api_outputs: also write unique keys, run starts / lengths and run-id lists.
 hipError_t run_sort_rle(BwdArgs& a, bool api_outputs);

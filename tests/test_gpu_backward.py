@@ -157,6 +157,22 @@ def test_exact_arithmetic_bit_exact(wdtype, seed, tau, chunk):
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
 
 
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("sort_mode", [1, 2])
+def test_many_short_and_empty_bags_per_tile(weighted, sort_mode):
+    """Bags of 0-2 lookups: a radix tile spans several thousand bags (over a
+    thousand at a time are marked in the first per-table pass), with runs of
+    empty bags at tile boundaries. Sort view and exact-arithmetic weights."""
+    prob, packed = dg.exact_problem(61 + int(weighted), T=2, B=30000, dims=(4, 8),
+                                    weighted=weighted, max_len=2, max_rows=300)
+    _compare_sort(gpu_sort(prob, tau=8, sort_mode=sort_mode), H.oracle_sort(prob, 8), prob.N)
+    w = gpu_backward(prob, H.device_weights_from_host(packed), tau=8, chunk=4,
+                     sort_mode=sort_mode)
+    ref = packed.copy()
+    H.oracle_backward(prob, ref)
+    assert np.array_equal(w.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+
+
 @pytest.mark.parametrize("dims,wdtype", [((4,), "f32"), ((1,), "f32"), ((2, 4), "f32"),
                                          ((4,), "f16"), ((1, 2), "f16")])
 @pytest.mark.parametrize("tau", [128, 2 ** 31 - 1])
