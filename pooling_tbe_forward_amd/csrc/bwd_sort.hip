@@ -328,19 +328,14 @@ enum PayloadMode : int {
 // table; digits are of the row (the id), and each block adds its digit counts
 // to one of its table's seg_copies copies ([T][seg_copies][npasses][kRadixMax],
 // zeroed by k_seg_setup).
-// LITE (segmented sort whose first radix pass reads the ids itself): digit
-// counts only, no keys or payloads; for each radix tile that starts among the
-// block's lookups, the bag holding that first position goes to tile_bag.
-template <typename IT, int MODE, bool LITE>
+template <typename IT, int MODE>
 __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
     const IT* __restrict__ indices, const IT* __restrict__ offsets,
     const float* __restrict__ psw, uint32_t* __restrict__ keys, void* __restrict__ vals,
     uint32_t* __restrict__ totals, PassBits pb, uint32_t* __restrict__ status,
-    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot,
-    uint32_t* __restrict__ tile_bag, const uint32_t* __restrict__ seg_first, uint32_t sort_tile)
+    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot)
 {
-    static_assert(!LITE || MODE != kPayloadMean, "mean pooling keeps the full key pass");
     __shared__ uint32_t hist[4][kRadixMax];
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
     __shared__ uint32_t hoff[kPrepMaxBags + 1];   // first key of each table the block touches
@@ -369,23 +364,6 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const uint32_t len = nb ? boff[nb] : 0u;
     uint32_t top = 1;
     while (top < nb) top <<= 1;
-    if constexpr (LITE) {
-        // tiles of this table whose first position (relative to the table's
-        // first lookup) falls in [rel0, rel0 + len)
-        const uint32_t t = blockIdx.x / seg_bpt;
-        const uint32_t rel0 =
-            static_cast<uint32_t>(P0 - static_cast<int64_t>(offsets[size_t(t) * B]));
-        for (uint32_t kt = (rel0 + sort_tile - 1) / sort_tile + tid; kt * sort_tile < rel0 + len;
-             kt += kPrepThreads) {
-            const uint32_t rp = kt * sort_tile - rel0;
-            uint32_t g = 0;   // the last bag whose start is <= rp (not empty)
-            for (uint32_t st = top; st > 0; st >>= 1) {
-                const uint32_t c = g + st;
-                g = (c < nb && boff[c] <= rp) ? c : g;
-            }
-            tile_bag[seg_first[t] + kt] = g0 + g - t * B;
-        }
-    }
     constexpr int UN = 8;
     for (uint32_t base = 0; base < len; base += kPrepThreads * UN) {
         IT id[UN];
@@ -395,14 +373,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         for (int u = 0; u < UN; ++u) {
             const uint32_t rp = base + u * kPrepThreads + tid;
             id[u] = rp < len ? indices[P0 + rp] : IT(0);
-            wv[u] = (!LITE && (MODE == kPayloadSampleW || (MODE == kPayloadMean && psw)) && rp < len)
+            wv[u] = ((MODE == kPayloadSampleW || (MODE == kPayloadMean && psw)) && rp < len)
                         ? psw[P0 + rp] : 1.f;
             g[u] = 0;
         }
         // g[u]: the last bag whose start is <= rp (that bag is not empty);
         // branch-free, so the searches of the used slots interleave
-        const uint32_t nu = LITE ? 0u : (len - base + kPrepThreads - 1) / kPrepThreads;   // slots in use
-        for (uint32_t st = LITE ? 0u : top; st > 0; st >>= 1) {
+        const uint32_t nu = (len - base + kPrepThreads - 1) / kPrepThreads;   // slots in use
+        for (uint32_t st = top; st > 0; st >>= 1) {
 #pragma unroll
             for (int u = 0; u < UN; ++u) {
                 if (u < nu) {
@@ -417,7 +395,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         // registers are not reused before the loop ends, so no wait on it
         uint32_t key[UN], pay[UN];
 #pragma unroll
-        for (int u = 0; u < UN && !LITE; ++u) {
+        for (int u = 0; u < UN; ++u) {
             const uint32_t gg = g0 + g[u];
             const uint32_t t = gg / B;
             key[u] = hoff[t - t_first] + static_cast<uint32_t>(id[u]);
@@ -438,7 +416,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         for (int u = 0; u < UN; ++u) {
             const bool ok = base + u * kPrepThreads + tid < len;
             // (segmented sort: the row's digits)
-            const uint32_t dk = (LITE || seg) ? static_cast<uint32_t>(id[u]) : key[u];
+            const uint32_t dk = seg ? static_cast<uint32_t>(id[u]) : key[u];
             if (ok)
                 for (int q = 0; q < pb.npasses; ++q) {
                     const uint32_t d = (dk >> pb.shift[q]) & pb.mask[q];
@@ -451,7 +429,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
                 }
         }
 #pragma unroll
-        for (int u = 0; u < UN && !LITE; ++u) {
+        for (int u = 0; u < UN; ++u) {
             const uint32_t rp = base + u * kPrepThreads + tid;
             if (rp < len) {
                 const int64_t p = P0 + rp;
@@ -479,6 +457,107 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
             const uint32_t c = hist[q][i % kRadixMax];
             if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
         }
+    }
+    // the look-back words of the radix passes and the run-length encode
+    for (size_t i = blockIdx.x * size_t(kPrepThreads) + tid; i < status_words;
+         i += size_t(gridDim.x) * kPrepThreads)
+        status[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Key pass of a per-table sort whose first radix pass reads the batch itself:
+// digit counts only.  Block layout as k_prep's segmented one (seg_bpt blocks
+// per table, bags_per_block bags each); the ids are streamed two batches
+// deep (the next batch loads while this one is counted) and nothing is
+// written per lookup.  For each radix tile that starts among the block's
+// lookups, the bag holding that first position (within its table) goes to
+// tile_bag[seg_first[t] + tile index in the table].
+template <typename IT>
+__global__ __launch_bounds__(kPrepThreads) void k_count(
+    uint32_t B, uint32_t bags_per_block, const IT* __restrict__ indices,
+    const IT* __restrict__ offsets, PassBits pb, uint32_t* __restrict__ status,
+    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot,
+    uint32_t* __restrict__ tile_bag, const uint32_t* __restrict__ seg_first, uint32_t sort_tile)
+{
+    __shared__ uint32_t hist[4][kRadixMax];
+    __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) (&hist[0][0])[i] = 0u;
+    const uint32_t t = blockIdx.x / seg_bpt, j = blockIdx.x - t * seg_bpt;
+    const uint32_t b0 = j * bags_per_block;
+    const uint32_t nb = b0 < B ? min(bags_per_block, B - b0) : 0u;
+    const size_t g0 = size_t(t) * B + b0;
+    const int64_t P0 = static_cast<int64_t>(offsets[g0]);
+    const uint32_t len = static_cast<uint32_t>(static_cast<int64_t>(offsets[g0 + nb]) - P0);
+    const int64_t T0 = static_cast<int64_t>(offsets[size_t(t) * B]);   // the table's first lookup
+    // this block's bag starts, loaded now and staged after the counts
+    constexpr int BPT = (kPrepMaxBags + kPrepThreads) / kPrepThreads;
+    uint32_t bs[BPT];
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        const uint32_t i = k * kPrepThreads + tid;
+        bs[k] = i <= nb ? static_cast<uint32_t>(static_cast<int64_t>(offsets[g0 + i]) - P0) : 0u;
+    }
+    __syncthreads();   // counters cleared
+    constexpr int UN = 8;
+    constexpr uint32_t kStep = kPrepThreads * UN;
+    auto load = [&](uint32_t base, uint32_t (&id)[UN]) {
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const uint32_t rp = base + u * kPrepThreads + tid;
+            id[u] = rp < len ? static_cast<uint32_t>(indices[P0 + rp]) : 0u;
+        }
+    };
+    uint32_t cur[UN], nxt[UN];
+    load(0, cur);
+    for (uint32_t base = 0; base < len; base += kStep) {
+        if (base + kStep < len) load(base + kStep, nxt);
+        // digit counts; lanes sharing the wave's first active lane's digit
+        // add once (a table's rows often share their upper digits)
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (base + u * kPrepThreads + tid < len)
+                for (int q = 0; q < pb.npasses; ++q) {
+                    const uint32_t d = (cur[u] >> pb.shift[q]) & pb.mask[q];
+                    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+                    const uint64_t same = __ballot(d == d0);
+                    if (d != d0)
+                        atomicAdd(&hist[q][d], 1u);
+                    else if (lane == __builtin_ctzll(same))
+                        atomicAdd(&hist[q][d0], static_cast<uint32_t>(__popcll(same)));
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) cur[u] = nxt[u];
+    }
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        const uint32_t i = k * kPrepThreads + tid;
+        if (i <= nb) boff[i] = bs[k];
+    }
+    __syncthreads();
+    {   // one copy of this table's counts (blocks of the table share the copies)
+        uint32_t* tt = tab_tot + (size_t(t) * seg_copies + j % seg_copies) * pb.npasses * kRadixMax;
+        for (int i = tid; i < pb.npasses * kRadixMax; i += kPrepThreads) {
+            const uint32_t c = hist[i / kRadixMax][i % kRadixMax];
+            if (c) atomicAdd(&tt[i], c);
+        }
+    }
+    // tiles of this table whose first position (relative to the table's first
+    // lookup) falls in [rel0, rel0 + len)
+    uint32_t top = 1;
+    while (top < nb) top <<= 1;
+    const uint32_t rel0 = static_cast<uint32_t>(P0 - T0);
+    for (uint32_t kt = (rel0 + sort_tile - 1) / sort_tile + tid; kt * sort_tile < rel0 + len;
+         kt += kPrepThreads) {
+        const uint32_t rp = kt * sort_tile - rel0;
+        uint32_t g = 0;   // the last bag whose start is <= rp (not empty)
+        for (uint32_t st = top; st > 0; st >>= 1) {
+            const uint32_t c = g + st;
+            g = (c < nb && boff[c] <= rp) ? c : g;
+        }
+        tile_bag[seg_first[t] + kt] = b0 + g;
     }
     // the look-back words of the radix passes and the run-length encode
     for (size_t i = blockIdx.x * size_t(kPrepThreads) + tid; i < status_words;
@@ -1319,7 +1398,7 @@ hipError_t sort_passes(BwdArgs& a)
     return hipGetLastError();
 }
 
-template <typename IT, int MODE, bool LITE>
+template <typename IT, int MODE>
 void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
 {
     const BwdLayout& L = a.L;
@@ -1335,7 +1414,19 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                            static_cast<uint32_t>(L.sort_tile),
                            reinterpret_cast<uint32_t*>(ws + L.off_seg_first));
     }
-    hipLaunchKernelGGL((k_prep<IT, MODE, LITE>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
+    if (a.fused) {
+        hipLaunchKernelGGL((k_count<IT>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
+                           static_cast<uint32_t>(a.B), static_cast<uint32_t>(L.prep_bags),
+                           static_cast<const IT*>(a.indices), static_cast<const IT*>(a.offsets),
+                           pb, reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words,
+                           static_cast<uint32_t>(L.prep_bpt), static_cast<uint32_t>(L.seg_copies),
+                           reinterpret_cast<uint32_t*>(ws + L.off_tab_tot),
+                           reinterpret_cast<uint32_t*>(ws + L.off_tile_bag),
+                           reinterpret_cast<const uint32_t*>(ws + L.off_seg_first),
+                           static_cast<uint32_t>(L.sort_tile));
+        return;
+    }
+    hipLaunchKernelGGL((k_prep<IT, MODE>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
                        a.plan->d_tables, static_cast<uint32_t>(a.B), total_bags,
                        static_cast<uint32_t>(L.prep_bags), static_cast<const IT*>(a.indices),
                        static_cast<const IT*>(a.offsets), a.psw,
@@ -1344,10 +1435,7 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                        reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlTotals, pb,
                        reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words,
                        static_cast<uint32_t>(L.prep_bpt), static_cast<uint32_t>(L.seg_copies),
-                       L.seg ? reinterpret_cast<uint32_t*>(ws + L.off_tab_tot) : nullptr,
-                       reinterpret_cast<uint32_t*>(ws + L.off_tile_bag),
-                       reinterpret_cast<const uint32_t*>(ws + L.off_seg_first),
-                       static_cast<uint32_t>(L.sort_tile));
+                       L.seg ? reinterpret_cast<uint32_t*>(ws + L.off_tab_tot) : nullptr);
 }
 
 }  // namespace
@@ -1385,28 +1473,21 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
     a.fused = L.seg && mode != kPayloadMean ? 1 : 0;
     a.payload_mode = mode;
     const bool i64 = p->idtype == TBE_I64;
-    if (a.fused) {
-        if (mode == kPayloadPos)
-            i64 ? launch_prep<int64_t, kPayloadPos, true>(a, pb, total_bags)
-                : launch_prep<int32_t, kPayloadPos, true>(a, pb, total_bags);
-        else if (mode == kPayloadSample)
-            i64 ? launch_prep<int64_t, kPayloadSample, true>(a, pb, total_bags)
-                : launch_prep<int32_t, kPayloadSample, true>(a, pb, total_bags);
-        else
-            i64 ? launch_prep<int64_t, kPayloadSampleW, true>(a, pb, total_bags)
-                : launch_prep<int32_t, kPayloadSampleW, true>(a, pb, total_bags);
-    } else if (mode == kPayloadPos)
-        i64 ? launch_prep<int64_t, kPayloadPos, false>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadPos, false>(a, pb, total_bags);
+    if (a.fused)   // counts only: the payload is made by the first radix pass
+        i64 ? launch_prep<int64_t, kPayloadSample>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSample>(a, pb, total_bags);
+    else if (mode == kPayloadPos)
+        i64 ? launch_prep<int64_t, kPayloadPos>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadPos>(a, pb, total_bags);
     else if (mode == kPayloadSample)
-        i64 ? launch_prep<int64_t, kPayloadSample, false>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadSample, false>(a, pb, total_bags);
+        i64 ? launch_prep<int64_t, kPayloadSample>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSample>(a, pb, total_bags);
     else if (mode == kPayloadSampleW)
-        i64 ? launch_prep<int64_t, kPayloadSampleW, false>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadSampleW, false>(a, pb, total_bags);
+        i64 ? launch_prep<int64_t, kPayloadSampleW>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadSampleW>(a, pb, total_bags);
     else
-        i64 ? launch_prep<int64_t, kPayloadMean, false>(a, pb, total_bags)
-            : launch_prep<int32_t, kPayloadMean, false>(a, pb, total_bags);
+        i64 ? launch_prep<int64_t, kPayloadMean>(a, pb, total_bags)
+            : launch_prep<int32_t, kPayloadMean>(a, pb, total_bags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     stage_mark(p, 1, a.stream);

@@ -103,10 +103,11 @@ def _rows_on_device(prob, w_dev, keys, like):
 @pytest.mark.parametrize("name,B,tau", [("toy", None, 2), ("uniform", 256, 128),
                                         ("stress", 256, 16), ("mixed", 64, 128)])
 @pytest.mark.parametrize("opt", ["sgd", "adagrad"])
-def test_mean_backward_vs_oracle(name, B, tau, opt):
+@pytest.mark.parametrize("sort_mode", [1, 2])
+def test_mean_backward_vs_oracle(name, B, tau, opt, sort_mode):
     prob = dg.make_problem(name, seed=910, **({} if B is None else dict(B=B)))
     plan = _plan(prob)
-    tbe.tbe_set_tuning(plan, tau=tau, chunk=8)
+    tbe.tbe_set_tuning(plan, tau=tau, chunk=8, sort_mode=sort_mode)
     d = H.device_inputs(prob)
     w = dg.packed_weights_torch(prob, "cuda")
     ws = tbe.alloc_workspace(plan, prob.B, prob.N)
