@@ -646,15 +646,20 @@ __global__ __launch_bounds__(1024) void k_seg_setup(
 // a tile reads the ids itself (key = the table's first key + row) and makes
 // its payload: the bag of each position comes from marks at the bags' first
 // positions in LDS and a running maximum over positions, starting from the
-// bag that holds the tile's first position (tile_bag).
+// bag that holds the tile's first position (tile_bag).  Mean pooling's
+// weight / bag length: each marked bag's length is kept at its first
+// position too, and a second running maximum (of marked positions) finds the
+// first position of each position's bag.
 struct FirstPass {
     const void* indices;        // int32, or int64 when i64
     const void* offsets;        // [T * B + 1], same type
-    const float* psw;           // per-sample weights (payload pairs)
+    const float* psw;           // per-sample weights (payload pairs; may be null with mean)
     const uint32_t* tile_bag;   // [ntiles] bag (within its table) of each tile's first position
+    const TableDesc* tables;    // weighted flags (mean pooling)
     uint32_t B;
     uint32_t i64;
     uint32_t pos_payload;       // payload = lookup position instead of the bag
+    uint32_t mean;              // payload = (bag, weight / bag length)
 };
 
 struct SegPass {
@@ -691,6 +696,10 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
     __shared__ PT sv[LOWLDS ? 1 : kSortThreads * R];
     __shared__ uint8_t sdig[LOWLDS ? kSortThreads * R : 1];
     __shared__ uint32_t wmax[FIRST ? kSortThreads / 64 : 1];
+    __shared__ uint32_t wlen[FIRST ? kSortThreads / 64 : 1];   // mean: length of each wave's last marked bag
+    // mean: bag lengths at their first positions, in the payload staging
+    // buffer (free until the staging)
+    uint32_t* const len_at = reinterpret_cast<uint32_t*>(&sv[0]);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -720,8 +729,11 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
     } else {
         if (tid == 0) s_tile = take_ticket(ticket, ntiles);
         for (int i = tid; i < NW * RX; i += kSortThreads) (&wcnt[0][0])[i] = 0u;
-        if constexpr (FIRST)   // bag marks
+        if constexpr (FIRST) {   // bag marks (and lengths)
             for (int i = tid; i < static_cast<int>(kTile); i += kSortThreads) sk[i] = 0u;
+            if (sizeof(PT) == 8 && !LOWLDS && fp.mean)
+                for (int i = tid; i < static_cast<int>(kTile); i += kSortThreads) len_at[i] = 0u;
+        }
         __syncthreads();
         tile = __builtin_amdgcn_readfirstlane(s_tile);
         if (tile >= ntiles) {
@@ -754,7 +766,11 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
     PT v[R];
     // FIRST: the bag holding the tile's first position, and the first 1024
     // bags after it (their first positions), loaded under the rank
-    uint32_t fb = 0u, st_first = 0u;
+    constexpr bool MEANOK = FIRST && sizeof(PT) == 8 && !LOWLDS;   // tiles that can pool means
+    const bool mean = MEANOK && fp.mean != 0u;
+    uint32_t fb = 0u, st_first = 0u, en_first = 0u, len_fb = 0u;
+    uint32_t mlen[R];   // mean: each position's bag length when its bag starts in this wave
+    bool tab_w = false;
     size_t ob = 0;
     auto bag_start = [&](uint32_t c) {
         return fp.i64 ? static_cast<uint32_t>(static_cast<const int64_t*>(fp.offsets)[ob + c])
@@ -777,11 +793,18 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
             k[r] = hoff + row;
             if constexpr (sizeof(PT) == 8) {
                 uint32_t wb = 0u;
-                if (ok) wb = __float_as_uint(fp.psw[i]);
+                if (ok && fp.psw) wb = __float_as_uint(fp.psw[i]);
                 v[r].y = wb;
             }
         }
-        if (fb + 1u + tid < fp.B) st_first = bag_start(fb + 1u + tid);
+        if (fb + 1u + tid < fp.B) {
+            st_first = bag_start(fb + 1u + tid);
+            if (mean) en_first = bag_start(fb + 2u + tid);   // fb + 2 + tid <= B
+        }
+        if (mean) {
+            len_fb = __builtin_amdgcn_readfirstlane(bag_start(fb + 1u) - bag_start(fb));
+            tab_w = fp.psw && (__builtin_amdgcn_readfirstlane(fp.tables[tab].flags) & TD_WEIGHTED);
+        }
     }
     uint32_t inc = 0;
     if (tid < RX) {
@@ -837,13 +860,19 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
         // (the largest of bags starting together is the one not empty); the
         // barrier that ends the rank ends the first 1024 bags' marks
         uint32_t c = fb + 1u + tid;
-        uint32_t st = st_first;
+        uint32_t st = st_first, en = en_first;
         for (;;) {
             const bool more = c < fp.B && st < tend;
-            if (more && st > t0) atomicMax(&sk[st - t0], c);
+            if (more && st > t0) {
+                atomicMax(&sk[st - t0], c);
+                if (mean) atomicMax(&len_at[st - t0], en - st);   // empty bags add 0
+            }
             if (!__syncthreads_or(tid == kSortThreads - 1 && more)) break;
             c += kSortThreads;
-            if (c < fp.B) st = bag_start(c);
+            if (c < fp.B) {
+                st = bag_start(c);
+                if (mean) en = bag_start(c + 1u);
+            }
         }
         // each position's bag: running maximum over the wave's positions
         // (the rounds are scanned side by side, then carried in order)
@@ -863,6 +892,20 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
             run = last > run ? last : run;
         }
         if (lane == 0) wmax[wave] = run;   // read after the next barrier
+        if (mean) {
+            // the first position of each position's bag when it starts in
+            // this wave (0: it started earlier), and that bag's length
+            uint32_t srun = 0u;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t li = static_cast<uint32_t>(wave) * (64u * R) + r * 64u + lane;
+                uint32_t m = wave_incl_max(sk[li] != 0u ? li : 0u);
+                m = m > srun ? m : srun;
+                srun = __builtin_amdgcn_readlane(m, 63);
+                mlen[r] = m != 0u ? len_at[m] : 0u;
+            }
+            if (lane == 0) wlen[wave] = srun != 0u ? len_at[srun] : 0u;
+        }
     } else {
         __syncthreads();
     }
@@ -904,10 +947,20 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(LO
     if constexpr (FIRST) {   // the bags carried in from earlier waves
         uint32_t prior = 0u;
         for (int w = 0; w < wave; ++w) prior = wmax[w] > prior ? wmax[w] : prior;
+        uint32_t clen = len_fb;   // mean: length of the bag carried in from earlier waves
+        if (mean)
+            for (int w = 0; w < wave; ++w) clen = wlen[w] != 0u ? wlen[w] : clen;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if constexpr (sizeof(PT) == 8) {
                 v[r].x = v[r].x > prior ? v[r].x : prior;
+                if constexpr (MEANOK) {
+                    if (mean) {   // d(mean)/d(row) = weight / bag length
+                        const uint32_t bl = mlen[r] != 0u ? mlen[r] : clen;
+                        const float w = tab_w ? __uint_as_float(v[r].y) : 1.f;
+                        v[r].y = __float_as_uint(w / static_cast<float>(bl));
+                    }
+                }
             } else {
                 const uint32_t b = v[r] > prior ? v[r] : prior;
                 v[r] = fp.pos_payload ? wbase + r * 64u + lane : b;
@@ -1331,6 +1384,8 @@ void launch_onesweep(BwdArgs& a, uint32_t nb, const uint32_t* keys_in, const PT*
         fp.B = static_cast<uint32_t>(a.B);
         fp.i64 = a.plan->idtype == TBE_I64 ? 1u : 0u;
         fp.pos_payload = a.payload_mode == kPayloadPos ? 1u : 0u;
+        fp.mean = a.payload_mode == kPayloadMean ? 1u : 0u;
+        fp.tables = a.plan->d_tables;
     }
     hipLaunchKernelGGL((k_onesweep<R, PT, NB, LOWLDS, FIRST>), dim3(nb), dim3(kSortThreads), 0, a.stream, keys_in,
                        vals_in, keys_out, vals_out, N, shift, ctl + kCtlTotals + pass * kRadixMax,
@@ -1469,8 +1524,8 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                    : (a.psw ? kPayloadSampleW : kPayloadSample);
     a.payload_pairs = mode == kPayloadSampleW || mode == kPayloadMean;
     // per-table sort: the first radix pass reads the ids and makes the
-    // payloads itself (mean pooling's 1/L payload keeps the full key pass)
-    a.fused = L.seg && mode != kPayloadMean ? 1 : 0;
+    // payloads itself
+    a.fused = L.seg ? 1 : 0;
     a.payload_mode = mode;
     const bool i64 = p->idtype == TBE_I64;
     if (a.fused)   // counts only: the payload is made by the first radix pass
