@@ -323,18 +323,15 @@ enum PayloadMode : int {
 // One block per run of whole bags (about kPrepKeys lookups), one lookup per
 // thread per step: the bag of a lookup comes from a branchless binary search
 // over the block's bag starts in LDS, so the searches of a thread's lookups
-// interleave.
-// Segmented sort (tab_tot set): seg_bpt blocks per table, each within one
-// table; digits are of the row (the id), and each block adds its digit counts
-// to one of its table's seg_copies copies ([T][seg_copies][npasses][kRadixMax],
-// zeroed by k_seg_setup).
+// interleave.  (One sort over every table's keys; the per-table sort counts
+// with k_count and makes keys and payloads in its first radix pass.)
 template <typename IT, int MODE>
 __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const TableDesc* __restrict__ tables, uint32_t B, uint32_t total_bags, uint32_t bags_per_block,
     const IT* __restrict__ indices, const IT* __restrict__ offsets,
     const float* __restrict__ psw, uint32_t* __restrict__ keys, void* __restrict__ vals,
     uint32_t* __restrict__ totals, PassBits pb, uint32_t* __restrict__ status,
-    size_t status_words, uint32_t seg_bpt, uint32_t seg_copies, uint32_t* __restrict__ tab_tot)
+    size_t status_words)
 {
     __shared__ uint32_t hist[4][kRadixMax];
     __shared__ uint32_t boff[kPrepMaxBags + 1];   // bag starts, relative to the block's first lookup
@@ -342,15 +339,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     __shared__ uint32_t hwt[MODE == kPayloadMean ? kPrepMaxBags + 1 : 1];   // tables' weighted flag
     const int tid = threadIdx.x;
     for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) (&hist[0][0])[i] = 0u;
-    const bool seg = tab_tot != nullptr;
-    uint32_t g0 = blockIdx.x * bags_per_block;
-    uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
-    if (seg) {
-        const uint32_t t = blockIdx.x / seg_bpt, j = blockIdx.x - t * seg_bpt;
-        const uint32_t b0 = j * bags_per_block;
-        g0 = t * B + b0;
-        nb = b0 < B ? min(bags_per_block, B - b0) : 0u;
-    }
+    const uint32_t g0 = blockIdx.x * bags_per_block;
+    const uint32_t nb = g0 < total_bags ? min(bags_per_block, total_bags - g0) : 0u;
     const uint32_t t_first = nb ? g0 / B : 0;
     const uint32_t t_count = nb ? (g0 + nb - 1) / B - t_first + 1 : 0;   // <= nb
     const int64_t P0 = nb ? static_cast<int64_t>(offsets[g0]) : 0;
@@ -415,8 +405,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const bool ok = base + u * kPrepThreads + tid < len;
-            // (segmented sort: the row's digits)
-            const uint32_t dk = seg ? static_cast<uint32_t>(id[u]) : key[u];
+            const uint32_t dk = key[u];
             if (ok)
                 for (int q = 0; q < pb.npasses; ++q) {
                     const uint32_t d = (dk >> pb.shift[q]) & pb.mask[q];
@@ -442,21 +431,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
         }
     }
     __syncthreads();
-    if (seg) {   // one copy of this table's counts (blocks of the table share the copies)
-        const uint32_t t = blockIdx.x / seg_bpt, j = blockIdx.x - t * seg_bpt;
-        uint32_t* tt = tab_tot + (size_t(t) * seg_copies + j % seg_copies) * pb.npasses * kRadixMax;
-        for (int i = tid; i < pb.npasses * kRadixMax; i += kPrepThreads) {
-            const uint32_t c = hist[i / kRadixMax][i % kRadixMax];
-            if (c) atomicAdd(&tt[i], c);
-        }
-    } else {
-        // digit totals are spread over kTotCopies copies (fewer adds per address)
-        uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadixMax);
-        for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) {
-            const int q = i / kRadixMax;
-            const uint32_t c = hist[q][i % kRadixMax];
-            if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
-        }
+    // digit totals are spread over kTotCopies copies (fewer adds per address)
+    uint32_t* tcopy = totals + (blockIdx.x % kTotCopies) * (4 * kRadixMax);
+    for (int i = tid; i < 4 * kRadixMax; i += kPrepThreads) {
+        const int q = i / kRadixMax;
+        const uint32_t c = hist[q][i % kRadixMax];
+        if (q < pb.npasses && c) atomicAdd(&tcopy[i], c);
     }
     // the look-back words of the radix passes and the run-length encode
     for (size_t i = blockIdx.x * size_t(kPrepThreads) + tid; i < status_words;
@@ -466,8 +446,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 
 // ---------------------------------------------------------------------------
 // Key pass of a per-table sort whose first radix pass reads the batch itself:
-// digit counts only.  Block layout as k_prep's segmented one (seg_bpt blocks
-// per table, bags_per_block bags each); the ids are streamed two batches
+// digit counts only.  seg_bpt blocks per table, each over bags_per_block
+// bags of that one table, so its counts are the table's (added to one of
+// seg_copies copies, zeroed by k_seg_setup); the ids are streamed two batches
 // deep (the next batch loads while this one is counted) and nothing is
 // written per lookup.  For each radix tile that starts among the block's
 // lookups, the bag holding that first position (within its table) goes to
@@ -1439,8 +1420,8 @@ hipError_t sort_passes(BwdArgs& a)
     for (int pass = 0; pass < L.npasses; ++pass) {
         const int nbits = L.digit_bits[pass];
         // one instantiation per digit width: the rank tests only the digit's bits;
-        // a fused first pass reads the ids itself
-        const bool first = pass == 0 && a.fused != 0;
+        // the first pass of a per-table sort reads the ids itself
+        const bool first = pass == 0 && L.seg;
         auto* f = first ? pick_onesweep<R, PT, false, true>(nbits) : pick_onesweep<R, PT, false, false>(nbits);
         if constexpr (sizeof(PT) == 4)
             if (low)
@@ -1469,7 +1450,7 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                            static_cast<uint32_t>(L.sort_tile),
                            reinterpret_cast<uint32_t*>(ws + L.off_seg_first));
     }
-    if (a.fused) {
+    if (L.seg) {   // counts only: the first radix pass makes keys and payloads
         hipLaunchKernelGGL((k_count<IT>), dim3(L.prep_blocks), dim3(kPrepThreads), 0, a.stream,
                            static_cast<uint32_t>(a.B), static_cast<uint32_t>(L.prep_bags),
                            static_cast<const IT*>(a.indices), static_cast<const IT*>(a.offsets),
@@ -1488,9 +1469,7 @@ void launch_prep(const BwdArgs& a, const PassBits& pb, uint32_t total_bags)
                        reinterpret_cast<uint32_t*>(ws + L.off_keys[0]),
                        static_cast<void*>(ws + L.off_vals[0]),
                        reinterpret_cast<uint32_t*>(ws + L.off_ctl) + kCtlTotals, pb,
-                       reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words,
-                       static_cast<uint32_t>(L.prep_bpt), static_cast<uint32_t>(L.seg_copies),
-                       L.seg ? reinterpret_cast<uint32_t*>(ws + L.off_tab_tot) : nullptr);
+                       reinterpret_cast<uint32_t*>(ws + L.off_status), L.status_words);
 }
 
 }  // namespace
@@ -1523,12 +1502,9 @@ hipError_t run_sort_rle(BwdArgs& a, bool api_outputs)
                    : p->pooling == TBE_POOL_MEAN ? kPayloadMean
                    : (a.psw ? kPayloadSampleW : kPayloadSample);
     a.payload_pairs = mode == kPayloadSampleW || mode == kPayloadMean;
-    // per-table sort: the first radix pass reads the ids and makes the
-    // payloads itself
-    a.fused = L.seg ? 1 : 0;
-    a.payload_mode = mode;
+    a.payload_mode = mode;   // the per-table sort's first radix pass makes it
     const bool i64 = p->idtype == TBE_I64;
-    if (a.fused)   // counts only: the payload is made by the first radix pass
+    if (L.seg)   // counts only: the payload is made by the first radix pass
         i64 ? launch_prep<int64_t, kPayloadSample>(a, pb, total_bags)
             : launch_prep<int32_t, kPayloadSample>(a, pb, total_bags);
     else if (mode == kPayloadPos)

@@ -161,9 +161,7 @@ struct BwdArgs {
     // and whether its payload is (sample, weight) pairs or sample ids
     int final_buf;
     int payload_pairs;
-    // nonzero when the first radix pass of a per-table sort reads the ids
-    // itself after a counts-only key pass; the payload's kind
-    int fused;
+    // the payload's kind (the first radix pass of a per-table sort makes it)
     int payload_mode;
 };
 // api_outputs: also write unique keys, run starts / lengths and run-id lists.
