@@ -157,6 +157,24 @@ def test_exact_arithmetic_bit_exact(wdtype, seed, tau, chunk):
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
 
 
+@pytest.mark.parametrize("T", [300, 1024, 1025, 2100])
+def test_many_tables(T):
+    """Table counts past each staging limit: descriptors in the segment
+    kernel's LDS (256), tables laid out by one block in the per-table sort
+    (1024; past it the sort is one sort of all keys even when per-table
+    sorting is asked for), and hash offsets in the run-length encode's LDS
+    (2048). Sort view and exact-arithmetic weights against the oracle."""
+    rng = np.random.default_rng(T)
+    dims = tuple(int(x) for x in rng.choice([4, 8, 12], size=T))
+    prob, packed = dg.exact_problem(80 + T % 7, T=T, B=3, dims=dims, weighted=True,
+                                    max_len=4, max_rows=40)
+    _compare_sort(gpu_sort(prob, tau=4, sort_mode=2), H.oracle_sort(prob, 4), prob.N)
+    w = gpu_backward(prob, H.device_weights_from_host(packed), tau=4, chunk=2, sort_mode=2)
+    ref = packed.copy()
+    H.oracle_backward(prob, ref)
+    assert np.array_equal(w.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+
+
 @pytest.mark.parametrize("weighted", [False, True])
 @pytest.mark.parametrize("sort_mode", [1, 2])
 def test_many_short_and_empty_bags_per_tile(weighted, sort_mode):
