@@ -334,21 +334,25 @@ def test_error_codes():
                              0.1, tbe.alloc_workspace(plan, prob.B, prob.N))
     with pytest.raises(tbe.TBEError):
         tbe.tbe_set_tuning(plan, tau=0)
+    for bad in (-1, 3):
+        with pytest.raises(tbe.TBEError):
+            tbe.tbe_set_tuning(plan, sort_mode=bad)
     with pytest.raises(tbe.TBEError):
         tbe.tbe_plan_create([10], [0])
 
 
 def test_workspace_reused_across_calls_and_sizes():
-    """One initialised workspace serves many calls of different sizes and both
-    entry points: every call leaves the control block clean."""
+    """One initialised workspace serves many calls of different sizes, both
+    entry points and both sort modes in turn: every call leaves the control
+    block clean."""
     big = dg.make_problem("stress", seed=21, B=512)
     plan_big = H.make_plan(big)
-    tbe.tbe_set_tuning(plan_big, tau=8, chunk=4)
+    tbe.tbe_set_tuning(plan_big, tau=8, chunk=4, sort_mode=2)
     ws = _workspace(plan_big, big)
-    for k, B in enumerate([512, 37, 300, 500]):
+    for k, B in enumerate([512, 37, 300, 500, 400, 256]):
         prob = dg.make_problem("stress", seed=30 + k, B=B)
         plan = H.make_plan(prob)
-        tbe.tbe_set_tuning(plan, tau=8, chunk=4)
+        tbe.tbe_set_tuning(plan, tau=8, chunk=4, sort_mode=1 + (k // 2) % 2)
         d = H.device_inputs(prob)
         if k % 2 == 0:
             v = tbe.tbe_sort_rle(plan, prob.B, d["indices"], d["offsets"], ws)
