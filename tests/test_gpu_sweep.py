@@ -79,3 +79,27 @@ def test_random_exact_case(case):
     ref = packed.copy()
     H.oracle_backward(prob, ref)
     assert np.array_equal(w.cpu().numpy().view(np.uint8), ref.view(np.uint8)), c
+
+
+def test_random_exact_bulk():
+    """Two thousand more small cases in one test (another seed), failing on the
+    first mismatch with its case."""
+    for c in _cases(n=2000, seed=11):
+        test_random_exact_case(c)
+
+
+def test_random_exact_larger_batches():
+    """Batches of 200-3000 samples, so tables span several radix tiles (and the
+    per-table sort its several tiles per table), up to 5000 rows per table."""
+    rng = np.random.default_rng(13)
+    for k in range(60):
+        T = int(rng.integers(1, 9))
+        test_random_exact_case(dict(
+            seed=5000 + k, T=T, B=int(rng.integers(200, 3000)),
+            dims=tuple(int(x) for x in rng.choice(_DIMS[:12], size=T)),
+            wdtype=str(rng.choice(["f32", "f16"])), weighted=bool(rng.integers(0, 2)),
+            index_dtype=str(rng.choice(["i32", "i64"])),
+            max_len=int(rng.choice([3, 12, 40, 90])),
+            max_rows=int(rng.choice([5, 40, 300, 5000])),
+            tau=int(rng.choice([1, 8, 64, 2 ** 31 - 1])), chunk=int(rng.choice([3, 16, 256])),
+            hist_mode=int(rng.choice([0, 1, 2])), sort_mode=int(rng.choice([0, 1, 2]))))
