@@ -13,19 +13,29 @@
 // lookup's sample id and per-sample weight as its payload -- nothing is ever
 // sorted twice and no weight is looked up again by position.
 //
-// Kernels (caller's stream, no host synchronisation):
-//   k_prep      per block of bags: key[j] and its payload (j itself for the
-//               sort_rle entry point; the bag's sample id, plus the per-sample
-//               weight when there is one, for the backward -- so the sorted
-//               result needs no gather), digit histograms of every radix pass
-//               (equal digits of a wavefront merged by ballots, then LDS, then
-//               one global add per digit), and clears the look-back words
-//   k_onesweep  one launch per radix pass (8-bit digits, only the
-//               ceil(log2(sum rows)) key bits are sorted): a tile takes a
-//               ticket in launch order, ranks its keys stably (wave ballots
-//               find equal digits, per-wave LDS counters order them), looks
-//               back over earlier tiles' published digit counts for its
-//               offsets, and scatters key + payload
+// Kernels (caller's stream, no host synchronisation).  A batch's lookups come
+// table by table and keys of different tables never collide, so by default
+// each table's segment of lookup positions is sorted on its own, on row bits
+// only (the widest table's), with look-back chains inside one table; with
+// very many tables, or few tiles per table, one sort runs over all keys.
+//   k_seg_setup (per table) lays out radix tiles inside the tables' segments
+//               and zeroes the per-table digit counts
+//   k_count     (per table) digit counts of every radix pass from the ids
+//               alone, and the bag holding each tile's first position
+//   k_prep      (one sort) per block of bags: key[j] and its payload (j itself
+//               for the sort_rle entry point; the bag's sample id, plus the
+//               per-sample weight or 1/L when there is one, for the
+//               backward), digit histograms of every radix pass (equal digits
+//               of a wavefront merged by ballots, then LDS, then one global
+//               add per digit), and clears the look-back words
+//   k_onesweep  one launch per radix pass (digits of up to 9 bits over the
+//               key bits that need sorting): a tile takes a ticket in launch
+//               order, ranks its keys stably (wave ballots find equal digits,
+//               per-wave LDS counters order them), looks back over earlier
+//               tiles' published digit counts for its offsets, and scatters
+//               key + payload.  The first pass of a per-table sort reads the
+//               ids and weights itself and finds each position's bag (the
+//               payload k_prep would have written)
 //   k_rle       one launch: run heads, lengths (galloping search), the short /
 //               long split and the long-run chunk counts; tile offsets come
 //               from the same look-back, so the run lists stay in key order
