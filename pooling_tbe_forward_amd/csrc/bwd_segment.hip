@@ -339,6 +339,7 @@ constexpr uint32_t kF32Run = 256;
 // even where a row fits one lane (the second lane then idles).
 constexpr int kMinLprLog2 = 1;
 constexpr int kLdsTables = 256;   // table descriptors and item offsets staged in LDS
+constexpr int kCombineLdsHash = 2048;   // the combine's table search in LDS up to this many tables
 
 // A wave-uniform value kept in a scalar register (values read from LDS land in
 // vector registers, one copy per lane).
@@ -519,8 +520,16 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
                                                       const ACC* __restrict__ partials)
 {
     __shared__ Pack<ACC, VEC> red[4][64];   // each wave's folded slab sum
+    __shared__ uint32_t shash[kCombineLdsHash + 1];   // tables' first keys, when few enough
     if (payload_mismatch(c)) return;
     const int tid = threadIdx.x;
+    // a run's table is found by a search over the tables' first keys: in LDS
+    // (one load round per block) rather than a chain of dependent loads
+    const bool lds_hash = c.T <= kCombineLdsHash;
+    if (lds_hash) {
+        for (int i = tid; i <= c.T; i += 256) shash[i] = ldg(c.hash_off + i);
+        __syncthreads();
+    }
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int lpr = c.lpr_log2;
@@ -531,7 +540,18 @@ __global__ __launch_bounds__(256) void k_long_combine(SegArgs c, WT* __restrict_
     const uint32_t nlong = min(ldg(c.counts + 2), c.max_long);
     for (uint32_t k = blockIdx.x; k < nlong; k += gridDim.x) {
         const uint4 li = ldg(c.long_info + k);
-        const TableDesc d = ldg(c.tables + find_table(c.hash_off, c.T, li.x));
+        int t;
+        if (lds_hash) {
+            int lo = 0, hi = c.T;   // shash[lo] <= key < shash[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (shash[mid] <= li.x) lo = mid; else hi = mid;
+            }
+            t = lo;
+        } else {
+            t = find_table(c.hash_off, c.T, li.x);
+        }
+        const TableDesc d = ldg(c.tables + t);
         WT* __restrict__ wrow = weights + d.w_off + static_cast<int64_t>(li.x - d.hash_off) * d.D;
         const uint32_t nq = (li.z + c.chunk - 1) / c.chunk;
         const uint32_t qend = min(li.w + nq, c.max_chunks);
